@@ -1,0 +1,258 @@
+"""TTQ oracle: a plain, slow, obviously correct CPU statement of what the
+TTQ q_proj hot path computes.
+
+TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product (the HIP library and its
+Python binding) never calls it, and it shares no code with the product: no
+kernels, headers, helpers, tables or constant generators.
+
+Sources (the pages about arXiv 2603.19296, "TTQ: Activation-Aware Test-Time
+Quantization to Accelerate LLM Inference On The Fly", Koike-Akino, Liu, Wang):
+  [pd]  paper-daily.com deep reading, §2 (method details), §5, §6
+  [nb]  nubint.ai review, section on the proposed method
+  [gde] gist.science (German), technical summary §2 (Methodik)
+  [gfr] gist.science (French), technical summary §2 A/B (Méthodologie)
+  [tl]  thelatestinai.com listing, Tables 14-15 (layer shapes)
+
+Where the pages leave a step open, the reading taken here is stated in the
+function that implements it.
+
+Precision.  Statistics and the projection are computed in fp64.  The
+quantiser decides integer codes, so it runs in the precision the kernel
+uses, fp32, with every operation rounded once (numpy float32 ops on float32
+arrays are IEEE single operations; division and sqrt are correctly rounded;
+np.rint is round-half-to-even).
+
+Pins (what ties this code to the pages and to mathematics rather than to
+itself) live in tests/test_oracle_*.py; every function here has at least one.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "colstats", "colstats_f64", "svd_factors", "residual", "quantize", "pack",
+    "unpack", "dequant", "linear", "linear_dense", "rtn_reference_levels",
+]
+
+
+# ---------------------------------------------------------------------------
+# O1  Online activation statistics
+# ---------------------------------------------------------------------------
+def colstats_f64(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5) -> np.ndarray:
+    """Diagonal activation statistic in fp64, one value per input channel j.
+
+    [pd] §2 defines the AWQ diagonal as diag[X X^T + lambda I]^alpha, computed
+    online from each prompt's own X; [gde] §2 and [gfr] §2A write the diagonal
+    as a p-norm of the channel's activations plus lambda, raised to alpha.
+    Reading taken (the pages disagree on sum / mean / root): the mean over the
+    T tokens of |x_tj|^p, no p-th root, lambda added after the mean, alpha
+    applied to the sum:  d_j = (mean_t |x_tj|^p + lambda)^alpha.  With p=2 the
+    mean is the diagonal of the autocorrelation E[X X^T] used in [pd] §2, and
+    lambda acts as the shrinkage of [nb].
+
+    X is [T][d] (tokens x input channels).  T must be at least 1.
+    """
+    X64 = np.asarray(X).astype(np.float64)
+    if X64.ndim != 2 or X64.shape[0] < 1:
+        raise ValueError("X must be [T][d] with T >= 1")
+    T = X64.shape[0]
+    a = np.abs(X64)
+    if p == 2.0:
+        powed = a * a
+    elif p == 1.0:
+        powed = a
+    else:
+        powed = a ** p
+    mean = powed.sum(axis=0) / T
+    return (mean + lam) ** alpha
+
+
+def colstats(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5) -> np.ndarray:
+    """D as fp32: the fp64 statistic of colstats_f64 rounded once (RNE).
+    The quantiser below and the projection consume this fp32 D."""
+    return colstats_f64(X, p, lam, alpha).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# O2  Static low-rank factors and the residual to quantise
+# ---------------------------------------------------------------------------
+def svd_factors(W, r: int):
+    """Rank-r factors B [d'][r], A [r][d] from the SVD of W, computed once.
+
+    [pd] §2 and [gfr] §2B: W is split into a quantised residual plus B A, with
+    B, A initialised from the SVD of W and kept static ([gde] says PCA; the
+    SVD reading is taken).  Reading for the split: the balanced one,
+    B = U_r Sigma_r^(1/2), A = Sigma_r^(1/2) V_r^T (any split gives the same
+    product B A).  Computed in fp64, stored fp32.
+    """
+    W64 = np.asarray(W).astype(np.float64)
+    d_out, d = W64.shape
+    if r == 0:
+        return np.zeros((d_out, 0), np.float32), np.zeros((0, d), np.float32)
+    U, S, Vt = np.linalg.svd(W64, full_matrices=False)
+    root = np.sqrt(S[:r])
+    B = U[:, :r] * root[None, :]
+    A = root[:, None] * Vt[:r, :]
+    return B.astype(np.float32), A.astype(np.float32)
+
+
+def residual(W, B, A) -> np.ndarray:
+    """W_res = fp16(W - B A), with the subtraction done in fp64 on the given
+    (fp32) factors and rounded once to fp16.  [pd] §2: the quantised part is
+    the residual of the low-rank factors.  With r = 0, W_res = W."""
+    W16 = np.asarray(W, dtype=np.float16)
+    B = np.asarray(B, dtype=np.float32)
+    A = np.asarray(A, dtype=np.float32)
+    if B.shape[1] == 0:
+        return W16.copy()
+    return (W16.astype(np.float64) - B.astype(np.float64) @ A.astype(np.float64)).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# O3  Activation-scaled group round-to-nearest quantiser
+# ---------------------------------------------------------------------------
+def quantize(W_res, D32, q: int, g: int):
+    """Quantise V = W_res D^(1/2) group-wise with round-to-nearest.
+
+    [pd] §2: RTN quantise-dequantise per group of weights; the AWQ closed form
+    quantises W D^(1/2) and unscales by D^(-1/2) ([gde] §2, [gfr] §2A).  [gde]
+    names the per-group parameters: a scale S and a zero point Z (asymmetric).
+
+    Readings taken where the pages are silent:
+      * a group is g consecutive input channels of one output row (the GEMM
+        reduction axis);
+      * the range is extended to include zero, mn = min(0, min v),
+        mx = max(0, max v), so the zero point is an integer inside [0, N];
+      * the scale is (mx - mn)/N in fp32, stored as fp16 rounded upward (the
+        smallest positive fp16 not below it), and codes are chosen against the
+        stored scale; an all-zero group stores scale 1 and zero 0;
+      * z = clamp(rint(-mn/s), 0, N), c = clamp(rint(v/s) + z, 0, N), with IEEE
+        division and round-half-to-even.
+
+    Steps per group, all in fp32 with single rounding:
+      sq_j = sqrt(D_j);  v = w * sq_j;  mn, mx;  s32 = (mx - mn)/N;
+      s16 = up-rounded fp16 of s32;  s = s16;  z;  codes.
+
+    Returns codes uint8 [d'][d], scales fp16 [d'][d/g], zeros fp16 [d'][d/g].
+    """
+    W16 = np.asarray(W_res, dtype=np.float16)
+    D32 = np.asarray(D32, dtype=np.float32)
+    d_out, d = W16.shape
+    if d % g != 0:
+        raise ValueError("d must be a multiple of g")
+    N = np.float32(2 ** q - 1)
+    zero32 = np.float32(0.0)
+
+    sq = np.sqrt(D32)                                    # fp32, correctly rounded
+    v = W16.astype(np.float32) * sq[None, :]             # fp32 product, one rounding
+    grp = v.reshape(d_out, d // g, g)
+    mn = np.minimum(grp.min(axis=2), zero32)
+    mx = np.maximum(grp.max(axis=2), zero32)
+    s32 = (mx - mn) / N                                  # fp32 subtract, fp32 divide
+
+    s16 = s32.astype(np.float16)                         # RNE ...
+    low = s16.astype(np.float32) < s32                   # ... then step up if below
+    s16[low] = np.nextafter(s16[low], np.float16(np.inf))
+    s16[s16 == 0] = np.float16(2.0 ** -24)               # smallest positive fp16
+    empty = mx == mn                                     # all-zero group
+    s16[empty] = np.float16(1.0)
+    s = s16.astype(np.float32)
+
+    z = np.clip(np.rint(-mn / s), zero32, N) + zero32    # + 0 stores zero as +0
+    z[empty] = zero32
+    codes = np.clip(np.rint(grp / s[:, :, None]) + z[:, :, None], zero32, N)
+    return codes.astype(np.uint8).reshape(d_out, d), s16, z.astype(np.float16)
+
+
+def dequant(codes, s16, z16, g: int) -> np.ndarray:
+    """The dequantised scaled weight V_hat = (c - z) s, fp64 [d'][d]."""
+    c = np.asarray(codes).astype(np.float64)
+    d_out, d = c.shape
+    s = np.repeat(np.asarray(s16).astype(np.float64), g, axis=1)
+    z = np.repeat(np.asarray(z16).astype(np.float64), g, axis=1)
+    assert s.shape == (d_out, d)
+    return (c - z) * s
+
+
+def rtn_reference_levels(q: int) -> np.ndarray:
+    """The integer code grid 0..2^q-1 (used by the brute-force pin)."""
+    return np.arange(2 ** q, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# O4  Packing
+# ---------------------------------------------------------------------------
+def pack(codes, q: int) -> np.ndarray:
+    """Pack q-bit codes into little-endian 32-bit words.
+
+    The pages give no storage format (they only name a Marlin-style kernel,
+    [pd] §5).  Format taken: along each output row, consecutive blocks of 32
+    codes; each block is q uint32 words forming one bitstream in which code k
+    (0..31) occupies bits [q*k, q*k + q).  Result shape [d'][d/32][q].
+    """
+    c = np.asarray(codes).astype(np.uint64)
+    d_out, d = c.shape
+    if d % 32:
+        raise ValueError("d must be a multiple of 32")
+    if c.size and c.max() >= 2 ** q:
+        raise ValueError("code does not fit in q bits")
+    blk = c.reshape(d_out, d // 32, 32)
+    words = np.zeros((d_out, d // 32, q), dtype=np.uint64)
+    for k in range(32):
+        bit = q * k
+        w, off = divmod(bit, 32)
+        words[:, :, w] |= (blk[:, :, k] << np.uint64(off)) & np.uint64(0xFFFFFFFF)
+        if off + q > 32:
+            words[:, :, w + 1] |= blk[:, :, k] >> np.uint64(32 - off)
+    return words.astype(np.uint32)
+
+
+def unpack(words, q: int, d: int) -> np.ndarray:
+    """Inverse of pack: [d'][d/32][q] uint32 -> codes uint8 [d'][d]."""
+    wd = np.asarray(words).astype(np.uint64)
+    d_out = wd.shape[0]
+    out = np.zeros((d_out, d // 32, 32), dtype=np.uint64)
+    mask = np.uint64(2 ** q - 1)
+    for k in range(32):
+        bit = q * k
+        w, off = divmod(bit, 32)
+        val = wd[:, :, w] >> np.uint64(off)
+        if off + q > 32:
+            val |= wd[:, :, w + 1] << np.uint64(32 - off)
+        out[:, :, k] = val & mask
+    return out.reshape(d_out, d).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# O5  The low-bit projection
+# ---------------------------------------------------------------------------
+def linear(X, codes, s16, z16, D32, g: int, B=None, A=None) -> np.ndarray:
+    """Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X), in fp64.
+
+    [pd] §2: the quantised weight is unscaled by D^(-1/2); with the static
+    low-rank factors the layer is W_q + B A ([gfr] §2B).  The D^(-1/2) factor
+    is applied to the input (pre-scaling, [pd] §5).  X is [T][d], Y is
+    [T][d'].  This is the factored evaluation; linear_dense builds the
+    effective weight first.
+    """
+    X64 = np.asarray(X).astype(np.float64)
+    Vh = dequant(codes, s16, z16, g)
+    rs = 1.0 / np.sqrt(np.asarray(D32).astype(np.float64))
+    Y = (X64 * rs[None, :]) @ Vh.T
+    if B is not None and np.asarray(B).shape[1] > 0:
+        B64 = np.asarray(B).astype(np.float64)
+        A64 = np.asarray(A).astype(np.float64)
+        Y = Y + (X64 @ A64.T) @ B64.T
+    return Y
+
+
+def linear_dense(X, codes, s16, z16, D32, g: int, B=None, A=None) -> np.ndarray:
+    """The same Y through the explicit effective weight
+    W_eff = V_hat D^(-1/2) + B A, then Y = X W_eff^T."""
+    Vh = dequant(codes, s16, z16, g)
+    rs = 1.0 / np.sqrt(np.asarray(D32).astype(np.float64))
+    W_eff = Vh * rs[None, :]
+    if B is not None and np.asarray(B).shape[1] > 0:
+        W_eff = W_eff + np.asarray(B).astype(np.float64) @ np.asarray(A).astype(np.float64)
+    return np.asarray(X).astype(np.float64) @ W_eff.T
