@@ -1,0 +1,222 @@
+"""Benchmark of the TTQ q_proj hot path on one MI355X.
+
+Workload: the Qwen3-32B q_proj (d = 5120 -> d' = 8192, thelatestinai.com
+listing, Table 15: 64 heads x 128), one prompt of T = 16384 fp16 tokens,
+q = 4, g = 32, alpha = 0.5, lambda = 0.4, p = 2.  Synthetic seeded
+activations and weights (workloads module); inputs are resident in HBM
+before the timed region.
+
+One step = the whole per-prompt hot path: ttq_prepare (column statistic +
+quantise/pack) then ttq_linear (the low-bit projection of the prompt).
+Reported: prefill k tokens/s at r = 0 (the value), the same at r = 16, the
+decode projection for T in {1, 16, 64} reusing the prefill quantisation,
+per-kernel times with their roofline fractions, and the CPU oracle on a
+bounded sample as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_loop(fn, n, torch):
+    """Average GPU time of fn() over n back-to-back calls on the current stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3  # seconds
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU sharding of the path is "
+              "described, not implemented (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels"}
+
+    import numpy as np
+    import torch
+
+    import test_activation_aware_amd as ttq
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.CONFIGS[5]
+    T, d, d_out, q, g = w.T, w.d, w.d_out, 4, 32
+    log(f"bench: generating inputs T={T} d={d} d'={d_out}")
+    X_np, W_np = wl.config_inputs(5)
+    X = torch.from_numpy(X_np).cuda()
+    W = torch.from_numpy(W_np).cuda()
+    Y = torch.empty((T, d_out), dtype=torch.float16, device="cuda")
+    layer = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+    torch.cuda.synchronize()
+
+    def step():
+        layer.prepare(X)
+        layer.linear(X, out=Y)
+
+    result = {}
+    # ---- the headline step: prepare + prefill projection, r = 0 ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    value = T * args.steps / elapsed / 1e3
+
+    # ---- per-kernel times (same inputs, same launch configuration) ----
+    kernels = {}
+    n_k = max(10, args.steps)
+    if "kernels" in only:
+        D, R = layer.D, layer.dinvsqrt
+        ws = layer.workspace
+        t_cs = time_loop(lambda: ttq.ttq_colstats(X, w.p, w.lam, w.alpha, D=D, dinvsqrt=R, workspace=ws), n_k, torch)
+        t_qp = time_loop(lambda: ttq.ttq_quantize_pack(W, D, q, g, layer.codes, layer.scales, layer.zeros), n_k, torch)
+        t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm(X, R, layer.codes, layer.scales, layer.zeros, q, g, d_out,
+                                                      out=Y), n_k, torch)
+        cs_bytes = T * d * 2 + 8 * d
+        qp_bytes = 2 * d_out * d + 4 * d + q * d_out * d // 8 + 4 * d_out * d // g
+        gm_flops = 2.0 * T * d * d_out
+        kernels = {
+            "colstats": {"us": t_cs * 1e6, "GBs": cs_bytes / t_cs / 1e9,
+                         "frac_hbm": cs_bytes / t_cs / 1e9 / HBM_PEAK_GBS},
+            "quantize_pack": {"us": t_qp * 1e6, "GBs": qp_bytes / t_qp / 1e9,
+                              "frac_hbm": qp_bytes / t_qp / 1e9 / HBM_PEAK_GBS},
+            "wlowbit_gemm": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
+                             "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
+        }
+        result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm / 1e12,
+                              "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                              "traffic": None, "kernel": "ttq_wlowbit_gemm"}
+        log(f"bench: kernels {json.dumps(kernels)}")
+
+    # ---- r = 16: the same step with the rank-16 factors ----
+    r16 = None
+    if "r16" in only:
+        rng = np.random.default_rng(5)
+        log("bench: host SVD for r=16")
+        B, A = ttq.svd_factors(W_np, 16)
+        layer16 = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, B=B, A=A)
+
+        def step16():
+            layer16.prepare(X)
+            layer16.linear(X, out=Y)
+        for _ in range(args.warmup):
+            step16()
+        t16 = time_loop(step16, args.steps, torch)
+        t_z = time_loop(lambda: ttq.ttq_lowrank_z(X, layer16.A, out=layer16.z), n_k, torch)
+        r16 = {"value": T / t16 / 1e3, "ms_per_step": t16 * 1e3, "lowrank_z_us": t_z * 1e6}
+        layer16.close()
+        del rng
+
+    # ---- decode: reuse the prefill quantisation for T = 1, 16, 64 ----
+    decode = {}
+    if "decode" in only:
+        layer.prepare(X)
+        for Td in w.decode_T:
+            Xn = torch.from_numpy(wl.decode_inputs(5, Td, step=Td)).cuda()
+            Yn = torch.empty((Td, d_out), dtype=torch.float16, device="cuda")
+            for _ in range(3):
+                layer.linear(Xn, out=Yn)
+            td = time_loop(lambda: layer.linear(Xn, out=Yn), 50, torch)
+            wbytes = q * d_out * d / 8 + 4 * d_out * d / g + 2 * Td * (d + d_out) + 4 * d
+            decode[str(Td)] = {"k_tok_s": Td / td / 1e3, "us": td * 1e6,
+                               "GBs": wbytes / td / 1e9, "frac_hbm": wbytes / td / 1e9 / HBM_PEAK_GBS}
+
+    # ---- CPU oracle baseline on a bounded sample ----
+    cpu = None
+    if not args.skip_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = cores
+        log("bench: timing the CPU oracle")
+        t0 = time.perf_counter()
+        D0 = oracle.colstats(X_np, w.p, w.lam, w.alpha)
+        c0, s0, z0 = oracle.quantize(W_np, D0, q, g)
+        oracle.pack(c0, q)
+        t_prep = time.perf_counter() - t0
+        n_tok = 512
+        t0 = time.perf_counter()
+        oracle.linear(X_np[:n_tok], c0, s0, z0, D0, g)
+        t_lin = time.perf_counter() - t0
+        t_cpu = t_prep + t_lin * T / n_tok
+        cpu = {"value": T / t_cpu / 1e3, "unit": "k tokens/s", "cores": int(max(1, blas_threads)),
+               "kind": "oracle",
+               "sample": (f"prepare (colstats + quantize + pack) on the full {T}-token prompt "
+                          f"({t_prep:.2f} s), projection on its first {n_tok} tokens ({t_lin:.2f} s) "
+                          f"scaled linearly to {T}; {cores} cores visible, numpy fp64/fp32")}
+
+    out = {
+        "metric": "q_proj prefill k tokens/s (prepare+GEMM) at 4-bit r=0/16; % HBM/MFMA peak",
+        "value": value,
+        "unit": "k tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-32B q_proj prefill, one prompt", "d": d, "d_out": d_out, "T": T,
+                   "q": q, "g": g, "r": 0, "alpha": w.alpha, "lambda": w.lam, "p": w.p,
+                   "x_dtype": "f16"},
+    }
+    if "roofline" in result:
+        out["roofline"] = result["roofline"]
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    if r16 is not None:
+        out["r16"] = r16
+    if kernels:
+        out["kernels"] = kernels
+    if decode:
+        out["decode"] = decode
+    print(json.dumps(out), flush=True)
+    layer.close()
+
+
+if __name__ == "__main__":
+    main()

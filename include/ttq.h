@@ -1,0 +1,214 @@
+/*
+ * ttq.h - C ABI of the TTQ (activation-aware test-time quantization) q_proj
+ * hot path for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (arXiv 2603.19296, "TTQ: Activation-Aware Test-Time
+ * Quantization to Accelerate LLM Inference On The Fly"):
+ *   per prompt X [T][d]:  d_j = (mean_t |x_tj|^p + lambda)^alpha
+ *     (paper-daily.com deep reading, section 2, online AWQ diagonal;
+ *      gist.science German summary, section 2, p-norm form)
+ *   W_res = W - B A with static rank-r factors from the SVD of W
+ *     (paper-daily.com section 2 low-rank compensation; gist.science French
+ *      summary, section 2B)
+ *   codes, scales, zeros = group RTN of W_res D^(1/2)
+ *     (paper-daily.com section 2: RTN QDQ and the closed form Q[W D^(1/2)] D^(-1/2))
+ *   Y = Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
+ *     (paper-daily.com section 5: pre-scaling fused into the low-bit kernel)
+ * Quantisation parameters are computed at prefill and reused by decode
+ * (paper-daily.com section 6).
+ *
+ * Conventions for every entry point
+ *   - Tensors are row-major.  X is [T][ldx] (tokens x input channels, the
+ *     first d columns used), W is [d_out][d_in] fp16, Y is [T][ldy].
+ *   - Pointers marked "device" are HIP device (or managed) memory owned by
+ *     the caller.  The library never allocates, frees or synchronises device
+ *     memory; it only enqueues kernels on the caller's stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All calls are asynchronous; inputs must stay valid until the enqueued
+ *     work has run.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Every function validates all arguments before enqueuing anything; on
+ *     error it returns a non-zero ttq_status, writes nothing, and leaves a
+ *     thread-local message readable with ttq_last_error().
+ *   - Alignment: every device base pointer must be 16-byte aligned, and row
+ *     strides (ldx, ldy) must be multiples of 8 elements (TTQ_ERR_ALIGN).
+ *   - NaN or Inf in X, W or D propagate or give unspecified codes; they are
+ *     not checked.
+ *   - No C++ exception crosses this interface.
+ *
+ * Packed code format (the pages fix none): per output row, blocks of 32
+ * consecutive input channels; each block is q little-endian uint32 words that
+ * form one bitstream, code k of the block occupying bits [q*k, q*k+q).
+ * codes is [d_out][d_in/32][q] uint32; scales and zeros are [d_out][d_in/g]
+ * fp16 (zeros hold exact integers 0..2^q-1).
+ */
+#ifndef TTQ_H
+#define TTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTQ_ABI_VERSION 1
+
+typedef enum ttq_status {
+  TTQ_OK = 0,
+  TTQ_ERR_INVALID_ARG = 1, /* a scalar argument out of its documented range */
+  TTQ_ERR_UNSUPPORTED = 2, /* valid for the method, not built for the GPU (e.g. q=5) */
+  TTQ_ERR_SHAPE = 3,       /* sizes inconsistent, or a buffer too small */
+  TTQ_ERR_NULL = 4,        /* a required pointer is NULL */
+  TTQ_ERR_ALIGN = 5,       /* a pointer or stride breaks the alignment rule */
+  TTQ_ERR_HIP = 6          /* the HIP runtime refused a launch */
+} ttq_status;
+
+typedef enum ttq_dtype {
+  TTQ_F32 = 0,
+  TTQ_F16 = 1
+} ttq_dtype;
+
+/* Hyper-parameters of one q_proj.  Fixed per layer, no test-time search
+ * (paper-daily.com section 2: alpha 0.5-0.75, lambda 0.4, p = 2).
+ *   d_in  (d)  input channels,  multiple of 64 and of g
+ *   d_out (d') output channels, multiple of 4
+ *   q  bits per code: 2, 3 or 4 on the GPU
+ *   g  group size along d_in: 32, 64 or 128
+ *   r  low-rank rank: 0 or 16
+ *   alpha >= 0, p > 0, lambda > 0 unless alpha == 0 (a dead channel would
+ *   otherwise get d_j = 0 and an infinite D^(-1/2)). */
+typedef struct ttq_config {
+  int32_t d_in;
+  int32_t d_out;
+  int32_t q;
+  int32_t g;
+  int32_t r;
+  float alpha;
+  float lambda;
+  float p;
+} ttq_config;
+
+/* Byte sizes of every caller-owned buffer for a configuration and the
+ * largest T a handle will see. */
+typedef struct ttq_sizes {
+  size_t codes_bytes;     /* uint32 [d_out][d_in/32][q]                  */
+  size_t scales_bytes;    /* fp16   [d_out][d_in/g]                      */
+  size_t zeros_bytes;     /* fp16   [d_out][d_in/g]                      */
+  size_t d_bytes;         /* fp32   [d_in]   D                           */
+  size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2)                    */
+  size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */
+  size_t z_bytes;         /* fp32   [T_max][r]    A X     (0 when r = 0) */
+  size_t workspace_bytes; /* fp32 column-statistic partial sums          */
+} ttq_sizes;
+
+/* Device buffers a handle works in (all caller-owned, see ttq_sizes).
+ * B (fp32 [d_out][r]) and A (fp32 [r][d_in]) are the static factors; they
+ * and wres / z are ignored when r = 0. */
+typedef struct ttq_buffers {
+  uint32_t* codes;
+  void* scales;
+  void* zeros;
+  float* D;
+  float* dinvsqrt;
+  void* wres;
+  const float* B;
+  const float* A;
+  float* z;
+  float* workspace;
+  int64_t T_max;
+  size_t workspace_bytes;
+} ttq_buffers;
+
+typedef struct ttq_handle ttq_handle;
+
+/* ABI version the library was built with (TTQ_ABI_VERSION). */
+int32_t ttq_abi_version(void);
+
+/* Static text for a status code.  Never NULL. */
+const char* ttq_status_string(ttq_status s);
+
+/* Detail of the last error on the calling thread ("" if none).  Valid until
+ * the next call into the library on this thread. */
+const char* ttq_last_error(void);
+
+/* Pure host: checks cfg and fills *out for prompts of up to T_max tokens. */
+ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out);
+
+/* Pure host: creates an opaque host object recording cfg and the device
+ * pointers in *bufs (not owning them).  Buffers are checked against
+ * ttq_query_sizes(cfg, bufs->T_max).  Destroy with ttq_destroy. */
+ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle** out);
+void ttq_destroy(ttq_handle* h);
+
+/* Binds the weight W (device fp16 [d_out][d_in]) once per layer.
+ * r = 0: the handle borrows W (keep it alive and unchanged).
+ * r > 0: enqueues W_res = fp16(W - B A) into bufs->wres, with the product
+ *   accumulated in fp64 from the fp32 factors and rounded once (the factors
+ *   come from a host SVD of W, computed once: paper-daily.com section 2,
+ *   gist.science French summary section 2B). */
+ttq_status ttq_set_weight(ttq_handle* h, const void* W, void* stream);
+
+/* Per-prompt prefill step, prepare(X, W, q, g, alpha, lambda, p) with W and
+ * the hyper-parameters bound in the handle:
+ *   D, D^(-1/2) = colstats(X)  then  codes, scales, zeros = quantize(W_res, D).
+ * X: device [T][ldx] of dtype xdt, 1 <= T <= T_max. */
+ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
+                       int64_t ldx, void* stream);
+
+/* The low-bit projection with the handle's current quantisation:
+ *   Y = Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
+ * X: device [T][ldx] of dtype xdt; Y: device [T][ldy] of the same dtype,
+ * fp32 accumulation.  0 <= T <= T_max (r > 0) or any T >= 0 (r = 0);
+ * T = 0 enqueues nothing.  Used for the prefill tokens and, unchanged, for
+ * decode batches that reuse the prefill quantisation. */
+ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
+                      int64_t ldx, void* Y, int64_t ldy, void* stream);
+
+/* ---- Sub-steps, exported so each kernel can be checked on its own ---- */
+
+/* Column statistic: D[j] = fp32((mean_{t<T} |X[t][j]|^p + lambda)^alpha) and
+ * dinvsqrt[j] = fp32(1/sqrt(D[j])), j < d.  Partial sums go to workspace
+ * (fp32, at least ttq_colstats_workspace_bytes(T, d) bytes).  Sums are
+ * taken in a fixed order: the result is deterministic. */
+size_t ttq_colstats_workspace_bytes(int64_t T, int64_t d);
+ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx,
+                        float p, float lambda, float alpha, float* D, float* dinvsqrt,
+                        float* workspace, size_t workspace_bytes, void* stream);
+
+/* Quantise and pack W_src D^(1/2) (device fp16 [d_out][d_in], D device fp32
+ * [d_in]) with the rules of the oracle: fp32 arithmetic, zero-inclusive
+ * group range, fp16 scale rounded upward, z = rint(-mn/s),
+ * c = clamp(rint(v/s) + z, 0, 2^q-1), round half to even, IEEE division.
+ * Writes codes, scales, zeros (layouts above).  Any D > 0 may be supplied
+ * (e.g. D = 1 gives plain RTN, a calibrated D gives static AWQ). */
+ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g,
+                             const void* W_src, const float* D, uint32_t* codes,
+                             void* scales, void* zeros, void* stream);
+
+/* W_res = fp16(W - B A): W device fp16 [d_out][d_in], B device fp32
+ * [d_out][r], A device fp32 [r][d_in]; products summed in fp64. */
+ttq_status ttq_residual(int32_t d_out, int32_t d_in, int32_t r, const void* W,
+                        const float* B, const float* A, void* W_res, void* stream);
+
+/* Z = X A^T: X device [T][ldx] (dtype xdt), A device fp32 [r][d_in],
+ * Z device fp32 [T][r], fp32 accumulation.  r must be 16. */
+ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_dtype xdt,
+                         int64_t ldx, const float* A, float* Z, void* stream);
+
+/* Y = V_hat (dinvsqrt * X) + B Z with V_hat[n][k] = (code - z) * s, fp16
+ * operands on the matrix cores and fp32 accumulation.  dinvsqrt device fp32
+ * [d_in]; codes/scales/zeros as produced by ttq_quantize_pack; B device fp32
+ * [d_out][r] and Z device fp32 [T][r] (both ignored when r = 0).  Y has X's
+ * dtype. */
+ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g,
+                            int32_t r, const void* X, ttq_dtype xdt, int64_t ldx,
+                            const float* dinvsqrt, const uint32_t* codes,
+                            const void* scales, const void* zeros, const float* B,
+                            const float* Z, void* Y, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTQ_H */

@@ -1,0 +1,277 @@
+"""TTQ (activation-aware test-time quantization) q_proj hot path on MI355X.
+
+Thin Python binding over libttq.so (include/ttq.h).  Every step of the path
+runs in the library's HIP kernels; this module only marshals torch tensors
+(device memory) and the current HIP stream into the C calls.  There is no CPU
+fallback: without the built library, or without a GPU, calls raise.
+
+Functions with the C names take torch tensors:
+    ttq_colstats, ttq_quantize_pack, ttq_residual, ttq_lowrank_z,
+    ttq_wlowbit_gemm, ttq_query_sizes
+and TTQLinear wraps the handle API (ttq_create / ttq_set_weight /
+ttq_prepare / ttq_linear / ttq_destroy) for one q_proj layer:
+
+    layer = TTQLinear(W, q=4, g=32, alpha=0.5, lam=0.4, p=2.0, r=0, T_max=T)
+    layer.prepare(X)        # per prompt: D, codes, scales, zeros
+    Y = layer.linear(X)     # prefill projection; later decode batches reuse it
+
+The method: per prompt the channel statistic d_j = (mean_t |x_tj|^p +
+lambda)^alpha (paper-daily.com deep reading of arXiv 2603.19296, section 2),
+group RTN of (W - B A) D^(1/2), and Y = Q[(W - BA) D^(1/2)] (D^(-1/2) X) +
+B (A X) with static factors from the SVD of W (same section; gist.science
+French summary, section 2B).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _capi
+from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
+
+__all__ = [
+    "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
+    "ttq_residual", "ttq_lowrank_z", "ttq_wlowbit_gemm", "ttq_query_sizes",
+    "ttq_colstats_workspace_bytes", "ttq_abi_version",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream() -> int:
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t, name: str, dtype=None):
+    """Pointer of a device tensor, after checking device, dtype and layout."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _x_args(X, name="X"):
+    """(pointer, dtype code, T, ldx) of a row-major [T][>=d] activation."""
+    torch = _torch()
+    if X.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {X.device})")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    if X.dtype == torch.float16:
+        dt = TTQ_F16
+    elif X.dtype == torch.float32:
+        dt = TTQ_F32
+    else:
+        raise TypeError(f"{name} must be float16 or float32 (got {X.dtype})")
+    ld = X.stride(0) if X.shape[0] > 1 else X.shape[1]   # one row: the stride is never used
+    return ctypes.c_void_p(X.data_ptr()), dt, X.shape[0], ld
+
+
+def ttq_abi_version() -> int:
+    return load().ttq_abi_version()
+
+
+def ttq_colstats_workspace_bytes(T: int, d: int) -> int:
+    return load().ttq_colstats_workspace_bytes(T, d)
+
+
+def ttq_query_sizes(d_in, d_out, q, g, r, alpha, lam, p, T_max) -> dict:
+    cfg = _capi.ttq_config(d_in, d_out, q, g, r, alpha, lam, p)
+    out = _capi.ttq_sizes()
+    check(load().ttq_query_sizes(ctypes.byref(cfg), T_max, ctypes.byref(out)), "ttq_query_sizes")
+    return {n: getattr(out, n) for n, _ in _capi.ttq_sizes._fields_}
+
+
+def ttq_colstats(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5, D=None, dinvsqrt=None,
+                 workspace=None):
+    """D, D^(-1/2) (fp32 [d]) of the prompt X [T][d] on the GPU."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    d = X.shape[1]
+    D = torch.empty(d, dtype=torch.float32, device=X.device) if D is None else D
+    dinvsqrt = torch.empty(d, dtype=torch.float32, device=X.device) if dinvsqrt is None else dinvsqrt
+    nbytes = ttq_colstats_workspace_bytes(T, d)
+    if workspace is None:
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=X.device)
+    check(load().ttq_colstats(x, dt, T, d, ldx, p, lam, alpha, _dev(D, "D", torch.float32),
+                              _dev(dinvsqrt, "dinvsqrt", torch.float32),
+                              _dev(workspace, "workspace", torch.float32),
+                              workspace.numel() * 4, _stream()), "ttq_colstats")
+    return D, dinvsqrt
+
+
+def ttq_quantize_pack(W, D, q: int, g: int, codes=None, scales=None, zeros=None):
+    """codes uint32 [d'][d/32][q] (as int32), scales, zeros fp16 [d'][d/g]."""
+    torch = _torch()
+    d_out, d_in = W.shape
+    dev = W.device
+    codes = torch.empty((d_out, d_in // 32, q), dtype=torch.int32, device=dev) if codes is None else codes
+    scales = torch.empty((d_out, d_in // g), dtype=torch.float16, device=dev) if scales is None else scales
+    zeros = torch.empty((d_out, d_in // g), dtype=torch.float16, device=dev) if zeros is None else zeros
+    check(load().ttq_quantize_pack(d_out, d_in, q, g, _dev(W, "W", torch.float16),
+                                   _dev(D, "D", torch.float32), _dev(codes, "codes", torch.int32),
+                                   _dev(scales, "scales", torch.float16),
+                                   _dev(zeros, "zeros", torch.float16), _stream()),
+          "ttq_quantize_pack")
+    return codes, scales, zeros
+
+
+def ttq_residual(W, B, A, out=None):
+    """W_res = fp16(W - B A) on the GPU (fp64 sum of the rank-r product)."""
+    torch = _torch()
+    d_out, d_in = W.shape
+    r = B.shape[1]
+    out = torch.empty_like(W) if out is None else out
+    check(load().ttq_residual(d_out, d_in, r, _dev(W, "W", torch.float16), _dev(B, "B", torch.float32),
+                              _dev(A, "A", torch.float32), _dev(out, "W_res", torch.float16), _stream()),
+          "ttq_residual")
+    return out
+
+
+def ttq_lowrank_z(X, A, out=None):
+    """Z = X A^T, fp32 [T][r]."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    r = A.shape[0]
+    out = torch.empty((T, r), dtype=torch.float32, device=X.device) if out is None else out
+    check(load().ttq_lowrank_z(T, X.shape[1], r, x, dt, ldx, _dev(A, "A", torch.float32),
+                               _dev(out, "Z", torch.float32), _stream()), "ttq_lowrank_z")
+    return out
+
+
+def ttq_wlowbit_gemm(X, dinvsqrt, codes, scales, zeros, q: int, g: int, d_out: int, B=None, Z=None,
+                     out=None):
+    """Y = V_hat (D^(-1/2) X) + B Z with the packed codes; Y has X's dtype."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    d_in = X.shape[1]
+    r = 0 if B is None else B.shape[1]
+    out = torch.empty((T, d_out), dtype=X.dtype, device=X.device) if out is None else out
+    if out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be 2-D with unit column stride")
+    ldy = out.stride(0) if T > 1 else d_out
+    bp = _dev(B, "B", torch.float32) if r else None
+    zp = _dev(Z, "Z", torch.float32) if r else None
+    check(load().ttq_wlowbit_gemm(T, d_in, d_out, q, g, r, x, dt, ldx,
+                                  _dev(dinvsqrt, "dinvsqrt", torch.float32),
+                                  _dev(codes, "codes", torch.int32), _dev(scales, "scales", torch.float16),
+                                  _dev(zeros, "zeros", torch.float16), bp, zp,
+                                  ctypes.c_void_p(out.data_ptr()), ldy, _stream()), "ttq_wlowbit_gemm")
+    return out
+
+
+def svd_factors(W, r: int, oversample: int = 16, power_iters: int = 6, seed: int = 0):
+    """Static rank-r factors B [d'][r], A [r][d] (fp32, balanced split
+    B = U_r S_r^(1/2), A = S_r^(1/2) V_r^T) of the weight, computed once on the
+    host as the pages prescribe (SVD-initialised static factors).
+
+    Small weights use LAPACK's full SVD.  Large ones use a randomised range
+    finder with power iterations (Halko, Martinsson & Tropp, "Finding
+    structure with randomness", 2011, Algorithms 4.4 and 5.1) followed by an
+    exact SVD of the small projected matrix."""
+    W64 = np.asarray(W, dtype=np.float64)
+    d_out, d_in = W64.shape
+    if r == 0:
+        return np.zeros((d_out, 0), np.float32), np.zeros((0, d_in), np.float32)
+    if min(d_out, d_in) <= 2048:
+        U, S, Vt = np.linalg.svd(W64, full_matrices=False)
+    else:
+        rng = np.random.default_rng(seed)
+        k = r + oversample
+        Q, _ = np.linalg.qr(W64 @ rng.standard_normal((d_in, k)))
+        for _ in range(power_iters):
+            Qt, _ = np.linalg.qr(W64.T @ Q)
+            Q, _ = np.linalg.qr(W64 @ Qt)
+        Ub, S, Vt = np.linalg.svd(Q.T @ W64, full_matrices=False)
+        U = Q @ Ub
+    root = np.sqrt(S[:r])
+    return ((U[:, :r] * root[None, :]).astype(np.float32),
+            (root[:, None] * Vt[:r, :]).astype(np.float32))
+
+
+class TTQLinear:
+    """One q_proj through the handle API.  Owns its device buffers (torch);
+    the C library only records pointers to them."""
+
+    def __init__(self, W, q: int = 4, g: int = 32, alpha: float = 0.5, lam: float = 0.4,
+                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None):
+        torch = _torch()
+        if W.dtype != torch.float16 or W.device.type != "cuda" or not W.is_contiguous():
+            raise ValueError("W must be a contiguous fp16 GPU tensor [d_out][d_in]")
+        self.d_out, self.d_in = W.shape
+        self.q, self.g, self.r = q, g, r
+        self.alpha, self.lam, self.p = alpha, lam, p
+        self.T_max = T_max
+        lib = load()
+        self._cfg = _capi.ttq_config(self.d_in, self.d_out, q, g, r, alpha, lam, p)
+        sz = _capi.ttq_sizes()
+        check(lib.ttq_query_sizes(ctypes.byref(self._cfg), T_max, ctypes.byref(sz)), "ttq_query_sizes")
+        dev = W.device
+        self.W = W
+        self.codes = torch.empty((self.d_out, self.d_in // 32, q), dtype=torch.int32, device=dev)
+        self.scales = torch.empty((self.d_out, self.d_in // g), dtype=torch.float16, device=dev)
+        self.zeros = torch.empty((self.d_out, self.d_in // g), dtype=torch.float16, device=dev)
+        self.D = torch.empty(self.d_in, dtype=torch.float32, device=dev)
+        self.dinvsqrt = torch.empty(self.d_in, dtype=torch.float32, device=dev)
+        self.workspace = torch.empty(max(1, sz.workspace_bytes // 4), dtype=torch.float32, device=dev)
+        if r > 0:
+            if B is None or A is None:
+                B, A = svd_factors(W.float().cpu().numpy(), r)
+            self.B = torch.as_tensor(np.ascontiguousarray(B), dtype=torch.float32).to(dev)
+            self.A = torch.as_tensor(np.ascontiguousarray(A), dtype=torch.float32).to(dev)
+            self.wres = torch.empty_like(W)
+            self.z = torch.empty((T_max, r), dtype=torch.float32, device=dev)
+        else:
+            self.B = self.A = self.wres = self.z = None
+        ptr = lambda t: None if t is None else t.data_ptr()
+        self._bufs = _capi.ttq_buffers(ptr(self.codes), ptr(self.scales), ptr(self.zeros), ptr(self.D),
+                                       ptr(self.dinvsqrt), ptr(self.wres), ptr(self.B), ptr(self.A),
+                                       ptr(self.z), ptr(self.workspace), T_max, self.workspace.numel() * 4)
+        h = ctypes.c_void_p()
+        check(lib.ttq_create(ctypes.byref(self._cfg), ctypes.byref(self._bufs), ctypes.byref(h)), "ttq_create")
+        self._h = h
+        check(lib.ttq_set_weight(self._h, ctypes.c_void_p(W.data_ptr()), _stream()), "ttq_set_weight")
+
+    def prepare(self, X) -> None:
+        """Per-prompt prefill step: D, D^(-1/2), codes, scales and zeros."""
+        x, dt, T, ldx = _x_args(X)
+        if X.shape[1] != self.d_in:
+            raise ValueError(f"X has {X.shape[1]} channels, the layer {self.d_in}")
+        check(load().ttq_prepare(self._h, x, dt, T, ldx, _stream()), "ttq_prepare")
+
+    def linear(self, X, out=None):
+        """Y [T][d_out] with the current quantisation (prefill or decode)."""
+        torch = _torch()
+        x, dt, T, ldx = _x_args(X)
+        if X.shape[1] != self.d_in:
+            raise ValueError(f"X has {X.shape[1]} channels, the layer {self.d_in}")
+        out = torch.empty((T, self.d_out), dtype=X.dtype, device=X.device) if out is None else out
+        if out.dtype != X.dtype or out.dim() != 2 or out.stride(1) != 1 or out.shape != (T, self.d_out):
+            raise ValueError("out must be [T][d_out] with X's dtype and unit column stride")
+        ldy = out.stride(0) if T > 1 else self.d_out
+        check(load().ttq_linear(self._h, x, dt, T, ldx, ctypes.c_void_p(out.data_ptr()), ldy, _stream()),
+              "ttq_linear")
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            load().ttq_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,334 @@
+// libttq C ABI (include/ttq.h): argument validation, size queries, the
+// handle that carries one q_proj's quantisation from prefill to decode, and
+// dispatch to the HIP kernels.  Every check runs before anything is
+// enqueued, so a rejected call leaves every output untouched.  No C++
+// exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "../../include/ttq.h"
+#include "ttq_internal.h"
+
+struct ttq_handle {
+  ttq_config cfg;
+  ttq_buffers buf;
+  const void* wsrc;  // W (r = 0) or buf.wres (r > 0)
+  bool weight_bound;
+  bool prepared;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ttq_status fail(ttq_status s, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  g_last_error = msg;
+  return s;
+}
+
+ttq_status ok() {
+  g_last_error.clear();
+  return TTQ_OK;
+}
+
+ttq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define TTQ_NEED(ptr)                                                          \
+  do {                                                                         \
+    if ((ptr) == nullptr) return fail(TTQ_ERR_NULL, "%s is NULL", #ptr);       \
+    if (!aligned16(ptr)) return fail(TTQ_ERR_ALIGN, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+
+ttq_status check_qgr(int32_t q, int32_t g, int32_t r) {
+  if (q == 5) return fail(TTQ_ERR_UNSUPPORTED, "q=5 is not built for the GPU (oracle only)");
+  if (q < 2 || q > 4) return fail(TTQ_ERR_INVALID_ARG, "q=%d, expected 2, 3 or 4", q);
+  if (g == 16 || g == 8) return fail(TTQ_ERR_UNSUPPORTED, "group size %d (micro-scaling) is not built", g);
+  if (g != 32 && g != 64 && g != 128) return fail(TTQ_ERR_INVALID_ARG, "g=%d, expected 32, 64 or 128", g);
+  if (r < 0) return fail(TTQ_ERR_INVALID_ARG, "r=%d is negative", r);
+  if (r != 0 && r != 16) return fail(TTQ_ERR_UNSUPPORTED, "rank r=%d is not built (0 or 16)", r);
+  return TTQ_OK;
+}
+
+ttq_status check_dims(int64_t d_in, int64_t d_out, int32_t g) {
+  if (d_in <= 0 || d_in % 64 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld must be a positive multiple of 64", (long long)d_in);
+  if (d_in % g != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld is not a multiple of g=%d", (long long)d_in, g);
+  if (d_in > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_in=%lld too large", (long long)d_in);
+  if (d_out <= 0 || d_out % 4 != 0) return fail(TTQ_ERR_SHAPE, "d_out=%lld must be a positive multiple of 4", (long long)d_out);
+  if (d_out > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_out=%lld too large", (long long)d_out);
+  return TTQ_OK;
+}
+
+ttq_status check_stats(float alpha, float lambda, float p) {
+  if (!std::isfinite(alpha) || alpha < 0.f) return fail(TTQ_ERR_INVALID_ARG, "alpha=%g must be finite and >= 0", alpha);
+  if (!std::isfinite(p) || p <= 0.f) return fail(TTQ_ERR_INVALID_ARG, "p=%g must be finite and > 0", p);
+  if (!std::isfinite(lambda) || lambda < 0.f) return fail(TTQ_ERR_INVALID_ARG, "lambda=%g must be finite and >= 0", lambda);
+  if (lambda == 0.f && alpha != 0.f)
+    return fail(TTQ_ERR_INVALID_ARG, "lambda=0 with alpha>0 gives d_j=0 for a dead channel");
+  return TTQ_OK;
+}
+
+ttq_status check_cfg(const ttq_config* cfg) {
+  if (cfg == nullptr) return fail(TTQ_ERR_NULL, "cfg is NULL");
+  ttq_status s = check_qgr(cfg->q, cfg->g, cfg->r);
+  if (s != TTQ_OK) return s;
+  s = check_dims(cfg->d_in, cfg->d_out, cfg->g);
+  if (s != TTQ_OK) return s;
+  return check_stats(cfg->alpha, cfg->lambda, cfg->p);
+}
+
+ttq_status check_x(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx) {
+  if (xdt != TTQ_F16 && xdt != TTQ_F32) return fail(TTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)xdt);
+  if (T < 0) return fail(TTQ_ERR_SHAPE, "T=%lld is negative", (long long)T);
+  if (T > (int64_t(1) << 31)) return fail(TTQ_ERR_SHAPE, "T=%lld too large", (long long)T);
+  if (ldx < d) return fail(TTQ_ERR_SHAPE, "ldx=%lld < d=%lld", (long long)ldx, (long long)d);
+  if (ldx % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldx=%lld is not a multiple of 8", (long long)ldx);
+  if (T > 0) TTQ_NEED(X);
+  return TTQ_OK;
+}
+
+size_t colstats_ws_bytes(int64_t T, int64_t d) {
+  return (size_t)ttq::colstats_chunks(T < 1 ? 1 : T) * (size_t)d * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ttq_abi_version(void) { return TTQ_ABI_VERSION; }
+
+const char* ttq_status_string(ttq_status s) {
+  switch (s) {
+    case TTQ_OK: return "TTQ_OK";
+    case TTQ_ERR_INVALID_ARG: return "TTQ_ERR_INVALID_ARG: argument out of range";
+    case TTQ_ERR_UNSUPPORTED: return "TTQ_ERR_UNSUPPORTED: not built for the GPU";
+    case TTQ_ERR_SHAPE: return "TTQ_ERR_SHAPE: inconsistent sizes";
+    case TTQ_ERR_NULL: return "TTQ_ERR_NULL: required pointer is NULL";
+    case TTQ_ERR_ALIGN: return "TTQ_ERR_ALIGN: misaligned pointer or stride";
+    case TTQ_ERR_HIP: return "TTQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown ttq_status";
+}
+
+const char* ttq_last_error(void) { return g_last_error.c_str(); }
+
+size_t ttq_colstats_workspace_bytes(int64_t T, int64_t d) {
+  if (T < 0 || d <= 0) return 0;
+  return colstats_ws_bytes(T, d);
+}
+
+ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out) {
+  ttq_status s = check_cfg(cfg);
+  if (s != TTQ_OK) return s;
+  if (out == nullptr) return fail(TTQ_ERR_NULL, "out is NULL");
+  if (T_max < 1) return fail(TTQ_ERR_SHAPE, "T_max=%lld must be >= 1", (long long)T_max);
+  const size_t din = (size_t)cfg->d_in, dout = (size_t)cfg->d_out;
+  out->codes_bytes = dout * (din / 32) * (size_t)cfg->q * 4;
+  out->scales_bytes = dout * (din / (size_t)cfg->g) * 2;
+  out->zeros_bytes = out->scales_bytes;
+  out->d_bytes = din * 4;
+  out->dinvsqrt_bytes = din * 4;
+  out->wres_bytes = cfg->r > 0 ? dout * din * 2 : 0;
+  out->z_bytes = cfg->r > 0 ? (size_t)T_max * (size_t)cfg->r * 4 : 0;
+  out->workspace_bytes = colstats_ws_bytes(T_max, cfg->d_in);
+  return ok();
+}
+
+ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle** out) {
+  if (out == nullptr) return fail(TTQ_ERR_NULL, "out is NULL");
+  if (bufs == nullptr) return fail(TTQ_ERR_NULL, "bufs is NULL");
+  ttq_sizes sz;
+  ttq_status s = ttq_query_sizes(cfg, bufs->T_max, &sz);
+  if (s != TTQ_OK) return s;
+  TTQ_NEED(bufs->codes);
+  TTQ_NEED(bufs->scales);
+  TTQ_NEED(bufs->zeros);
+  TTQ_NEED(bufs->D);
+  TTQ_NEED(bufs->dinvsqrt);
+  TTQ_NEED(bufs->workspace);
+  if (bufs->workspace_bytes < sz.workspace_bytes)
+    return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", bufs->workspace_bytes, sz.workspace_bytes);
+  if (cfg->r > 0) {
+    TTQ_NEED(bufs->wres);
+    TTQ_NEED(bufs->B);
+    TTQ_NEED(bufs->A);
+    TTQ_NEED(bufs->z);
+  }
+  ttq_handle* h = new (std::nothrow) ttq_handle;
+  if (h == nullptr) return fail(TTQ_ERR_INVALID_ARG, "host allocation of the handle failed");
+  h->cfg = *cfg;
+  h->buf = *bufs;
+  h->wsrc = nullptr;
+  h->weight_bound = false;
+  h->prepared = false;
+  *out = h;
+  return ok();
+}
+
+void ttq_destroy(ttq_handle* h) { delete h; }
+
+ttq_status ttq_set_weight(ttq_handle* h, const void* W, void* stream) {
+  if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
+  TTQ_NEED(W);
+  if (h->cfg.r == 0) {
+    h->wsrc = W;
+    h->weight_bound = true;
+    return ok();
+  }
+  hipError_t e = ttq::launch_residual(h->cfg.d_out, h->cfg.d_in, h->cfg.r, W, h->buf.B, h->buf.A,
+                                      h->buf.wres, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "residual launch");
+  h->wsrc = h->buf.wres;
+  h->weight_bound = true;
+  return ok();
+}
+
+ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx, float p,
+                        float lambda, float alpha, float* D, float* dinvsqrt, float* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (d <= 0 || d % 8 != 0) return fail(TTQ_ERR_SHAPE, "d=%lld must be a positive multiple of 8", (long long)d);
+  ttq_status s = check_x(X, xdt, T, d, ldx);
+  if (s != TTQ_OK) return s;
+  if (T < 1) return fail(TTQ_ERR_SHAPE, "T=%lld: the statistic needs at least one token", (long long)T);
+  s = check_stats(alpha, lambda, p);
+  if (s != TTQ_OK) return s;
+  TTQ_NEED(D);
+  TTQ_NEED(dinvsqrt);
+  TTQ_NEED(workspace);
+  if (workspace_bytes < colstats_ws_bytes(T, d))
+    return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, colstats_ws_bytes(T, d));
+  hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, d, ldx, p, lambda, alpha, D, dinvsqrt,
+                                      workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, "colstats launch");
+}
+
+ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g, const void* W_src,
+                             const float* D, uint32_t* codes, void* scales, void* zeros,
+                             void* stream) {
+  ttq_status s = check_qgr(q, g, 0);
+  if (s != TTQ_OK) return s;
+  s = check_dims(d_in, d_out, g);
+  if (s != TTQ_OK) return s;
+  TTQ_NEED(W_src);
+  TTQ_NEED(D);
+  TTQ_NEED(codes);
+  TTQ_NEED(scales);
+  TTQ_NEED(zeros);
+  hipError_t e = ttq::launch_quantize_pack(d_out, d_in, q, g, W_src, D, codes, scales, zeros,
+                                           static_cast<hipStream_t>(stream));
+  return hip_status(e, "quantize_pack launch");
+}
+
+ttq_status ttq_residual(int32_t d_out, int32_t d_in, int32_t r, const void* W, const float* B,
+                        const float* A, void* W_res, void* stream) {
+  ttq_status s = check_dims(d_in, d_out, 32);
+  if (s != TTQ_OK) return s;
+  if (r != 16) return fail(r <= 0 ? TTQ_ERR_INVALID_ARG : TTQ_ERR_UNSUPPORTED, "r=%d, the residual kernel is built for r=16", r);
+  TTQ_NEED(W);
+  TTQ_NEED(B);
+  TTQ_NEED(A);
+  TTQ_NEED(W_res);
+  hipError_t e = ttq::launch_residual(d_out, d_in, r, W, B, A, W_res, static_cast<hipStream_t>(stream));
+  return hip_status(e, "residual launch");
+}
+
+ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_dtype xdt,
+                         int64_t ldx, const float* A, float* Z, void* stream) {
+  if (d_in <= 0 || d_in % 64 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%d must be a positive multiple of 64", d_in);
+  if (r != 16) return fail(r <= 0 ? TTQ_ERR_INVALID_ARG : TTQ_ERR_UNSUPPORTED, "r=%d, the kernel is built for r=16", r);
+  ttq_status s = check_x(X, xdt, T, d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (T == 0) return ok();
+  TTQ_NEED(A);
+  TTQ_NEED(Z);
+  hipError_t e = ttq::launch_lowrank_z(T, d_in, r, X, xdt == TTQ_F32, ldx, A, Z, static_cast<hipStream_t>(stream));
+  return hip_status(e, "lowrank_z launch");
+}
+
+ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g, int32_t r,
+                            const void* X, ttq_dtype xdt, int64_t ldx, const float* dinvsqrt,
+                            const uint32_t* codes, const void* scales, const void* zeros,
+                            const float* B, const float* Z, void* Y, int64_t ldy, void* stream) {
+  ttq_status s = check_qgr(q, g, r);
+  if (s != TTQ_OK) return s;
+  s = check_dims(d_in, d_out, g);
+  if (s != TTQ_OK) return s;
+  s = check_x(X, xdt, T, d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (ldy < d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%d", (long long)ldy, d_out);
+  if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
+  if (T == 0) return ok();
+  TTQ_NEED(dinvsqrt);
+  TTQ_NEED(codes);
+  TTQ_NEED(scales);
+  TTQ_NEED(zeros);
+  TTQ_NEED(Y);
+  if (r > 0) {
+    TTQ_NEED(B);
+    TTQ_NEED(Z);
+  }
+  hipError_t e = ttq::launch_wlowbit_gemm(T, d_in, d_out, q, g, r, X, xdt == TTQ_F32, ldx, dinvsqrt,
+                                          codes, scales, zeros, B, Z, Y, ldy,
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, "wlowbit_gemm launch");
+}
+
+ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
+                       void* stream) {
+  if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
+  if (!h->weight_bound) return fail(TTQ_ERR_INVALID_ARG, "ttq_set_weight has not been called");
+  const ttq_config& c = h->cfg;
+  ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (T < 1) return fail(TTQ_ERR_SHAPE, "T=%lld: prepare needs at least one token", (long long)T);
+  if (T > h->buf.T_max) return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld", (long long)T, (long long)h->buf.T_max);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.D,
+                                      h->buf.dinvsqrt, h->buf.workspace, st);
+  if (e != hipSuccess) return hip_status(e, "colstats launch");
+  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes,
+                                h->buf.scales, h->buf.zeros, st);
+  if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
+  h->prepared = true;
+  return ok();
+}
+
+ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
+                      void* Y, int64_t ldy, void* stream) {
+  if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
+  if (!h->prepared) return fail(TTQ_ERR_INVALID_ARG, "ttq_prepare has not been called on this handle");
+  const ttq_config& c = h->cfg;
+  ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (ldy < c.d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%d", (long long)ldy, c.d_out);
+  if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
+  if (c.r > 0 && T > h->buf.T_max)
+    return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld (Z buffer)", (long long)T, (long long)h->buf.T_max);
+  if (T == 0) return ok();
+  TTQ_NEED(Y);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c.r > 0) {
+    hipError_t e = ttq::launch_lowrank_z(T, c.d_in, c.r, X, xdt == TTQ_F32, ldx, h->buf.A, h->buf.z, st);
+    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
+  }
+  hipError_t e = ttq::launch_wlowbit_gemm(T, c.d_in, c.d_out, c.q, c.g, c.r, X, xdt == TTQ_F32, ldx,
+                                          h->buf.dinvsqrt, h->buf.codes, h->buf.scales, h->buf.zeros,
+                                          h->buf.B, h->buf.z, Y, ldy, st);
+  return hip_status(e, "wlowbit_gemm launch");
+}
+
+}  // extern "C"

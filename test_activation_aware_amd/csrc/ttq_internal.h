@@ -1,0 +1,33 @@
+// Internal declarations shared by the HIP sources of libttq (not part of the
+// public ABI in include/ttq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttq {
+
+// Column statistic: partial sums then a fixed-order finalize.
+constexpr int kColstatsMaxChunks = 128;      // row chunks of the partial pass
+int colstats_chunks(int64_t T);              // chunks used for T tokens
+hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx,
+                           float p, float lambda, float alpha, float* D, float* dinvsqrt,
+                           float* partial, hipStream_t s);
+
+hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W,
+                                const float* D, uint32_t* codes, void* scales, void* zeros,
+                                hipStream_t s);
+
+hipError_t launch_residual(int d_out, int d_in, int r, const void* W, const float* B,
+                           const float* A, void* W_res, hipStream_t s);
+
+hipError_t launch_lowrank_z(int64_t T, int d_in, int r, const void* X, bool x_f32, int64_t ldx,
+                            const float* A, float* Z, hipStream_t s);
+
+hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r,
+                               const void* X, bool x_f32, int64_t ldx, const float* dinvsqrt,
+                               const uint32_t* codes, const void* scales, const void* zeros,
+                               const float* B, const float* Z, void* Y, int64_t ldy,
+                               hipStream_t s);
+
+}  // namespace ttq

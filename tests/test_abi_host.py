@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/ttq.h declares, reports sizes, and rejects bad arguments with the
+documented status before enqueuing anything.  No call here reaches a kernel
+launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_activation_aware_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttq.h")
+
+# aligned, non-null stand-ins: validation never dereferences them
+P = ctypes.c_void_p(1 << 20)
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _capi.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_capi.SIGNATURES) == names
+
+
+def test_abi_version_and_status_text(lib):
+    assert lib.ttq_abi_version() == 1
+    for s in range(7):
+        assert lib.ttq_status_string(s).decode().startswith("TTQ_")
+    assert lib.ttq_status_string(99) == b"unknown ttq_status"
+
+
+def _cfg(d_in=5120, d_out=8192, q=4, g=32, r=0, alpha=0.5, lam=0.4, p=2.0):
+    return _capi.ttq_config(d_in, d_out, q, g, r, alpha, lam, p)
+
+
+def test_query_sizes_cfg5(lib):
+    sz = _capi.ttq_sizes()
+    assert lib.ttq_query_sizes(ctypes.byref(_cfg()), 16384, ctypes.byref(sz)) == 0
+    assert sz.codes_bytes == 8192 * 160 * 4 * 4          # 20.97 MB of 4-bit codes
+    assert sz.scales_bytes == sz.zeros_bytes == 8192 * 160 * 2
+    assert sz.d_bytes == sz.dinvsqrt_bytes == 5120 * 4
+    assert sz.wres_bytes == 0 and sz.z_bytes == 0
+    assert sz.workspace_bytes == lib.ttq_colstats_workspace_bytes(16384, 5120) > 0
+    assert lib.ttq_query_sizes(ctypes.byref(_cfg(r=16, q=2)), 100, ctypes.byref(sz)) == 0
+    assert sz.wres_bytes == 8192 * 5120 * 2 and sz.z_bytes == 100 * 16 * 4
+    assert sz.codes_bytes == 8192 * 160 * 2 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=5), _capi.TTQ_ERR_UNSUPPORTED),
+    (dict(q=1), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(q=8), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(g=16), _capi.TTQ_ERR_UNSUPPORTED),
+    (dict(g=48), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(r=8), _capi.TTQ_ERR_UNSUPPORTED),
+    (dict(r=-1), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(d_in=100), _capi.TTQ_ERR_SHAPE),
+    (dict(d_in=64, g=128), _capi.TTQ_ERR_SHAPE),
+    (dict(d_out=6), _capi.TTQ_ERR_SHAPE),
+    (dict(d_out=0), _capi.TTQ_ERR_SHAPE),
+    (dict(alpha=-0.1), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(p=0.0), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(lam=0.0), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(lam=0.0, alpha=0.0), _capi.TTQ_OK),
+])
+def test_config_validation(lib, kw, status):
+    sz = _capi.ttq_sizes()
+    got = lib.ttq_query_sizes(ctypes.byref(_cfg(**kw)), 16, ctypes.byref(sz))
+    assert got == status, lib.ttq_last_error()
+    if status:
+        assert lib.ttq_last_error() != b""
+
+
+def test_null_and_alignment(lib):
+    # quantize_pack: NULL W, misaligned D
+    assert lib.ttq_quantize_pack(64, 128, 4, 32, None, P, P, P, P, None) == _capi.TTQ_ERR_NULL
+    assert lib.ttq_quantize_pack(64, 128, 4, 32, P, MIS, P, P, P, None) == _capi.TTQ_ERR_ALIGN
+    # colstats: odd ldx, T = 0, lambda = 0 with alpha > 0, small workspace
+    assert lib.ttq_colstats(P, 1, 4, 128, 130, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_ALIGN
+    assert lib.ttq_colstats(P, 1, 0, 128, 128, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.0, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
+    assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 4, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_colstats(P, 7, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
+    # gemm: ldy too small, r = 16 without Z, T = 0 is an accepted no-op
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 1, 128, P, P, P, P, None, None, P, 32, None) \
+        == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 16, P, 1, 128, P, P, P, P, P, None, P, 64, None) \
+        == _capi.TTQ_ERR_NULL
+    assert lib.ttq_wlowbit_gemm(0, 128, 64, 4, 32, 0, None, 1, 128, None, None, None, None, None, None,
+                                None, 64, None) == _capi.TTQ_OK
+    # residual and lowrank_z are built for r = 16 only
+    assert lib.ttq_residual(64, 128, 8, P, P, P, P, None) == _capi.TTQ_ERR_UNSUPPORTED
+    assert lib.ttq_lowrank_z(4, 128, 0, P, 1, 128, P, P, None) == _capi.TTQ_ERR_INVALID_ARG
+    assert lib.ttq_lowrank_z(0, 128, 16, None, 1, 128, None, None, None) == _capi.TTQ_OK
+
+
+def _buffers(T_max, r=0, workspace_bytes=1 << 30):
+    z = P if r else None
+    return _capi.ttq_buffers(P.value, P.value, P.value, P.value, P.value, z and P.value,
+                             z and P.value, z and P.value, z and P.value, P.value, T_max, workspace_bytes)
+
+
+def test_handle_lifecycle_errors(lib):
+    h = ctypes.c_void_p()
+    cfg = _cfg(d_in=128, d_out=64)
+    bad = _buffers(16, workspace_bytes=4)
+    assert lib.ttq_create(ctypes.byref(cfg), ctypes.byref(bad), ctypes.byref(h)) == _capi.TTQ_ERR_SHAPE
+    cfg16 = _cfg(d_in=128, d_out=64, r=16)
+    assert lib.ttq_create(ctypes.byref(cfg16), ctypes.byref(_buffers(16)), ctypes.byref(h)) == _capi.TTQ_ERR_NULL
+    assert lib.ttq_create(ctypes.byref(cfg), ctypes.byref(_buffers(16)), ctypes.byref(h)) == _capi.TTQ_OK
+    try:
+        # prepare before the weight is bound, linear before prepare
+        assert lib.ttq_prepare(h, P, 1, 4, 128, None) == _capi.TTQ_ERR_INVALID_ARG
+        assert lib.ttq_linear(h, P, 1, 4, 128, P, 64, None) == _capi.TTQ_ERR_INVALID_ARG
+        # r = 0: binding the weight is pure host work (the handle borrows W)
+        assert lib.ttq_set_weight(h, P, None) == _capi.TTQ_OK
+        assert lib.ttq_set_weight(h, MIS, None) == _capi.TTQ_ERR_ALIGN
+        assert lib.ttq_prepare(h, P, 1, 0, 128, None) == _capi.TTQ_ERR_SHAPE
+        assert lib.ttq_prepare(h, P, 1, 17, 128, None) == _capi.TTQ_ERR_SHAPE   # > T_max
+        assert lib.ttq_prepare(h, P, 1, 4, 64, None) == _capi.TTQ_ERR_SHAPE     # ldx < d
+        assert lib.ttq_prepare(h, None, 1, 4, 128, None) == _capi.TTQ_ERR_NULL
+    finally:
+        lib.ttq_destroy(h)
+    lib.ttq_destroy(None)

@@ -1,0 +1,340 @@
+"""GPU parity: every kernel, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bars: D within 1e-5 relative; codes, scales and zeros bit-exact when the
+quantiser is given the oracle's fp32 D (and the same W_res); W_res bit-exact;
+Y within 1e-3 relative Frobenius error (fp16 operands, fp32 accumulation).
+Sizes span several tiles with ragged tails; the full configurations are
+checked on sampled outputs the oracle computes row by row."""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+import test_activation_aware_amd as ttq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-3
+D_TOL = 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ttq.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=8)
+def cfg_inputs(cfg, T=None, d_out=None, prompt=0):
+    return wl.config_inputs(cfg, prompt=prompt, T=T, d_out=d_out)
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+def oracle_dinvsqrt(D32):
+    return (1.0 / np.sqrt(D32.astype(np.float64))).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# colstats
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,T", [(1, 2048), (1, 333), (2, 2048), (3, 4096), (3, 1), (4, 8192),
+                                   (5, 16384), (5, 4097), (5, 31)])
+def test_colstats_parity(cfg, T):
+    w = wl.CONFIGS[cfg]
+    say(f"colstats cfg={cfg} T={T}")
+    X, _ = cfg_inputs(cfg, T=T, d_out=8)
+    Dg, Rg = ttq.ttq_colstats(dev(X), w.p, w.lam, w.alpha)
+    D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
+    Dg, Rg = host(Dg), host(Rg)
+    assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+    R0 = 1.0 / np.sqrt(D0.astype(np.float64))
+    assert np.max(np.abs(Rg - R0) / R0) <= D_TOL
+
+
+@pytest.mark.parametrize("p,alpha,lam", [(1.0, 0.5, 0.4), (1.5, 0.6, 0.4), (2.0, 0.0, 0.4),
+                                         (2.0, 0.75, 0.4), (2.0, 0.0, 0.0), (3.0, 0.5, 1.0)])
+def test_colstats_hyperparameters(p, alpha, lam):
+    say(f"colstats p={p} alpha={alpha} lam={lam}")
+    X, _ = cfg_inputs(4, T=1000, d_out=8)
+    Dg, _ = ttq.ttq_colstats(dev(X), p, lam, alpha)
+    Dg = host(Dg)
+    D0 = oracle.colstats(X, p, lam, alpha)
+    if alpha == 0.0:
+        assert np.all(Dg == 1.0)
+    assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+
+
+def test_colstats_deterministic_and_strided():
+    X, _ = cfg_inputs(3, T=3000, d_out=8)
+    Xd = dev(X)
+    a = host(ttq.ttq_colstats(Xd)[0])
+    b = host(ttq.ttq_colstats(Xd)[0])
+    assert a.tobytes() == b.tobytes()
+    # a strided view (ldx > d) gives the same statistic
+    wide = torch.zeros((X.shape[0], X.shape[1] + 64), dtype=Xd.dtype, device="cuda")
+    wide[:, :X.shape[1]] = Xd
+    c = host(ttq.ttq_colstats(wide[:, :X.shape[1]])[0])
+    assert a.tobytes() == c.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# quantize_pack: bit-exact given the oracle's D
+# ---------------------------------------------------------------------------
+def _check_quant(W16, D32, q, g, tag):
+    say(f"quantize {tag} q={q} g={g} shape={W16.shape}")
+    cg, sg, zg = ttq.ttq_quantize_pack(dev(W16), dev(D32), q, g)
+    c0, s0, z0 = oracle.quantize(W16, D32, q, g)
+    words0 = oracle.pack(c0, q)
+    cg = host(cg).view(np.uint32)
+    assert cg.shape == words0.shape
+    bad = np.argwhere(cg != words0)
+    assert bad.size == 0, f"{len(bad)} code words differ, first at {bad[:3].tolist()}"
+    assert host(sg).view(np.uint16).tobytes() == s0.view(np.uint16).tobytes(), "scales differ"
+    assert host(zg).view(np.uint16).tobytes() == z0.view(np.uint16).tobytes(), "zeros differ"
+
+
+@pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (2, 3, 32), (3, 4, 32), (3, 4, 64), (3, 4, 128),
+                                     (4, 4, 32), (5, 4, 32), (5, 2, 32)])
+def test_quantize_pack_bitexact(cfg, q, g):
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg)
+    D = oracle.colstats(X[:1024], w.p, w.lam, w.alpha)
+    if w.planted_rank:
+        B, A = oracle.svd_factors(W, w.planted_rank)
+        W = oracle.residual(W, B, A)
+    _check_quant(W, D, q, g, f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("q", [2, 3, 4])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_quantize_pack_edge_cases(q, g):
+    rng = np.random.default_rng(100 * q + g)
+    d_out, d = 96, 512
+    W = rng.standard_normal((d_out, d)) * 0.02
+    W[0] = 0.0                                       # all-zero rows / groups
+    W[1, :] = np.abs(W[1, :])                        # one-signed positive
+    W[2, :] = -np.abs(W[2, :])                       # one-signed negative
+    W[3, :] = 0.0123                                 # constant groups
+    W[4] = rng.standard_normal(d) * 1e-6             # scales in the fp16 subnormal range
+    W[5] = rng.standard_normal(d) * 1e-3
+    W[6] = rng.standard_normal(d) * 4.0              # large weights
+    W[7, :g] = 0.0
+    W[7, 0] = 6.1e-5                                 # lone tiny element
+    # exact-tie rows: values on a quarter grid with D = 1 put v/s on half-integers
+    for r in range(8, 24):
+        vals = rng.integers(-6, 25, size=d) * 0.25
+        vals[::g] = -1.5
+        vals[1::g] = 6.0
+        W[r] = vals
+    W16 = W.astype(np.float16)
+    D = np.exp(rng.standard_normal(d) * 2.0).astype(np.float32)
+    D[:] = np.where(np.arange(d) % 3 == 0, 1.0, D)   # exact ones next to wide-range values
+    _check_quant(W16, D, q, g, "edge")
+    _check_quant(W16, np.ones(d, np.float32), q, g, "edge-D1")
+    _check_quant(W16, np.full(d, 4.0, np.float32), q, g, "edge-D4")
+
+
+def test_quantize_ragged_rows():
+    # d_out not a multiple of the lanes' row stride
+    X, W = cfg_inputs(3)
+    D = oracle.colstats(X[:256], alpha=0.75)
+    _check_quant(W[:52], D, 4, 32, "rows52")
+    _check_quant(W[:4], D, 3, 128, "rows4")
+
+
+# ---------------------------------------------------------------------------
+# residual and low-rank Z
+# ---------------------------------------------------------------------------
+def test_residual_bitexact_cfg2():
+    _, W = cfg_inputs(2)
+    B, A = oracle.svd_factors(W, 16)
+    say("residual cfg2")
+    Rg = host(ttq.ttq_residual(dev(W), dev(B), dev(A)))
+    R0 = oracle.residual(W, B, A)
+    assert Rg.view(np.uint16).tobytes() == R0.view(np.uint16).tobytes()
+
+
+def test_residual_bitexact_cfg5_shape():
+    _, W = cfg_inputs(5, T=8)
+    rng = np.random.default_rng(7)
+    # factors of SVD scale (sigma_1 of an 8192x5120 N(0, 0.01^2) matrix is about 1.7)
+    B = (rng.standard_normal((W.shape[0], 16)) * 0.013).astype(np.float32)
+    A = (rng.standard_normal((16, W.shape[1])) * 0.018).astype(np.float32)
+    say("residual cfg5 shape")
+    Rg = host(ttq.ttq_residual(dev(W), dev(B), dev(A)))
+    R0 = oracle.residual(W, B, A)
+    assert Rg.view(np.uint16).tobytes() == R0.view(np.uint16).tobytes()
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 2048), (4, 333), (5, 16384), (1, 100)])
+def test_lowrank_z(cfg, T):
+    X, W = cfg_inputs(cfg, T=T, d_out=64)
+    A = (np.random.default_rng(cfg).standard_normal((16, X.shape[1])) * 0.02).astype(np.float32)
+    say(f"lowrank_z cfg={cfg} T={T}")
+    Zg = host(ttq.ttq_lowrank_z(dev(X), dev(A)))
+    Z0 = X.astype(np.float64) @ A.astype(np.float64).T
+    assert rel_fro(Zg, Z0) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# wlowbit_gemm given the oracle's codes
+# ---------------------------------------------------------------------------
+def _gemm_case(cfg, T, q, g, r, sample_rows=None):
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg, T=T)
+    D = oracle.colstats(X, w.p, w.lam, w.alpha)
+    B, A = (oracle.svd_factors(W, r) if r and cfg <= 3 else (None, None))
+    if r and B is None:
+        rng = np.random.default_rng(cfg)
+        B = (rng.standard_normal((W.shape[0], r)) * 0.013).astype(np.float32)
+        A = (rng.standard_normal((r, W.shape[1])) * 0.018).astype(np.float32)
+    Wq = oracle.residual(W, B, A) if r else W
+    c, s, z = oracle.quantize(Wq, D, q, g)
+    say(f"gemm cfg={cfg} T={T} q={q} g={g} r={r}")
+    Xd = dev(X)
+    Zd = ttq.ttq_lowrank_z(Xd, dev(A)) if r else None
+    Yd = ttq.ttq_wlowbit_gemm(Xd, dev(oracle_dinvsqrt(D)), dev(oracle.pack(c, q)), dev(s), dev(z), q, g,
+                              W.shape[0], B=dev(B) if r else None, Z=Zd)
+    Yg = host(Yd)
+    assert Yg.dtype == X.dtype and Yg.shape == (T, W.shape[0])
+    rows = np.arange(T) if sample_rows is None else sample_rows
+    Y0 = oracle.linear(X[rows], c, s, z, D, g, B, A)
+    err = rel_fro(Yg[rows], Y0)
+    say(f"  rel_fro={err:.3e}")
+    assert np.all(np.isfinite(Yg[rows]))
+    assert err <= Y_TOL
+    return err
+
+
+@pytest.mark.parametrize("cfg,T,q,g,r", [
+    (1, 333, 4, 32, 0), (1, 2048, 4, 32, 0),
+    (2, 2048, 3, 32, 16), (2, 1, 3, 32, 16), (2, 300, 3, 32, 0),
+    (3, 1000, 4, 32, 0), (3, 1000, 4, 64, 0), (3, 1000, 4, 128, 0), (3, 257, 2, 64, 0), (3, 100, 3, 128, 16),
+    (4, 777, 4, 32, 0), (4, 513, 4, 32, 16),
+])
+def test_gemm_parity(cfg, T, q, g, r):
+    _gemm_case(cfg, T, q, g, r)
+
+
+@pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16)])
+def test_gemm_parity_full_cfg5_sampled(q, r):
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 16383],
+                                     np.random.default_rng(3).integers(0, 16384, 59)]))
+    _gemm_case(5, 16384, q, 32, r, sample_rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# end to end through the handle API (prepare once, project prefill + decode)
+# ---------------------------------------------------------------------------
+def _e2e(cfg, q, g, r, T=None, prompt=0, sample_rows=None, alpha=None, decode_T=()):
+    w = wl.CONFIGS[cfg]
+    alpha = w.alpha if alpha is None else alpha
+    X, W = cfg_inputs(cfg, T=T, prompt=prompt)
+    T = X.shape[0]
+    B = A = None
+    if r:
+        B, A = oracle.svd_factors(W, r)
+    say(f"e2e cfg={cfg} q={q} g={g} r={r} T={T} prompt={prompt} alpha={alpha}")
+    layer = ttq.TTQLinear(dev(W), q=q, g=g, alpha=alpha, lam=w.lam, p=w.p, r=r, T_max=T, B=B, A=A)
+    Xd = dev(X)
+    layer.prepare(Xd)
+    Yg = host(layer.linear(Xd))
+    D0 = oracle.colstats(X, w.p, w.lam, alpha)
+    Dg = host(layer.D)
+    assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+    Wq = oracle.residual(W, B, A) if r else W
+    c0, s0, z0 = oracle.quantize(Wq, D0, q, g)
+    cg = oracle.unpack(host(layer.codes).view(np.uint32), q, W.shape[1])
+    agree = np.mean(cg == c0)
+    say(f"  code agreement with the oracle's own D: {agree:.6f}")
+    assert agree >= 0.999
+    rows = np.arange(T) if sample_rows is None else sample_rows
+    Y0 = oracle.linear(X[rows], c0, s0, z0, D0, g, B, A)
+    err = rel_fro(Yg[rows], Y0)
+    say(f"  prefill rel_fro={err:.3e}")
+    assert err <= Y_TOL
+    for Td in decode_T:
+        Xn = wl.decode_inputs(cfg, Td, step=Td)
+        Yn = host(layer.linear(dev(Xn)))
+        e = rel_fro(Yn, oracle.linear(Xn, c0, s0, z0, D0, g, B, A))
+        say(f"  decode T={Td} rel_fro={e:.3e}")
+        assert e <= Y_TOL
+    layer.close()
+
+
+def test_e2e_cfg1():
+    _e2e(1, 4, 32, 0)
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.0])
+def test_e2e_cfg2_lowrank(alpha):
+    _e2e(2, 3, 32, 16, alpha=alpha)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_e2e_cfg3_groupsize(g):
+    _e2e(3, 4, g, 0, T=2048)
+
+
+@pytest.mark.parametrize("prompt", [0, 1, 2, 3])
+def test_e2e_cfg4_prompts(prompt):
+    rows = np.random.default_rng(prompt).integers(0, 8192, 96)
+    _e2e(4, 4, 32, 0, prompt=prompt, sample_rows=rows)
+
+
+@pytest.mark.parametrize("q", [4, 2])
+def test_e2e_cfg5_prefill_and_decode(q):
+    rows = np.random.default_rng(9).integers(0, 16384, 64)
+    _e2e(5, q, 32, 0, sample_rows=rows, decode_T=(1, 16, 64))
+
+
+def test_alpha_zero_gives_rtn_on_gpu():
+    X, W = cfg_inputs(2, T=512)
+    layer = ttq.TTQLinear(dev(W), q=3, g=32, alpha=0.0, lam=0.4, r=0, T_max=512)
+    layer.prepare(dev(X))
+    assert np.all(host(layer.D) == 1.0)
+    c0, s0, z0 = oracle.quantize(W, np.ones(W.shape[1], np.float32), 3, 32)
+    assert host(layer.codes).view(np.uint32).tobytes() == oracle.pack(c0, 3).tobytes()
+    assert host(layer.scales).view(np.uint16).tobytes() == s0.view(np.uint16).tobytes()
+    layer.close()
+
+
+def test_prepare_and_linear_deterministic():
+    X, W = cfg_inputs(3, T=1024)
+    layer = ttq.TTQLinear(dev(W), q=4, g=32, alpha=0.75, r=0, T_max=1024)
+    Xd = dev(X)
+    layer.prepare(Xd)
+    c1, y1 = host(layer.codes).tobytes(), host(layer.linear(Xd)).tobytes()
+    layer.prepare(Xd)
+    c2, y2 = host(layer.codes).tobytes(), host(layer.linear(Xd)).tobytes()
+    assert c1 == c2 and y1 == y2
+    assert host(layer.linear(Xd[:0])).shape == (0, W.shape[0])
+    layer.close()
