@@ -115,6 +115,7 @@ def weight(cfg: int, d_out: int, d: int, sigma: float, planted_rank: int = 0,
     ||P||_F = planted_rel_norm * ||G||_F, G being the Gaussian part.  All
     its k singular values equal c."""
     G = _rng(cfg, ROLE_W).standard_normal((d_out, d)) * sigma
+    planted_rank = min(planted_rank, d_out, d)   # tiny test shapes
     if planted_rank:
         rng = _rng(cfg, ROLE_PLANTED)
         U, _ = np.linalg.qr(rng.standard_normal((d_out, planted_rank)))
