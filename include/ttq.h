@@ -36,11 +36,19 @@
  *     not checked.
  *   - No C++ exception crosses this interface.
  *
- * Packed code format (the pages fix none): per output row, blocks of 32
- * consecutive input channels; each block is q little-endian uint32 words that
- * form one bitstream, code k of the block occupying bits [q*k, q*k+q).
- * codes is [d_out][d_in/32][q] uint32; scales and zeros are [d_out][d_in/g]
- * fp16 (zeros hold exact integers 0..2^q-1).
+ * Packed code format (the pages fix none).  Codes: per output row, blocks
+ * of 32 consecutive input channels; each block is q little-endian uint32
+ * words forming one bitstream, code k of the block at bits [q*k, q*k+q).
+ * The words are stored in a tiled order, so that one 64-channel step of 32
+ * output rows is one contiguous chunk of 32 * 2q words:
+ *   word w of block b of row n  ->  index ((nt * (d_in/64) + ks) * 32 + r) * 2q + pos
+ *   nt = n / 32, r = n % 32, ks = b / 2, h = b % 2,
+ *   pos = 4*(w % 2) + 2*h + w/2 for q = 4 (words b0w0 b0w2 b1w0 b1w2 b0w1
+ *   b0w3 b1w1 b1w3), pos = q*h + w for q = 2, 3.
+ * Scales and zeros (fp16, zeros exact integers 0..2^q-1), one per row n and
+ * group gi of g channels, are stored at index (nt * (d_in/g) + gi) * 32 + r.
+ * codes hold d_out * (d_in/32) * q uint32; scales and zeros d_out * (d_in/g)
+ * fp16 each.
  */
 #ifndef TTQ_H
 #define TTQ_H
@@ -72,7 +80,7 @@ typedef enum ttq_dtype {
 /* Hyper-parameters of one q_proj.  Fixed per layer, no test-time search
  * (paper-daily.com section 2: alpha 0.5-0.75, lambda 0.4, p = 2).
  *   d_in  (d)  input channels,  multiple of 64 and of g
- *   d_out (d') output channels, multiple of 4
+ *   d_out (d') output channels, multiple of 32
  *   q  bits per code: 2, 3 or 4 on the GPU
  *   g  group size along d_in: 32, 64 or 128
  *   r  low-rank rank: 0 or 16
@@ -92,9 +100,9 @@ typedef struct ttq_config {
 /* Byte sizes of every caller-owned buffer for a configuration and the
  * largest T a handle will see. */
 typedef struct ttq_sizes {
-  size_t codes_bytes;     /* uint32 [d_out][d_in/32][q]                  */
-  size_t scales_bytes;    /* fp16   [d_out][d_in/g]                      */
-  size_t zeros_bytes;     /* fp16   [d_out][d_in/g]                      */
+  size_t codes_bytes;     /* uint32, d_out * (d_in/32) * q, tiled order  */
+  size_t scales_bytes;    /* fp16, d_out * (d_in/g), tiled order         */
+  size_t zeros_bytes;     /* fp16, d_out * (d_in/g), tiled order         */
   size_t d_bytes;         /* fp32   [d_in]   D                           */
   size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2)                    */
   size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */

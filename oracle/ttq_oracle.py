@@ -33,6 +33,7 @@ import numpy as np
 __all__ = [
     "colstats", "colstats_f64", "svd_factors", "residual", "quantize", "pack",
     "unpack", "dequant", "linear", "linear_dense", "rtn_reference_levels",
+    "tiled_code_index", "tile_codes", "untile_codes", "tile_groups", "untile_groups",
 ]
 
 
@@ -222,6 +223,75 @@ def unpack(words, q: int, d: int) -> np.ndarray:
             val |= wd[:, :, w + 1] << np.uint64(32 - off)
         out[:, :, k] = val & mask
     return out.reshape(d_out, d).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# O4b  Tiled storage order of the packed codes and of the group parameters
+# ---------------------------------------------------------------------------
+# The pages fix no storage order.  The library stores the canonical words of
+# pack() in a tiled order so that one 64-channel step of 32 output rows is one
+# contiguous chunk.  This is a pure permutation of words (no bit changes):
+#
+#   canonical word (row n, 32-channel block b, word w), 0 <= w < q
+#   nt = n // 32, r = n % 32        row tile and row inside it
+#   ks = b // 2,  h = b % 2         64-channel step and block inside it
+#   pos = 4*(w % 2) + 2*h + w // 2  when q == 4, else q*h + w
+#   index = ((nt * (d/64) + ks) * 32 + r) * 2q + pos
+#
+# For q = 4 the 8 words of one row and step are stored as
+# b0w0 b0w2 b1w0 b1w2 b0w1 b0w3 b1w1 b1w3.  Scales and zeros (one value per
+# row and group gi) go to index (nt * (d/g) + gi) * 32 + r.
+
+def tiled_code_index(n, b, w, q: int, d: int):
+    """Flat tiled index of canonical word (n, b, w); numpy-broadcastable."""
+    n = np.asarray(n, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    w = np.asarray(w, dtype=np.int64)
+    nt, r = n // 32, n % 32
+    ks, h = b // 2, b % 2
+    if q == 4:
+        pos = 4 * (w % 2) + 2 * h + w // 2
+    else:
+        pos = q * h + w
+    return ((nt * (d // 64) + ks) * 32 + r) * (2 * q) + pos
+
+
+def tile_codes(words, q: int) -> np.ndarray:
+    """Canonical [d'][d/32][q] words -> flat tiled uint32 array."""
+    words = np.asarray(words, dtype=np.uint32)
+    d_out, nb, qq = words.shape
+    if qq != q or d_out % 32 or nb % 2:
+        raise ValueError("tiling needs d' % 32 == 0 and d % 64 == 0")
+    n, b, w = np.meshgrid(np.arange(d_out), np.arange(nb), np.arange(q), indexing="ij")
+    out = np.zeros(words.size, dtype=np.uint32)
+    out[tiled_code_index(n, b, w, q, nb * 32)] = words
+    return out
+
+
+def untile_codes(flat, q: int, d_out: int, d: int) -> np.ndarray:
+    """Inverse of tile_codes."""
+    flat = np.asarray(flat, dtype=np.uint32).reshape(-1)
+    n, b, w = np.meshgrid(np.arange(d_out), np.arange(d // 32), np.arange(q), indexing="ij")
+    return flat[tiled_code_index(n, b, w, q, d)]
+
+
+def tile_groups(vals) -> np.ndarray:
+    """[d'][ng] per-group values (scales or zeros) -> flat tiled array."""
+    vals = np.asarray(vals)
+    d_out, ng = vals.shape
+    if d_out % 32:
+        raise ValueError("tiling needs d' % 32 == 0")
+    n, gi = np.meshgrid(np.arange(d_out), np.arange(ng), indexing="ij")
+    out = np.zeros(vals.size, dtype=vals.dtype)
+    out[((n // 32) * ng + gi) * 32 + n % 32] = vals
+    return out
+
+
+def untile_groups(flat, d_out: int, ng: int) -> np.ndarray:
+    """Inverse of tile_groups."""
+    flat = np.asarray(flat).reshape(-1)
+    n, gi = np.meshgrid(np.arange(d_out), np.arange(ng), indexing="ij")
+    return flat[((n // 32) * ng + gi) * 32 + n % 32]
 
 
 # ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 __all__ = [
     "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
     "ttq_residual", "ttq_lowrank_z", "ttq_wlowbit_gemm", "ttq_query_sizes",
-    "ttq_colstats_workspace_bytes", "ttq_abi_version",
+    "ttq_colstats_workspace_bytes", "ttq_abi_version", "code_shape", "group_shape",
 ]
 
 
@@ -112,14 +112,25 @@ def ttq_colstats(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5, D=None
     return D, dinvsqrt
 
 
+def code_shape(d_out: int, d_in: int, q: int):
+    """Shape of the packed codes in the tiled order: [d'/32][d/64][32][2q]."""
+    return (d_out // 32, d_in // 64, 32, 2 * q)
+
+
+def group_shape(d_out: int, d_in: int, g: int):
+    """Shape of the scales / zeros in the tiled order: [d'/32][d/g][32]."""
+    return (d_out // 32, d_in // g, 32)
+
+
 def ttq_quantize_pack(W, D, q: int, g: int, codes=None, scales=None, zeros=None):
-    """codes uint32 [d'][d/32][q] (as int32), scales, zeros fp16 [d'][d/g]."""
+    """Packed codes (uint32 stored as int32) and fp16 scales, zeros, all in the
+    tiled order of include/ttq.h."""
     torch = _torch()
     d_out, d_in = W.shape
     dev = W.device
-    codes = torch.empty((d_out, d_in // 32, q), dtype=torch.int32, device=dev) if codes is None else codes
-    scales = torch.empty((d_out, d_in // g), dtype=torch.float16, device=dev) if scales is None else scales
-    zeros = torch.empty((d_out, d_in // g), dtype=torch.float16, device=dev) if zeros is None else zeros
+    codes = torch.empty(code_shape(d_out, d_in, q), dtype=torch.int32, device=dev) if codes is None else codes
+    scales = torch.empty(group_shape(d_out, d_in, g), dtype=torch.float16, device=dev) if scales is None else scales
+    zeros = torch.empty(group_shape(d_out, d_in, g), dtype=torch.float16, device=dev) if zeros is None else zeros
     check(load().ttq_quantize_pack(d_out, d_in, q, g, _dev(W, "W", torch.float16),
                                    _dev(D, "D", torch.float32), _dev(codes, "codes", torch.int32),
                                    _dev(scales, "scales", torch.float16),
@@ -220,9 +231,9 @@ class TTQLinear:
         check(lib.ttq_query_sizes(ctypes.byref(self._cfg), T_max, ctypes.byref(sz)), "ttq_query_sizes")
         dev = W.device
         self.W = W
-        self.codes = torch.empty((self.d_out, self.d_in // 32, q), dtype=torch.int32, device=dev)
-        self.scales = torch.empty((self.d_out, self.d_in // g), dtype=torch.float16, device=dev)
-        self.zeros = torch.empty((self.d_out, self.d_in // g), dtype=torch.float16, device=dev)
+        self.codes = torch.empty(code_shape(self.d_out, self.d_in, q), dtype=torch.int32, device=dev)
+        self.scales = torch.empty(group_shape(self.d_out, self.d_in, g), dtype=torch.float16, device=dev)
+        self.zeros = torch.empty(group_shape(self.d_out, self.d_in, g), dtype=torch.float16, device=dev)
         self.D = torch.empty(self.d_in, dtype=torch.float32, device=dev)
         self.dinvsqrt = torch.empty(self.d_in, dtype=torch.float32, device=dev)
         self.workspace = torch.empty(max(1, sz.workspace_bytes // 4), dtype=torch.float32, device=dev)

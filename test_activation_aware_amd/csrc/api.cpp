@@ -68,7 +68,7 @@ ttq_status check_dims(int64_t d_in, int64_t d_out, int32_t g) {
   if (d_in <= 0 || d_in % 64 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld must be a positive multiple of 64", (long long)d_in);
   if (d_in % g != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld is not a multiple of g=%d", (long long)d_in, g);
   if (d_in > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_in=%lld too large", (long long)d_in);
-  if (d_out <= 0 || d_out % 4 != 0) return fail(TTQ_ERR_SHAPE, "d_out=%lld must be a positive multiple of 4", (long long)d_out);
+  if (d_out <= 0 || d_out % 32 != 0) return fail(TTQ_ERR_SHAPE, "d_out=%lld must be a positive multiple of 32", (long long)d_out);
   if (d_out > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_out=%lld too large", (long long)d_out);
   return TTQ_OK;
 }

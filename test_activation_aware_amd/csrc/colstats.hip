@@ -9,9 +9,10 @@
 //     columns (one 16-byte load per row) and the 4 waves take interleaved
 //     rows of the chunk.  Lane sums stay in fp32 registers, the 4 waves are
 //     combined through LDS and one partial per (chunk, column) is written.
-//   pass 2 (colstats_finalize): one thread per column sums the chunk
-//     partials in chunk order in fp64, divides by T, adds lambda, raises to
-//     alpha and rounds once to fp32.  No atomics: bitwise deterministic.
+//   pass 2 (colstats_finalize): per column, 8 threads sum interleaved slices
+//     of the chunk partials in fp64 and the slices are combined in a fixed
+//     order; then divide by T, add lambda, raise to alpha, round once to
+//     fp32.  No atomics: bitwise deterministic.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -89,15 +90,27 @@ __global__ __launch_bounds__(kThreads) void colstats_partial(const TX* __restric
   }
 }
 
+// 256 threads = 32 columns x 8 slices of the chunk list; slice w sums chunks
+// w, w+8, w+16, ... and the 8 slice sums are added in slice order.
 __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict__ partial, int chunks,
                                                          int64_t d, int64_t T, double lambda,
                                                          double alpha, float* __restrict__ D,
                                                          float* __restrict__ dinvsqrt) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d) return;
+  const int cx = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int64_t j = (int64_t)blockIdx.x * 32 + cx;
   double s = 0.0;
-  for (int c = 0; c < chunks; ++c) s += (double)partial[(int64_t)c * d + j];
-  const double m = s / (double)T;
+  if (j < d) {
+#pragma unroll 4
+    for (int c = sl; c < chunks; c += 8) s += (double)partial[(int64_t)c * d + j];
+  }
+  __shared__ double red[8][32];
+  red[sl][cx] = s;
+  __syncthreads();
+  if (sl != 0 || j >= d) return;
+  double t = red[0][cx];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) t += red[w][cx];
+  const double m = t / (double)T;
   const float dj = (float)pow(m + lambda, alpha);
   D[j] = dj;
   dinvsqrt[j] = (float)(1.0 / sqrt((double)dj));
@@ -119,7 +132,7 @@ hipError_t launch_typed(const void* X, int64_t T, int64_t d, int64_t ldx, float 
     hipLaunchKernelGGL((colstats_partial<TX, 0>), grid, dim3(kThreads), 0, s, x, T, d, ldx, rows, p, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(colstats_finalize, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, partial,
+  hipLaunchKernelGGL(colstats_finalize, dim3((unsigned)((d + 31) / 32)), dim3(256), 0, s, partial,
                      chunks, d, T, (double)lambda, (double)alpha, D, dinvsqrt);
   return hipGetLastError();
 }

@@ -13,12 +13,19 @@
 //   z    = clamp(rint(-mn / s), 0, N)   round half to even
 //   c    = clamp(rint(v / s) + z, 0, N)
 //
-// Work split: one lane owns one block of 32 consecutive input channels and
-// keeps the same block for every row it visits, so its 32 sqrt(D) values are
-// computed once and stay in registers.  A group of g = 64 or 128 channels is
-// 2 or 4 adjacent lanes; their min/max meet through lane shuffles.  Lanes of
-// a wave read 64 consecutive 64-byte blocks (4 KB contiguous) and write their
-// q packed words contiguously: the kernel streams W once (HBM-bound).
+// Output is in the tiled storage order (32-row tiles, one contiguous chunk
+// per 64-channel step; see include/ttq.h).
+//
+// Work split: a workgroup of 256 threads owns 256 input channels (8 blocks
+// of 32) and walks 32-row tiles of W.  Per tile:
+//   * the 32 x 256 fp16 slab (16 KB) comes in with 16-byte loads, two full
+//     rows per wave instruction, and is parked in LDS (the next tile's loads
+//     are issued before this tile is processed);
+//   * thread (r, b) = (row in tile, 32-channel block) quantises its block
+//     from LDS with the 32 sqrt(D) values the workgroup computed once;
+//     groups of 64 / 128 channels meet through an LDS min/max exchange;
+//   * codes are placed in LDS in the tiled order and leave as one contiguous
+//     store of 4 steps x 32 rows x 2q words; scales and zeros likewise.
 //
 // Codes use a reciprocal fast path: with r = 1/s (one IEEE division per
 // group), u = fma(v, r, z) lies within 2^-18 of v/s + z, so whenever u is
@@ -33,15 +40,8 @@ namespace ttq {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ float lane_min(float v, int width) {
-  for (int o = 1; o < width; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float lane_max(float v, int width) {
-  for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+constexpr int kCols = 256;             // channels per workgroup
+constexpr int kRowPitch = kCols + 8;   // fp16 elements per LDS row (pad: 16 bytes)
 
 // smallest positive fp16 that is >= x (x >= 0, finite)
 __device__ __forceinline__ _Float16 fp16_round_up(float x) {
@@ -52,95 +52,150 @@ __device__ __forceinline__ _Float16 fp16_round_up(float x) {
   return __builtin_bit_cast(_Float16, b);
 }
 
+// position of canonical word w of block-in-step h inside a row's 2q step words
+template <int Q>
+__device__ __forceinline__ constexpr int step_pos(int h, int w) {
+  if constexpr (Q == 4) return 4 * (w % 2) + 2 * h + w / 2;
+  else return Q * h + w;
+}
+
 template <int Q, int G>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
-    const _Float16* __restrict__ W, const float* __restrict__ D, int d_out, int nb,
-    int64_t rows_in_flight, uint32_t* __restrict__ codes, _Float16* __restrict__ scales,
+    const _Float16* __restrict__ W, const float* __restrict__ D, int d_out, int d_in,
+    int tiles_per_wg, uint32_t* __restrict__ codes, _Float16* __restrict__ scales,
     _Float16* __restrict__ zeros) {
-  constexpr int LPG = G / 32;  // lanes per group
+  constexpr int LPG = G / 32;               // blocks per group
   constexpr float N = (float)((1 << Q) - 1);
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (t >= (int64_t)nb * rows_in_flight) return;  // whole groups leave together
-  const int b = (int)(t % nb);
-  const int64_t row0 = t / nb;
-  const int64_t d = (int64_t)nb * 32;
-  const int ng = nb / LPG;
+  constexpr int SW = 2 * Q;                 // words per row per 64-channel step
+  constexpr int GPW = kCols / G;            // groups per workgroup column range
 
-  float sq[32];
-  {
-    const float4* dp = reinterpret_cast<const float4*>(D + (int64_t)b * 32);
+  __shared__ __attribute__((aligned(16))) _Float16 wt[32 * kRowPitch];
+  __shared__ float sq[kCols];
+  __shared__ __attribute__((aligned(16))) uint32_t outc[4 * 32 * SW];
+  __shared__ _Float16 outs[GPW * 32], outz[GPW * 32];
+  __shared__ float red_mn[8][32], red_mx[8][32];
+
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * kCols;
+  const int width = min(kCols, d_in - c0);  // 64, 128, 192 or 256
+  const int n_tiles = d_out / 32;
+  const int t_begin = blockIdx.y * tiles_per_wg;
+  const int t_end = min(n_tiles, t_begin + tiles_per_wg);
+
+  // sqrt(D) of this workgroup's channels, correctly rounded, once
+  if (tid < width) sq[tid] = sqrtf(D[c0 + tid]);
+
+  // slab loader: 1024 16-byte pieces, piece p -> row p / 32, column 8 * (p % 32)
+  uint4 pre[4];
+  auto load_tile = [&](int nt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float4 v = dp[i];
-      sq[4 * i + 0] = sqrtf(v.x);
-      sq[4 * i + 1] = sqrtf(v.y);
-      sq[4 * i + 2] = sqrtf(v.z);
-      sq[4 * i + 3] = sqrtf(v.w);
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + i * kThreads;
+      const int row = p >> 5, col = (p & 31) * 8;
+      if (col < width)
+        pre[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(nt * 32 + row) * d_in + c0 + col);
     }
-  }
+  };
+  if (t_begin < t_end) load_tile(t_begin);
 
-  for (int64_t row = row0; row < d_out; row += rows_in_flight) {
-    const uint4* wp = reinterpret_cast<const uint4*>(W + row * d + (int64_t)b * 32);
-    uint4 raw[4];
+  // this thread's block: r = row in tile, bl = block in the column range
+  const int r = tid & 31, bl = tid >> 5;
+  const bool active = 32 * bl < width;
+  const int h = bl & 1, ksl = bl >> 1;
+
+  for (int nt = t_begin; nt < t_end; ++nt) {
+    __syncthreads();  // previous tile's LDS reads and stores are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = wp[i];
-    const _Float16* w = reinterpret_cast<const _Float16*>(raw);
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + i * kThreads;
+      const int row = p >> 5, col = (p & 31) * 8;
+      if (col < width) *reinterpret_cast<uint4*>(&wt[row * kRowPitch + col]) = pre[i];
+    }
+    __syncthreads();
+    if (nt + 1 < t_end) load_tile(nt + 1);
 
     float v[32];
     float mn = 0.f, mx = 0.f;
+    if (active) {
+      const _Float16* src = &wt[r * kRowPitch + bl * 32];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      v[k] = (float)w[k] * sq[k];
-      mn = fminf(mn, v[k]);
-      mx = fmaxf(mx, v[k]);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * i);
+        const _Float16* e = reinterpret_cast<const _Float16*>(&raw);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[8 * i + k] = (float)e[k] * sq[bl * 32 + 8 * i + k];
+          mn = fminf(mn, v[8 * i + k]);
+          mx = fmaxf(mx, v[8 * i + k]);
+        }
+      }
     }
     if constexpr (LPG > 1) {
-      mn = lane_min(mn, LPG);
-      mx = lane_max(mx, LPG);
+      red_mn[bl][r] = mn;
+      red_mx[bl][r] = mx;
+      __syncthreads();
+      const int first = bl & ~(LPG - 1);
+#pragma unroll
+      for (int j = 0; j < LPG; ++j) {
+        mn = fminf(mn, red_mn[first + j][r]);
+        mx = fmaxf(mx, red_mx[first + j][r]);
+      }
     }
 
-    float s, zf;
-    _Float16 s16;
-    if (mx == mn) {  // all-zero group
-      s16 = (_Float16)1.0f;
-      s = 1.0f;
-      zf = 0.0f;
-    } else {
-      const float s32 = (mx - mn) / N;
-      s16 = fp16_round_up(s32);
-      s = (float)s16;
-      zf = fminf(fmaxf(rintf(-mn / s), 0.0f), N) + 0.0f;
-    }
-    const float rcp = 1.0f / s;
+    if (active) {
+      float s, zf;
+      _Float16 s16;
+      if (mx == mn) {  // all-zero group
+        s16 = (_Float16)1.0f;
+        s = 1.0f;
+        zf = 0.0f;
+      } else {
+        const float s32 = (mx - mn) / N;
+        s16 = fp16_round_up(s32);
+        s = (float)s16;
+        zf = fminf(fmaxf(rintf(-mn / s), 0.0f), N) + 0.0f;
+      }
+      const float rcp = 1.0f / s;
 
-    uint32_t word[Q];
+      uint32_t word[Q];
 #pragma unroll
-    for (int i = 0; i < Q; ++i) word[i] = 0u;
+      for (int i = 0; i < Q; ++i) word[i] = 0u;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float u = __builtin_fmaf(v[k], rcp, zf);
-      float c = rintf(u);
-      if (fabsf(u - c) > 0.5f - 0x1p-16f) c = rintf(v[k] / s) + zf;  // near a tie: exact path
-      c = fminf(fmaxf(c, 0.0f), N);
-      const uint32_t ci = (uint32_t)c;
-      const int bit = Q * k;
-      word[bit >> 5] |= ci << (bit & 31);
-      if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
+      for (int k = 0; k < 32; ++k) {
+        const float u = __builtin_fmaf(v[k], rcp, zf);
+        float c = rintf(u);
+        if (fabsf(u - c) > 0.5f - 0x1p-16f) c = rintf(v[k] / s) + zf;  // near a tie: exact path
+        c = fminf(fmaxf(c, 0.0f), N);
+        const uint32_t ci = (uint32_t)c;
+        const int bit = Q * k;
+        word[bit >> 5] |= ci << (bit & 31);
+        if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
+      }
+      uint32_t* dst = &outc[(ksl * 32 + r) * SW];
+#pragma unroll
+      for (int w = 0; w < Q; ++w) dst[step_pos<Q>(h, w)] = word[w];
+      if ((bl % LPG) == 0) {
+        outs[(bl / LPG) * 32 + r] = s16;
+        outz[(bl / LPG) * 32 + r] = (_Float16)zf;
+      }
     }
+    __syncthreads();
 
-    uint32_t* cp = codes + (row * nb + b) * Q;
-    if constexpr (Q == 4) {
-      *reinterpret_cast<uint4*>(cp) = make_uint4(word[0], word[1], word[2], word[3]);
-    } else if constexpr (Q == 2) {
-      *reinterpret_cast<uint2*>(cp) = make_uint2(word[0], word[1]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < Q; ++i) cp[i] = word[i];
+    // codes: steps [c0/64, c0/64 + width/64) of tile nt are contiguous
+    {
+      const int words = (width / 64) * 32 * SW;
+      uint32_t* gdst = codes + ((int64_t)nt * (d_in / 64) + c0 / 64) * 32 * SW;
+      for (int i = tid; i < words / 4; i += kThreads)
+        reinterpret_cast<uint4*>(gdst)[i] = reinterpret_cast<const uint4*>(outc)[i];
     }
-    if ((b % LPG) == 0) {
-      const int64_t gi = row * ng + b / LPG;
-      scales[gi] = s16;
-      zeros[gi] = (_Float16)zf;
+    // scales / zeros: groups [c0/G, c0/G + width/G) of tile nt are contiguous
+    {
+      const int n = (width / G) * 32;
+      const int64_t off = ((int64_t)nt * (d_in / G) + c0 / G) * 32;
+      for (int i = tid; i < n; i += kThreads) {
+        scales[off + i] = outs[i];
+        zeros[off + i] = outz[i];
+      }
     }
   }
 }
@@ -148,24 +203,25 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
 template <int Q>
 hipError_t launch_q(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
                     _Float16* scales, _Float16* zeros, hipStream_t s) {
-  const int nb = d_in / 32;
-  // rows visited per lane: about 8, so each lane's sqrt(D) work is amortised
-  int64_t rows_in_flight = (d_out + 7) / 8;
-  if (rows_in_flight < 1) rows_in_flight = 1;
-  const int64_t threads = (int64_t)nb * rows_in_flight;
-  const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+  const int col_wgs = (d_in + kCols - 1) / kCols;
+  const int n_tiles = d_out / 32;
+  // about 8 row tiles per workgroup, but enough workgroups to fill the chip
+  int per = 8;
+  while (per > 1 && (int64_t)col_wgs * ((n_tiles + per - 1) / per) < 1024) per >>= 1;
+  const int row_wgs = (n_tiles + per - 1) / per;
+  dim3 grid((unsigned)col_wgs, (unsigned)row_wgs);
   switch (g) {
     case 32:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 32>), dim3(blocks), dim3(kThreads), 0, s, W, D,
-                         d_out, nb, rows_in_flight, codes, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_kernel<Q, 32>), grid, dim3(kThreads), 0, s, W, D, d_out, d_in,
+                         per, codes, scales, zeros);
       break;
     case 64:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 64>), dim3(blocks), dim3(kThreads), 0, s, W, D,
-                         d_out, nb, rows_in_flight, codes, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_kernel<Q, 64>), grid, dim3(kThreads), 0, s, W, D, d_out, d_in,
+                         per, codes, scales, zeros);
       break;
     default:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 128>), dim3(blocks), dim3(kThreads), 0, s, W, D,
-                         d_out, nb, rows_in_flight, codes, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_kernel<Q, 128>), grid, dim3(kThreads), 0, s, W, D, d_out, d_in,
+                         per, codes, scales, zeros);
       break;
   }
   return hipGetLastError();

@@ -7,30 +7,40 @@
 // that fuses the pre-scaling of X).
 //
 // CDNA4 design (gfx950, wave64, MFMA v_mfma_f32_32x32x16_f16):
-//   * One workgroup = 4 waves computes a BN x BM tile of Y^T (BN output
-//     channels x BM tokens); waves are arranged 2 x 2, each owning a
-//     (BN/2) x (BM/2) sub-tile as 32x32 MFMA fragments with fp32 accumulators.
-//   * The MFMA "A" operand is the dequantised weight (rows = output channels),
-//     "B" is the pre-scaled input (columns = tokens).  Accumulator lanes then
-//     hold 4 consecutive output channels of one token: 8- or 16-byte stores.
-//   * K loop in steps of 64 input channels, double-buffered in LDS:
-//       X tile    BM x 64 fp16, pre-scaled by D^(-1/2) in fp32 and rounded once
-//                 to fp16 on its way from HBM to LDS (v_fma_mix), stored in a
-//                 q-specific channel order (below) with an XOR swizzle of the
-//                 16-byte chunks against LDS bank conflicts;
-//       codes     BN rows x 2 blocks x q words, odd row stride;
-//       s, z      BN rows x (64/g or 1) pairs (s, -(1024 + z)) as fp16.
-//     The next step's global loads are issued before the current step's MFMAs.
-//   * Dequantisation in registers: a code nibble c is turned into the fp16
-//     1024 + c by OR-ing the exponent bits 0x6400, two codes per 32-bit
-//     register; (1024 + c) - (1024 + z) = c - z is exact, times s gives the
-//     fp16 weight with one rounding (packed fp16 add and multiply).
-//   * The OR trick naturally pairs code j with code j+4 (q = 3, 4) or j+8
-//     (q = 2) of the same word; the MFMA only needs A and B to agree on the
-//     channel order, so the X tile is stored in that same permuted order.
+//   * A workgroup of 4 waves computes a 256 (output channels) x 128 (tokens)
+//     tile of Y^T; wave w owns channels [64w, 64w + 64) x all 128 tokens as
+//     2 x 4 fragments of 32x32 with fp32 accumulators.  Two workgroups fit on
+//     a CU (<= 256 registers per lane, ~53 KB LDS each), so one workgroup's
+//     loads and barrier overlap the other's MFMAs.
+//   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
+//     input (columns = tokens): accumulator lanes hold 4 consecutive output
+//     channels of one token, stored as 8 or 16 bytes.
+//   * K loop in steps of 64 input channels, two LDS stages:
+//       codes, scales, zeros  come straight from HBM into LDS
+//                 (global_load_lds_dwordx4): in the tiled storage order one
+//                 step of one 32-row tile is a contiguous chunk, so every
+//                 wave instruction moves contiguous bytes;
+//       X         8 lanes per 128-byte row segment -> registers -> multiplied
+//                 by D^(-1/2) in fp32 and rounded to fp16 (one v_fma_mix per
+//                 element) -> LDS, in a permuted channel order with an XOR
+//                 swizzle of 16-byte chunks (conflict-free both ways);
+//       D^(-1/2)  64 floats per step through a two-slot LDS ring.
+//     Loads for step k+1 are issued before the MFMAs of step k.
+//   * Rows past T or d_out are read clamped to valid rows; a token's output
+//     depends only on its own row, and padding outputs are never stored.
+//   * Dequantisation in registers: code c becomes the fp16 1024 + c by OR-ing
+//     the exponent bits 0x6400 (v_and_or_b32, two codes per register);
+//     (1024 + c) - (1024 + z) = c - z exactly, times s gives the fp16 weight
+//     with one rounding (packed fp16 add and multiply).  The OR trick pairs
+//     code j with code j+4 of each 8-code group, so the X tile is stored in
+//     the channel order 0 4 1 5 2 6 3 7 within every 8 channels: the MFMA
+//     only needs A and B to agree on the order of the reduction.
 //   * Rank-r term: before the K loop each fragment gets two extra MFMAs,
-//     B16 x Z_hi and B16 x Z_lo, with Z = Z_hi + Z_lo split into two fp16
-//     parts so the fp32 Z keeps about 22 bits.
+//     B16 x Z_hi and B16 x Z_lo with Z = Z_hi + Z_lo split into two fp16
+//     parts, so the fp32 Z keeps about 22 bits.
+//   * Workgroup ids go round-robin over the 8 XCDs; ids are regrouped so each
+//     XCD gets a contiguous band of tiles, walked in groups of 4 token tiles
+//     x all channel tiles, keeping the XCD's L2 on few X rows and W rows.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -42,44 +52,64 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;
-
-// Position p (0..15) inside a 16-channel chunk of the X tile -> channel.
-template <int Q>
-__device__ __forceinline__ constexpr int chunk_perm(int p) {
-  const int h = p >> 3, i = p & 7;
-  if constexpr (Q == 2) return 4 * h + (i >> 1) + ((i & 1) ? 8 : 0);
-  else return 8 * h + (i >> 1) + ((i & 1) ? 4 : 0);
-}
-
-// The 4 code pairs a lane feeds to one MFMA, as fp16 1024 + c in each half.
-// `wrow` points at the row's 2*Q words (two 32-channel blocks) in LDS;
-// s = 16-channel sub-step (0..3) of the 64-channel step, hh = lane half.
-template <int Q>
-__device__ __forceinline__ void code_pairs(const uint32_t* wrow, int s, int hh, uint32_t out[4]) {
-  const int kb = s >> 1, half = s & 1;
-  if constexpr (Q == 4) {
-    const uint32_t u = wrow[kb * 4 + 2 * half + hh];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = ((u >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-  } else if constexpr (Q == 2) {
-    const uint32_t u = wrow[kb * 2 + half] >> (8 * hh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = ((u >> (2 * j)) & 0x00030003u) | 0x64006400u;
-  } else {
-    const int bit = 3 * (16 * half + 8 * hh);  // 0, 24, 48, 72
-    const int w = bit >> 5, off = bit & 31;
-    const uint32_t lo = wrow[kb * 3 + w];
-    const uint32_t hi = (w < 2) ? wrow[kb * 3 + w + 1] : 0u;
-    const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)off);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      out[j] = ((win >> (3 * j)) & 7u) | (((win >> (3 * j + 12)) & 7u) << 16) | 0x64006400u;
-  }
-}
+constexpr int BN = 256;  // output channels per workgroup
+constexpr int BM = 128;  // tokens per workgroup
+constexpr int BK = 64;   // input channels per step
+constexpr int FN = 2;    // 32-row fragments per wave
+constexpr int FM = 4;    // 32-token fragments per wave
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// (a & m) | o in one VOP3 instruction (all operands in VGPRs)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// fp16 pair (low half of xa times da, low half of xb times db) or the high
+// halves (HI = 1): one v_fma_mix per element, fp32 product rounded to fp16
+template <int HI>
+__device__ __forceinline__ uint32_t mix_pair(uint32_t xa, uint32_t xb, float da, float db) {
+  uint32_t r;
+  if constexpr (HI == 0) {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(xa), "v"(da));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(xb), "v"(db));
+  } else {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(xa), "v"(da));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(xb), "v"(db));
+  }
+  return r;
+}
+
+// The 4 code pairs (fp16 1024 + c in each half) a lane feeds to one MFMA.
+// `rw` holds the row's step words as read from LDS (q = 4: this lane half's
+// 4 words, one per sub-step; q = 2: the 4 words of the step; q = 3: the 6
+// words of the step); s = 16-channel sub-step, hh = lane half.
+template <int Q>
+__device__ __forceinline__ void code_pairs(const uint32_t* rw, int s, int hh, uint32_t mask,
+                                           uint32_t magic, uint32_t out[4]) {
+  uint32_t u;
+  if constexpr (Q == 4) {
+    u = rw[s];
+  } else if constexpr (Q == 2) {
+    // the 8 two-bit codes of this lane half; spread its two bytes 16 bits apart
+    u = __builtin_amdgcn_perm(0u, rw[s] >> (16 * hh), 0x0C010C00u);
+  } else {
+    const int bit = 3 * (16 * (s & 1) + 8 * hh);  // 0, 24, 48, 72 within the block
+    const int w = bit >> 5, off = bit & 31;
+    const uint32_t lo = rw[3 * (s >> 1) + w];
+    const uint32_t hi = (w < 2) ? rw[3 * (s >> 1) + w + 1] : 0u;
+    const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)off);  // 8 codes, 24 bits
+    u = (win & 0xFFFu) | ((win << 4) & 0x0FFF0000u);                       // codes 4..7 to bit 16
+  }
+  constexpr int SH = (Q == 4) ? 4 : (Q == 3 ? 3 : 2);
+  out[0] = and_or(u, mask, magic);
+#pragma unroll
+  for (int j = 1; j < 4; ++j) out[j] = and_or(u >> (SH * j), mask, magic);
+}
 
 template <typename TX>
 __device__ __forceinline__ void store4(TX* p, const float* v) {
@@ -92,38 +122,51 @@ __device__ __forceinline__ void store4(TX* p, const float* v) {
   }
 }
 
-template <int Q, int G, typename TX, bool LOWRANK, int BN, int BM>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+// 16 bytes per lane from global memory into LDS; lane l lands at
+// lds_wave_base + 16 * l (the base is the same for the whole wave)
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int Q, int G, typename TX, bool LOWRANK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ X, int64_t ldx,
                          const float* __restrict__ dinvsqrt, const uint32_t* __restrict__ codes,
                          const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
                          const float* __restrict__ Bf, const float* __restrict__ Z,
-                         TX* __restrict__ Y, int64_t ldy, int tiles_n) {
-  constexpr int TN = BN / 2, TM = BM / 2;  // wave sub-tile
-  constexpr int FN = TN / 32, FM = TM / 32;
-  constexpr int GPK = (G <= BK) ? BK / G : 1;  // groups per K step
-  constexpr int WSTR = 2 * Q + 1;               // LDS words per code row (odd)
-  constexpr int XU = BM * 4 / kThreads;         // 16-channel X units per thread
-  constexpr int XV = 16 * (int)sizeof(TX) / 16; // 16-byte loads per unit
-  static_assert(BM * 4 % kThreads == 0, "X tile split");
-  static_assert(BN <= kThreads, "one code row per thread");
+                         TX* __restrict__ Y, int64_t ldy, int tiles_n, int tiles) {
+  constexpr int GPK = (G <= BK) ? BK / G : 1;   // groups per step
+  constexpr int SW = 2 * Q;                      // code words per row per step
+  constexpr int CW = 8 * 32 * SW;                // code words per step (8 row tiles)
+  constexpr int SZ = 8 * GPK * 32;               // scales (and zeros) per step
+  constexpr int XV = (int)sizeof(TX) / 2;        // 16-byte loads per 8 channels
 
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * BK];
-  __shared__ uint32_t ws[2][BN * WSTR];
-  __shared__ uint32_t szs[2][BN * GPK];
+  __shared__ __attribute__((aligned(16))) uint32_t cs[2][CW];
+  __shared__ __attribute__((aligned(16))) _Float16 szs[2][2 * SZ];  // scales then zeros
+  __shared__ __attribute__((aligned(16))) float dvs[2][BK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int tile = blockIdx.x;
-  const int tn = tile % tiles_n, tm = tile / tiles_n;
+  int tile = blockIdx.x;
+  if (tiles % kXcds == 0) tile = (tile % kXcds) * (tiles / kXcds) + tile / kXcds;
+  constexpr int kGroupM = 4;
+  const int tiles_m = tiles / tiles_n;
+  const int first_m = (tile / (kGroupM * tiles_n)) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = tile % (kGroupM * tiles_n);
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
   const int n0 = tn * BN;
   const int64_t m0 = (int64_t)tm * BM;
-  const int nb = d_in / 32;
+  const int ksteps = d_in / BK;
   const int ng = d_in / G;
-  const int KT = d_in / BK;
+  const int ntile0 = n0 / 32, ntiles = d_out / 32;
+
+  uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);  // code bits
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(mask), "+v"(magic));  // keep both in VGPRs for v_and_or_b32
 
   f16x acc[FN][FM];
 #pragma unroll
@@ -134,26 +177,29 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   if constexpr (LOWRANK) {
-    // B (fp32 [d_out][16]) -> fp16 A operand; Z (fp32 [T][16]) -> hi/lo fp16 B operands
     h8 bfr[FN];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const int n = n0 + wn * TN + i * 32 + l32;
-      const float* bp = Bf + (int64_t)min(n, d_out - 1) * 16 + 8 * hh;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bfr[i][e] = (_Float16)(n < d_out ? bp[e] : 0.f);
+      const int n = min(n0 + wave * 64 + i * 32 + l32, d_out - 1);
+      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
+      const float4 b0 = bp[0], b1 = bp[1];
+      bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
+      bfr[i][2] = (_Float16)b0.z; bfr[i][3] = (_Float16)b0.w;
+      bfr[i][4] = (_Float16)b1.x; bfr[i][5] = (_Float16)b1.y;
+      bfr[i][6] = (_Float16)b1.z; bfr[i][7] = (_Float16)b1.w;
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t t = m0 + wm * TM + j * 32 + l32;
+      const int64_t t = min(m0 + j * 32 + l32, T - 1);
+      const float4* zp = reinterpret_cast<const float4*>(Z + t * 16 + 8 * hh);
+      const float4 z0 = zp[0], z1 = zp[1];
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
       h8 zh, zl;
-      const float* zp = Z + min(t, T - 1) * 16 + 8 * hh;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float zv = t < T ? zp[e] : 0.f;
-        const _Float16 hv = (_Float16)zv;
+        const _Float16 hv = (_Float16)zv[e];
         zh[e] = hv;
-        zl[e] = (_Float16)(zv - (float)hv);
+        zl[e] = (_Float16)(zv[e] - (float)hv);
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
@@ -163,107 +209,154 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
     }
   }
 
-  // ---- global -> register staging ----
-  uint4 xr[XU][XV];
-  float dv[16];
-  uint32_t wr[2 * Q];
-  uint32_t sr[GPK];
-  const int xc = tid & 3;  // this thread's 16-channel chunk inside the 64-channel step
+  // ---- X staging: thread -> 8-channel chunk xc, rows (tid >> 3) + 32u ----
+  const int xc = tid & 7;
+  const TX* xrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t t = min(m0 + (tid >> 3) + 32 * u, T - 1);
+    xrow[u] = X + t * ldx + 8 * xc;
+  }
+  uint4 xr[4][XV];
+  float4 dvr = make_float4(0.f, 0.f, 0.f, 0.f);  // D^(-1/2) of the step after next (threads < 16)
 
-  auto load_stage = [&](int kt) {
+  // direct-to-LDS pieces of one step: codes, then scales and zeros
+  auto dma_step = [&](int kt, int buf) {
+    // codes: a tile's step chunk is 32 * 2Q words = 16Q slots of 16 bytes;
+    // slot p -> row tile p / 16Q, words 4 (p % 16Q) of that chunk
+#pragma unroll
+    for (int j = 0; j < (CW / 4 + kThreads - 1) / kThreads; ++j) {
+      const int base = (wave + 4 * j) * 64;  // first slot of this wave instruction
+      if (base < CW / 4) {
+        const int p = base + lane;
+        const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
+        const uint32_t* g = codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q));
+        if (p < CW / 4) lds_dma16(g, &cs[buf][4 * base]);
+      }
+    }
+    // scales and zeros: SZ halfs each, in slots of 8 halfs; slot p < SLOTS -> scales
+    constexpr int SLOTS = SZ / 8;
+    const int gk = (kt * BK) / G;
+#pragma unroll
+    for (int j = 0; j < (2 * SLOTS + kThreads - 1) / kThreads; ++j) {
+      const int base = (wave + 4 * j) * 64;
+      if (base < 2 * SLOTS) {
+        const int p = base + lane;
+        const int arr = p / SLOTS, q8 = p % SLOTS;
+        const int t = min(ntile0 + q8 / (4 * GPK), ntiles - 1);
+        const int within = 8 * (q8 % (4 * GPK));  // halfs inside the tile's GPK x 32 chunk
+        const _Float16* src = (arr == 0 ? scales : zeros) + ((int64_t)t * ng + gk) * 32 + within;
+        if (p < 2 * SLOTS) lds_dma16(src, &szs[buf][8 * base]);
+      }
+    }
+  };
+
+  auto load_x = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int row = (tid + u * kThreads) >> 2;
-      const int64_t t = m0 + row;
-      const TX* src = X + min(t, T - 1) * ldx + k0 + xc * 16;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int v = 0; v < XV; ++v) {
-        uint4 val = reinterpret_cast<const uint4*>(src)[v];
-        if (t >= T) val = make_uint4(0u, 0u, 0u, 0u);
-        xr[u][v] = val;
+      for (int v = 0; v < XV; ++v) xr[u][v] = reinterpret_cast<const uint4*>(xrow[u] + k0)[v];
+  };
+
+  auto store_x = [&](int buf) {
+    const float4 da = *reinterpret_cast<const float4*>(&dvs[buf][8 * xc]);
+    const float4 db = *reinterpret_cast<const float4*>(&dvs[buf][8 * xc + 4]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = (tid >> 3) + 32 * u;
+      uint32_t o[4];
+      if constexpr (sizeof(TX) == 2) {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&xr[u][0]);
+        // channel pairs (0,4) (1,5) (2,6) (3,7): halves of words (0,2) (0,2) (1,3) (1,3)
+        o[0] = mix_pair<0>(w[0], w[2], da.x, db.x);
+        o[1] = mix_pair<1>(w[0], w[2], da.y, db.y);
+        o[2] = mix_pair<0>(w[1], w[3], da.z, db.z);
+        o[3] = mix_pair<1>(w[1], w[3], da.w, db.w);
+      } else {
+        const float* e = reinterpret_cast<const float*>(&xr[u][0]);
+        const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          h2 y = {(_Float16)(e[p] * dd[p]), (_Float16)(e[p + 4] * dd[p + 4])};
+          o[p] = as_u32(y);
+        }
       }
-    }
-    const float4* dp = reinterpret_cast<const float4*>(dinvsqrt + k0 + xc * 16);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 f = dp[v];
-      dv[4 * v + 0] = f.x;
-      dv[4 * v + 1] = f.y;
-      dv[4 * v + 2] = f.z;
-      dv[4 * v + 3] = f.w;
-    }
-    if (tid < BN) {
-      const int n = min(n0 + tid, d_out - 1);
-      const uint32_t* cp = codes + ((int64_t)n * nb + kt * 2) * Q;
-#pragma unroll
-      for (int i = 0; i < 2 * Q; ++i) wr[i] = cp[i];
-      const int gk = (kt * BK) / G;
-#pragma unroll
-      for (int i = 0; i < GPK; ++i) {
-        const _Float16 s = scales[(int64_t)n * ng + gk + i];
-        const _Float16 z = zeros[(int64_t)n * ng + gk + i];
-        h2 p = {s, (_Float16)(-((float)z + 1024.0f))};
-        sr[i] = as_u32(p);
-      }
+      *reinterpret_cast<uint4*>(&xs[buf][row * BK + ((xc ^ (row & 7)) * 8)]) =
+          make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
 
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int row = (tid + u * kThreads) >> 2;
-      const TX* e = reinterpret_cast<const TX*>(&xr[u][0]);
-      uint32_t out[8];
-#pragma unroll
-      for (int p = 0; p < 16; p += 2) {
-        const int k0 = chunk_perm<Q>(p), k1 = chunk_perm<Q>(p + 1);
-        h2 y = {(_Float16)((float)e[k0] * dv[k0]), (_Float16)((float)e[k1] * dv[k1])};
-        out[p >> 1] = as_u32(y);
-      }
-      // two 16-byte chunks (8 channels each) at XOR-swizzled positions
-      const int c0 = (2 * xc) ^ (row & 7), c1 = (2 * xc + 1) ^ (row & 7);
-      *reinterpret_cast<uint4*>(&xs[buf][row * BK + c0 * 8]) = make_uint4(out[0], out[1], out[2], out[3]);
-      *reinterpret_cast<uint4*>(&xs[buf][row * BK + c1 * 8]) = make_uint4(out[4], out[5], out[6], out[7]);
-    }
-    if (tid < BN) {
-#pragma unroll
-      for (int i = 0; i < 2 * Q; ++i) ws[buf][tid * WSTR + i] = wr[i];
-#pragma unroll
-      for (int i = 0; i < GPK; ++i) szs[buf][tid * GPK + i] = sr[i];
-    }
-  };
-
-  load_stage(0);
-  store_stage(0);
+  // ---- prologue: D^(-1/2) of steps 0 and 1, stage 0 ----
+  if (tid < 16) {
+    *reinterpret_cast<float4*>(&dvs[0][4 * tid]) = reinterpret_cast<const float4*>(dinvsqrt)[tid];
+    if (ksteps > 1) dvr = reinterpret_cast<const float4*>(dinvsqrt + BK)[tid];
+  }
+  dma_step(0, 0);
+  load_x(0);
+  __syncthreads();
+  store_x(0);
+  if (tid < 16 && ksteps > 1) *reinterpret_cast<float4*>(&dvs[1][4 * tid]) = dvr;
   __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < ksteps; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) load_stage(kt + 1);
+    if (kt + 1 < ksteps) {
+      dma_step(kt + 1, buf ^ 1);
+      load_x(kt + 1);
+      if (tid < 16 && kt + 2 < ksteps)
+        dvr = reinterpret_cast<const float4*>(dinvsqrt + (kt + 2) * BK)[tid];
+    }
+
+    // this wave's code words and group parameters for the step
+    uint32_t rw[FN][(Q == 3) ? 6 : 4];
+    h2 sc[FN][GPK], nz[FN][GPK];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int tl = wave * 2 + i;  // row tile inside the workgroup
+      const uint32_t* rowp = &cs[buf][(tl * 32 + l32) * SW];
+      if constexpr (Q == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rowp + 4 * hh);
+        rw[i][0] = v.x; rw[i][1] = v.y; rw[i][2] = v.z; rw[i][3] = v.w;
+      } else if constexpr (Q == 2) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rowp);
+        rw[i][0] = v.x; rw[i][1] = v.y; rw[i][2] = v.z; rw[i][3] = v.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const uint2 v = *reinterpret_cast<const uint2*>(rowp + 2 * k);
+          rw[i][2 * k] = v.x;
+          rw[i][2 * k + 1] = v.y;
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < GPK; ++gi) {
+        const _Float16 s = szs[buf][(tl * GPK + gi) * 32 + l32];
+        const _Float16 z = szs[buf][SZ + (tl * GPK + gi) * 32 + l32];
+        const _Float16 n = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
+        sc[i][gi] = h2{s, s};
+        nz[i][gi] = h2{n, n};
+      }
+    }
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       h8 bx[FM];
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int row = wm * TM + j * 32 + l32;
+        const int row = j * 32 + l32;
         const int c = (2 * s + hh) ^ (row & 7);
         bx[j] = *reinterpret_cast<const h8*>(&xs[buf][row * BK + c * 8]);
       }
       const int gi = (G == 32) ? (s >> 1) : 0;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
-        const int nr = wn * TN + i * 32 + l32;
         uint32_t pr[4];
-        code_pairs<Q>(&ws[buf][nr * WSTR], s, hh, pr);
-        const h2 sz = as_h2(szs[buf][nr * GPK + gi]);
-        const h2 sc = {sz[0], sz[0]};
-        const h2 nz = {sz[1], sz[1]};
+        code_pairs<Q>(rw[i], s, hh, mask, magic, pr);
         h8 a;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const h2 wv = (as_h2(pr[j]) + nz) * sc;
+          const h2 wv = (as_h2(pr[j]) + nz[i][gi]) * sc[i][gi];
           a[2 * j] = wv[0];
           a[2 * j + 1] = wv[1];
         }
@@ -273,20 +366,23 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
       }
     }
 
-    if (kt + 1 < KT) store_stage(buf ^ 1);
+    if (kt + 1 < ksteps) {
+      store_x(buf ^ 1);
+      if (tid < 16 && kt + 2 < ksteps) *reinterpret_cast<float4*>(&dvs[buf][4 * tid]) = dvr;
+    }
     __syncthreads();
   }
 
   // ---- epilogue: lane holds token t = l32, channels 8*(e/4) + 4*hh + e%4 ----
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int64_t t = m0 + wm * TM + j * 32 + l32;
+    const int64_t t = m0 + j * 32 + l32;
     if (t >= T) continue;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int n = n0 + wn * TN + i * 32 + 8 * e4 + 4 * hh;
+        const int n = n0 + wave * 64 + i * 32 + 8 * e4 + 4 * hh;
         if (n < d_out) {
           float v[4] = {acc[i][j][4 * e4 + 0], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
                         acc[i][j][4 * e4 + 3]};
@@ -301,14 +397,13 @@ template <int Q, int G, typename TX, bool LR>
 hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
                       const uint32_t* codes, const void* scales, const void* zeros,
                       const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
-  constexpr int BN = 256, BM = 256;
   const int tiles_n = (d_out + BN - 1) / BN;
   const int64_t tiles_m = (T + BM - 1) / BM;
   const int64_t tiles = tiles_n * tiles_m;
-  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TX, LR, BN, BM>), dim3((unsigned)tiles), dim3(kThreads),
-                     0, s, T, d_in, d_out, static_cast<const TX*>(X), ldx, dinv, codes,
+  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TX, LR>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
+                     d_in, d_out, static_cast<const TX*>(X), ldx, dinv, codes,
                      static_cast<const _Float16*>(scales), static_cast<const _Float16*>(zeros), B, Z,
-                     static_cast<TX*>(Y), ldy, tiles_n);
+                     static_cast<TX*>(Y), ldy, tiles_n, (int)tiles);
   return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ def test_query_sizes_cfg5(lib):
     (dict(d_in=100), _capi.TTQ_ERR_SHAPE),
     (dict(d_in=64, g=128), _capi.TTQ_ERR_SHAPE),
     (dict(d_out=6), _capi.TTQ_ERR_SHAPE),
+    (dict(d_out=48), _capi.TTQ_ERR_SHAPE),
     (dict(d_out=0), _capi.TTQ_ERR_SHAPE),
     (dict(alpha=-0.1), _capi.TTQ_ERR_INVALID_ARG),
     (dict(alpha=float("nan")), _capi.TTQ_ERR_INVALID_ARG),
@@ -90,6 +91,7 @@ def test_config_validation(lib, kw, status):
 def test_null_and_alignment(lib):
     # quantize_pack: NULL W, misaligned D
     assert lib.ttq_quantize_pack(64, 128, 4, 32, None, P, P, P, P, None) == _capi.TTQ_ERR_NULL
+    assert lib.ttq_quantize_pack(40, 128, 4, 32, P, P, P, P, P, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_quantize_pack(64, 128, 4, 32, P, MIS, P, P, P, None) == _capi.TTQ_ERR_ALIGN
     # colstats: odd ldx, T = 0, lambda = 0 with alpha > 0, small workspace
     assert lib.ttq_colstats(P, 1, 4, 128, 130, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_ALIGN

@@ -112,13 +112,13 @@ def _check_quant(W16, D32, q, g, tag):
     say(f"quantize {tag} q={q} g={g} shape={W16.shape}")
     cg, sg, zg = ttq.ttq_quantize_pack(dev(W16), dev(D32), q, g)
     c0, s0, z0 = oracle.quantize(W16, D32, q, g)
-    words0 = oracle.pack(c0, q)
-    cg = host(cg).view(np.uint32)
+    words0 = oracle.tile_codes(oracle.pack(c0, q), q)
+    cg = host(cg).view(np.uint32).reshape(-1)
     assert cg.shape == words0.shape
-    bad = np.argwhere(cg != words0)
+    bad = np.flatnonzero(cg != words0)
     assert bad.size == 0, f"{len(bad)} code words differ, first at {bad[:3].tolist()}"
-    assert host(sg).view(np.uint16).tobytes() == s0.view(np.uint16).tobytes(), "scales differ"
-    assert host(zg).view(np.uint16).tobytes() == z0.view(np.uint16).tobytes(), "zeros differ"
+    assert host(sg).view(np.uint16).tobytes() == oracle.tile_groups(s0).view(np.uint16).tobytes(), "scales differ"
+    assert host(zg).view(np.uint16).tobytes() == oracle.tile_groups(z0).view(np.uint16).tobytes(), "zeros differ"
 
 
 @pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (2, 3, 32), (3, 4, 32), (3, 4, 64), (3, 4, 128),
@@ -163,11 +163,14 @@ def test_quantize_pack_edge_cases(q, g):
 
 
 def test_quantize_ragged_rows():
-    # d_out not a multiple of the lanes' row stride
+    # row counts that leave workgroups with a single tile or a partial set
     X, W = cfg_inputs(3)
     D = oracle.colstats(X[:256], alpha=0.75)
-    _check_quant(W[:52], D, 4, 32, "rows52")
-    _check_quant(W[:4], D, 3, 128, "rows4")
+    _check_quant(W[:96], D, 4, 32, "rows96")
+    _check_quant(W[:32], D, 3, 128, "rows32")
+    # channel counts that leave a partial 256-channel workgroup (64, 128, 192)
+    for d in (320, 384, 448):
+        _check_quant(np.ascontiguousarray(W[:64, :d]), D[:d], 4, 64 if d % 128 else 128, f"d{d}")
 
 
 # ---------------------------------------------------------------------------
@@ -221,7 +224,8 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None):
     say(f"gemm cfg={cfg} T={T} q={q} g={g} r={r}")
     Xd = dev(X)
     Zd = ttq.ttq_lowrank_z(Xd, dev(A)) if r else None
-    Yd = ttq.ttq_wlowbit_gemm(Xd, dev(oracle_dinvsqrt(D)), dev(oracle.pack(c, q)), dev(s), dev(z), q, g,
+    Yd = ttq.ttq_wlowbit_gemm(Xd, dev(oracle_dinvsqrt(D)), dev(oracle.tile_codes(oracle.pack(c, q), q)),
+                              dev(oracle.tile_groups(s)), dev(oracle.tile_groups(z)), q, g,
                               W.shape[0], B=dev(B) if r else None, Z=Zd)
     Yg = host(Yd)
     assert Yg.dtype == X.dtype and Yg.shape == (T, W.shape[0])
@@ -272,7 +276,8 @@ def _e2e(cfg, q, g, r, T=None, prompt=0, sample_rows=None, alpha=None, decode_T=
     assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
     Wq = oracle.residual(W, B, A) if r else W
     c0, s0, z0 = oracle.quantize(Wq, D0, q, g)
-    cg = oracle.unpack(host(layer.codes).view(np.uint32), q, W.shape[1])
+    cg = oracle.unpack(oracle.untile_codes(host(layer.codes).view(np.uint32), q, W.shape[0], W.shape[1]),
+                       q, W.shape[1])
     agree = np.mean(cg == c0)
     say(f"  code agreement with the oracle's own D: {agree:.6f}")
     assert agree >= 0.999
@@ -322,8 +327,8 @@ def test_alpha_zero_gives_rtn_on_gpu():
     layer.prepare(dev(X))
     assert np.all(host(layer.D) == 1.0)
     c0, s0, z0 = oracle.quantize(W, np.ones(W.shape[1], np.float32), 3, 32)
-    assert host(layer.codes).view(np.uint32).tobytes() == oracle.pack(c0, 3).tobytes()
-    assert host(layer.scales).view(np.uint16).tobytes() == s0.view(np.uint16).tobytes()
+    assert host(layer.codes).view(np.uint32).tobytes() == oracle.tile_codes(oracle.pack(c0, 3), 3).tobytes()
+    assert host(layer.scales).view(np.uint16).tobytes() == oracle.tile_groups(s0).view(np.uint16).tobytes()
     layer.close()
 
 

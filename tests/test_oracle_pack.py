@@ -1,4 +1,5 @@
-"""Pins for the packing format: hand-worked words and the round trip."""
+"""Pins for the packing format and its tiled storage order: hand-worked
+words and indices, round trips, bijection."""
 import json
 import os
 
@@ -43,3 +44,37 @@ def test_roundtrip(q, rows, blocks, seed):
 def test_rejects_oversized_codes():
     with pytest.raises(ValueError):
         oracle.pack(np.full((1, 32), 16, np.uint8), 4)
+
+
+def test_tiled_index_worked(golden_dir):
+    with open(os.path.join(golden_dir, "tiled_layout.json")) as f:
+        g = json.load(f)
+    for c in g["codes"]:
+        assert int(oracle.tiled_code_index(c["n"], c["b"], c["w"], c["q"], c["d"])) == c["index"], c
+    for c in g["groups"]:
+        v = np.zeros((c["d_out"], c["ng"]), np.float32)
+        v[c["n"], c["gi"]] = 1.0
+        assert int(np.argmax(oracle.tile_groups(v))) == c["index"]
+
+
+@pytest.mark.parametrize("q", [2, 3, 4])
+def test_tiled_layout_is_a_bijection(q):
+    d_out, d = 96, 320
+    n, b, w = np.meshgrid(np.arange(d_out), np.arange(d // 32), np.arange(q), indexing="ij")
+    idx = oracle.tiled_code_index(n, b, w, q, d).ravel()
+    assert np.array_equal(np.sort(idx), np.arange(d_out * d // 32 * q))
+    words = np.random.default_rng(q).integers(0, 2 ** 32, size=(d_out, d // 32, q), dtype=np.uint64).astype(np.uint32)
+    np.testing.assert_array_equal(oracle.untile_codes(oracle.tile_codes(words, q), q, d_out, d), words)
+    vals = np.random.default_rng(q).standard_normal((d_out, d // 32)).astype(np.float16)
+    np.testing.assert_array_equal(oracle.untile_groups(oracle.tile_groups(vals), d_out, d // 32), vals)
+
+
+def test_tiled_step_chunks_are_contiguous():
+    # one 64-channel step of one 32-row tile occupies one contiguous run of 32*2q words
+    q, d_out, d = 4, 64, 256
+    n, b, w = np.meshgrid(np.arange(32, 64), np.array([4, 5]), np.arange(q), indexing="ij")
+    idx = np.sort(oracle.tiled_code_index(n, b, w, q, d).ravel())
+    assert np.array_equal(idx, np.arange(idx[0], idx[0] + 32 * 2 * q))
+    # and a row's step words put the words of MFMA lane half 0 (w = 0, 2) first
+    row = oracle.tiled_code_index(5, np.array([0, 0, 1, 1, 0, 0, 1, 1]), np.array([0, 2, 0, 2, 1, 3, 1, 3]), 4, d)
+    assert np.array_equal(row - row[0], np.arange(8))
