@@ -10,16 +10,15 @@
 //   * A workgroup of 4 waves computes a 256 (output channels) x 128 (tokens)
 //     tile of Y^T; wave w owns channels [64w, 64w + 64) x all 128 tokens as
 //     2 x 4 fragments of 32x32 with fp32 accumulators.  Two workgroups fit on
-//     a CU (<= 256 registers per lane, ~53 KB LDS each), so one workgroup's
+//     a CU (<= 256 registers per lane, <= 54 KB LDS each), so one workgroup's
 //     loads and barrier overlap the other's MFMAs.
 //   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
 //     input (columns = tokens): accumulator lanes hold 4 consecutive output
 //     channels of one token, stored as 8 or 16 bytes.
 //   * K loop in steps of 64 input channels, two LDS stages:
-//       codes, scales, zeros  come straight from HBM into LDS
-//                 (global_load_lds_dwordx4): in the tiled storage order one
-//                 step of one 32-row tile is a contiguous chunk, so every
-//                 wave instruction moves contiguous bytes;
+//       codes, scales, zeros  in the tiled storage order one step of one
+//                 32-row tile is a contiguous chunk, so every wave load
+//                 instruction moves 1 KB of contiguous bytes;
 //       X         8 lanes per 128-byte row segment -> registers -> multiplied
 //                 by D^(-1/2) in fp32 and rounded to fp16 (one v_fma_mix per
 //                 element) -> LDS, in a permuted channel order with an XOR
@@ -122,12 +121,6 @@ __device__ __forceinline__ void store4(TX* p, const float* v) {
   }
 }
 
-// 16 bytes per lane from global memory into LDS; lane l lands at
-// lds_wave_base + 16 * l (the base is the same for the whole wave)
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
 template <int Q, int G, typename TX, bool LOWRANK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ X, int64_t ldx,
@@ -218,37 +211,48 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
     xrow[u] = X + t * ldx + 8 * xc;
   }
   uint4 xr[4][XV];
-  float4 dvr = make_float4(0.f, 0.f, 0.f, 0.f);  // D^(-1/2) of the step after next (threads < 16)
+  float4 dvr;  // D^(-1/2) of the step after next (threads < 16 keep it)
 
-  // direct-to-LDS pieces of one step: codes, then scales and zeros
-  auto dma_step = [&](int kt, int buf) {
-    // codes: a tile's step chunk is 32 * 2Q words = 16Q slots of 16 bytes;
-    // slot p -> row tile p / 16Q, words 4 (p % 16Q) of that chunk
-#pragma unroll
-    for (int j = 0; j < (CW / 4 + kThreads - 1) / kThreads; ++j) {
-      const int base = (wave + 4 * j) * 64;  // first slot of this wave instruction
-      if (base < CW / 4) {
-        const int p = base + lane;
-        const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
-        const uint32_t* g = codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q));
-        if (p < CW / 4) lds_dma16(g, &cs[buf][4 * base]);
-      }
+  // codes, scales and zeros of one step: 16-byte slots, slot p handled by
+  // thread p % 256; registers now, LDS after the MFMAs of the current step.
+  // (Copying them straight to LDS would make the compiler wait for every
+  // outstanding load before the step's first LDS read.)
+  constexpr int CSL = CW / 4;                        // code slots per step
+  constexpr int CPT = (CSL + kThreads - 1) / kThreads;
+  constexpr int SLOTS = SZ / 8;                      // slots per scales / zeros array
+  static_assert(CPT <= 2, "code slots per thread");
+  uint4 cr0, cr1;  // code slots tid and tid + 256 (scalars: an indexed array
+                   // would be moved out of registers)
+  uint4 sr;
+  // Every thread issues every load (indices clamped into range) and only the
+  // LDS stores are predicated: no divergent branch sits between a load and
+  // its use, so the compiler's wait counts stay exact.
+  auto load_w = [&](int kt) {
+    // a tile's step chunk is 32 * 2Q words = 16Q slots: slot p -> row tile
+    // p / 16Q, words 4 (p % 16Q) of that chunk
+    {
+      const int p = min(tid, CSL - 1);
+      const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
+      cr0 = *reinterpret_cast<const uint4*>(codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q)));
     }
-    // scales and zeros: SZ halfs each, in slots of 8 halfs; slot p < SLOTS -> scales
-    constexpr int SLOTS = SZ / 8;
+    if constexpr (CPT > 1) {
+      const int p = min(tid + kThreads, CSL - 1);
+      const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
+      cr1 = *reinterpret_cast<const uint4*>(codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q)));
+    }
+    const int p = min(tid, 2 * SLOTS - 1);  // slots < SLOTS: scales, then zeros
+    const int arr = p / SLOTS, q8 = p % SLOTS;
+    const int t = min(ntile0 + q8 / (4 * GPK), ntiles - 1);
+    const int within = 8 * (q8 % (4 * GPK));  // halfs inside the tile's GPK x 32 chunk
     const int gk = (kt * BK) / G;
-#pragma unroll
-    for (int j = 0; j < (2 * SLOTS + kThreads - 1) / kThreads; ++j) {
-      const int base = (wave + 4 * j) * 64;
-      if (base < 2 * SLOTS) {
-        const int p = base + lane;
-        const int arr = p / SLOTS, q8 = p % SLOTS;
-        const int t = min(ntile0 + q8 / (4 * GPK), ntiles - 1);
-        const int within = 8 * (q8 % (4 * GPK));  // halfs inside the tile's GPK x 32 chunk
-        const _Float16* src = (arr == 0 ? scales : zeros) + ((int64_t)t * ng + gk) * 32 + within;
-        if (p < 2 * SLOTS) lds_dma16(src, &szs[buf][8 * base]);
-      }
+    sr = *reinterpret_cast<const uint4*>((arr == 0 ? scales : zeros) + ((int64_t)t * ng + gk) * 32 + within);
+  };
+  auto store_w = [&](int buf) {
+    if (tid < CSL) *reinterpret_cast<uint4*>(&cs[buf][4 * tid]) = cr0;
+    if constexpr (CPT > 1) {
+      if (tid + kThreads < CSL) *reinterpret_cast<uint4*>(&cs[buf][4 * (tid + kThreads)]) = cr1;
     }
+    if (tid < 2 * SLOTS) *reinterpret_cast<uint4*>(&szs[buf][8 * tid]) = sr;
   };
 
   auto load_x = [&](int kt) {
@@ -288,13 +292,15 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
   };
 
   // ---- prologue: D^(-1/2) of steps 0 and 1, stage 0 ----
-  if (tid < 16) {
-    *reinterpret_cast<float4*>(&dvs[0][4 * tid]) = reinterpret_cast<const float4*>(dinvsqrt)[tid];
-    if (ksteps > 1) dvr = reinterpret_cast<const float4*>(dinvsqrt + BK)[tid];
+  {
+    const float4 d0 = reinterpret_cast<const float4*>(dinvsqrt)[tid & 15];
+    dvr = reinterpret_cast<const float4*>(dinvsqrt + min(1, ksteps - 1) * BK)[tid & 15];
+    if (tid < 16) *reinterpret_cast<float4*>(&dvs[0][4 * tid]) = d0;
   }
-  dma_step(0, 0);
+  load_w(0);
   load_x(0);
   __syncthreads();
+  store_w(0);
   store_x(0);
   if (tid < 16 && ksteps > 1) *reinterpret_cast<float4*>(&dvs[1][4 * tid]) = dvr;
   __syncthreads();
@@ -302,11 +308,14 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
   for (int kt = 0; kt < ksteps; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < ksteps) {
-      dma_step(kt + 1, buf ^ 1);
+      load_w(kt + 1);
       load_x(kt + 1);
-      if (tid < 16 && kt + 2 < ksteps)
-        dvr = reinterpret_cast<const float4*>(dinvsqrt + (kt + 2) * BK)[tid];
+      dvr = reinterpret_cast<const float4*>(dinvsqrt + min(kt + 2, ksteps - 1) * BK)[tid & 15];
     }
+    // keep the next step's LDS stores after this step's MFMAs: hoisted next to
+    // their loads they would make every step wait out the load latency
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // this wave's code words and group parameters for the step
     uint32_t rw[FN][(Q == 3) ? 6 : 4];
@@ -366,7 +375,10 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
       }
     }
 
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < ksteps) {
+      store_w(buf ^ 1);
       store_x(buf ^ 1);
       if (tid < 16 && kt + 2 < ksteps) *reinterpret_cast<float4*>(&dvs[buf][4 * tid]) = dvr;
     }
