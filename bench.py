@@ -176,16 +176,16 @@ def main():
         c0, s0, z0 = oracle.quantize(W_np, D0, q, g)
         oracle.pack(c0, q)
         t_prep = time.perf_counter() - t0
-        n_tok = 512
+        n_tok = T
         t0 = time.perf_counter()
         oracle.linear(X_np[:n_tok], c0, s0, z0, D0, g)
         t_lin = time.perf_counter() - t0
         t_cpu = t_prep + t_lin * T / n_tok
         cpu = {"value": T / t_cpu / 1e3, "unit": "k tokens/s", "cores": int(max(1, blas_threads)),
                "kind": "oracle",
-               "sample": (f"prepare (colstats + quantize + pack) on the full {T}-token prompt "
-                          f"({t_prep:.2f} s), projection on its first {n_tok} tokens ({t_lin:.2f} s) "
-                          f"scaled linearly to {T}; {cores} cores visible, numpy fp64/fp32")}
+               "sample": (f"one full step of the workload: prepare (colstats + quantize + pack) on the "
+                          f"{T}-token prompt ({t_prep:.2f} s) and the fp64 projection of all {n_tok} tokens "
+                          f"({t_lin:.2f} s); numpy, {cores} cores visible")}
 
     out = {
         "metric": "q_proj prefill k tokens/s (prepare+GEMM) at 4-bit r=0/16; % HBM/MFMA peak",
