@@ -13,7 +13,7 @@
  *   codes, scales, zeros = group RTN of W_res D^(1/2)
  *     (paper-daily.com section 2: RTN QDQ and the closed form Q[W D^(1/2)] D^(-1/2))
  *   Y = Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
- *     (paper-daily.com section 5: pre-scaling fused into the low-bit kernel)
+ *     (paper-daily.com section 5: a low-bit kernel on the pre-scaled input)
  * Quantisation parameters are computed at prefill and reused by decode
  * (paper-daily.com section 6).
  *
@@ -106,13 +106,13 @@ typedef struct ttq_sizes {
   size_t d_bytes;         /* fp32   [d_in]   D                           */
   size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2)                    */
   size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */
-  size_t z_bytes;         /* fp32   [T_max][r]    A X     (0 when r = 0) */
-  size_t workspace_bytes; /* fp32 column-statistic partial sums          */
+  size_t workspace_bytes; /* prepare: column-statistic partial sums      */
+  size_t linear_workspace_bytes; /* ttq_linear on T_max tokens            */
 } ttq_sizes;
 
 /* Device buffers a handle works in (all caller-owned, see ttq_sizes).
  * B (fp32 [d_out][r]) and A (fp32 [r][d_in]) are the static factors; they
- * and wres / z are ignored when r = 0. */
+ * and wres are ignored when r = 0.  The workspace serves ttq_prepare only. */
 typedef struct ttq_buffers {
   uint32_t* codes;
   void* scales;
@@ -122,7 +122,6 @@ typedef struct ttq_buffers {
   void* wres;
   const float* B;
   const float* A;
-  float* z;
   float* workspace;
   int64_t T_max;
   size_t workspace_bytes;
@@ -167,11 +166,17 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
 /* The low-bit projection with the handle's current quantisation:
  *   Y = Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
  * X: device [T][ldx] of dtype xdt; Y: device [T][ldy] of the same dtype,
- * fp32 accumulation.  0 <= T <= T_max (r > 0) or any T >= 0 (r = 0);
- * T = 0 enqueues nothing.  Used for the prefill tokens and, unchanged, for
- * decode batches that reuse the prefill quantisation. */
+ * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
+ * prefill tokens and, unchanged, for decode batches that reuse the prefill
+ * quantisation.  Runs ttq_prescale (fused with ttq_lowrank_z when r > 0:
+ * one read of X) into `workspace`, then ttq_wlowbit_gemm.  workspace: device
+ * memory of at least ttq_linear_workspace_bytes(T, d_in, r) bytes, owned by
+ * the caller; the handle itself is only read, so calls on one handle may run
+ * concurrently on different streams when each has its own workspace. */
+size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t r);
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
-                      int64_t ldx, void* Y, int64_t ldy, void* stream);
+                      int64_t ldx, void* Y, int64_t ldy, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* ---- Sub-steps, exported so each kernel can be checked on its own ---- */
 
@@ -200,20 +205,28 @@ ttq_status ttq_residual(int32_t d_out, int32_t d_in, int32_t r, const void* W,
                         const float* B, const float* A, void* W_res, void* stream);
 
 /* Z = X A^T: X device [T][ldx] (dtype xdt), A device fp32 [r][d_in],
- * Z device fp32 [T][r], fp32 accumulation.  r must be 16. */
+ * Z device fp32 [T][r], fp32 accumulation (A enters the matrix cores as two
+ * fp16 parts, about 22 bits).  r must be 16. */
 ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_dtype xdt,
                          int64_t ldx, const float* A, float* Z, void* stream);
 
-/* Y = V_hat (dinvsqrt * X) + B Z with V_hat[n][k] = (code - z) * s, fp16
- * operands on the matrix cores and fp32 accumulation.  dinvsqrt device fp32
- * [d_in]; codes/scales/zeros as produced by ttq_quantize_pack; B device fp32
- * [d_out][r] and Z device fp32 [T][r] (both ignored when r = 0).  Y has X's
- * dtype. */
+/* Xs = fp16(dinvsqrt * X): X device [T][ldx] (dtype xdt), dinvsqrt device
+ * fp32 [d_in], Xs device fp16 [T][d_in] (dense rows).  Each product is taken
+ * in fp32 and rounded to fp16.  Within every 8 consecutive channels Xs holds
+ * them in the order 0 4 1 5 2 6 3 7 (the order in which ttq_wlowbit_gemm's
+ * dequantisation pairs weights); d_in must be a multiple of 64. */
+ttq_status ttq_prescale(const void* X, ttq_dtype xdt, int64_t T, int32_t d_in, int64_t ldx,
+                        const float* dinvsqrt, void* Xs, void* stream);
+
+/* Y = V_hat Xs + B Z with V_hat[n][k] = (code - z) * s, fp16 operands on the
+ * matrix cores and fp32 accumulation.  Xs: device fp16 [T][ldxs] as written
+ * by ttq_prescale (ldxs >= d_in, a multiple of 8); codes/scales/zeros as
+ * produced by ttq_quantize_pack; B device fp32 [d_out][r] and Z device fp32
+ * [T][r] (both ignored when r = 0).  Y: device [T][ldy] of dtype ydt. */
 ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g,
-                            int32_t r, const void* X, ttq_dtype xdt, int64_t ldx,
-                            const float* dinvsqrt, const uint32_t* codes,
+                            int32_t r, const void* Xs, int64_t ldxs, const uint32_t* codes,
                             const void* scales, const void* zeros, const float* B,
-                            const float* Z, void* Y, int64_t ldy, void* stream);
+                            const float* Z, void* Y, ttq_dtype ydt, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

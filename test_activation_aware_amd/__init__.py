@@ -7,7 +7,7 @@ fallback: without the built library, or without a GPU, calls raise.
 
 Functions with the C names take torch tensors:
     ttq_colstats, ttq_quantize_pack, ttq_residual, ttq_lowrank_z,
-    ttq_wlowbit_gemm, ttq_query_sizes
+    ttq_prescale, ttq_wlowbit_gemm, ttq_query_sizes
 and TTQLinear wraps the handle API (ttq_create / ttq_set_weight /
 ttq_prepare / ttq_linear / ttq_destroy) for one q_proj layer:
 
@@ -33,8 +33,9 @@ from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 
 __all__ = [
     "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
-    "ttq_residual", "ttq_lowrank_z", "ttq_wlowbit_gemm", "ttq_query_sizes",
-    "ttq_colstats_workspace_bytes", "ttq_abi_version", "code_shape", "group_shape",
+    "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_query_sizes",
+    "ttq_colstats_workspace_bytes", "ttq_linear_workspace_bytes", "ttq_abi_version", "code_shape",
+    "group_shape",
 ]
 
 
@@ -85,6 +86,10 @@ def ttq_abi_version() -> int:
 
 def ttq_colstats_workspace_bytes(T: int, d: int) -> int:
     return load().ttq_colstats_workspace_bytes(T, d)
+
+
+def ttq_linear_workspace_bytes(T: int, d: int, r: int) -> int:
+    return load().ttq_linear_workspace_bytes(T, d, r)
 
 
 def ttq_query_sizes(d_in, d_out, q, g, r, alpha, lam, p, T_max) -> dict:
@@ -162,24 +167,40 @@ def ttq_lowrank_z(X, A, out=None):
     return out
 
 
-def ttq_wlowbit_gemm(X, dinvsqrt, codes, scales, zeros, q: int, g: int, d_out: int, B=None, Z=None,
-                     out=None):
-    """Y = V_hat (D^(-1/2) X) + B Z with the packed codes; Y has X's dtype."""
+def ttq_prescale(X, dinvsqrt, out=None):
+    """Xs = fp16(D^(-1/2) X), [T][d] with the channels of every group of 8
+    stored in the order 0 4 1 5 2 6 3 7 (the low-bit GEMM's input)."""
     torch = _torch()
     x, dt, T, ldx = _x_args(X)
-    d_in = X.shape[1]
+    d = X.shape[1]
+    out = torch.empty((T, d), dtype=torch.float16, device=X.device) if out is None else out
+    check(load().ttq_prescale(x, dt, T, d, ldx, _dev(dinvsqrt, "dinvsqrt", torch.float32),
+                              _dev(out, "Xs", torch.float16), _stream()), "ttq_prescale")
+    return out
+
+
+def ttq_wlowbit_gemm(Xs, codes, scales, zeros, q: int, g: int, d_out: int, B=None, Z=None,
+                     out=None, out_dtype=None):
+    """Y = V_hat Xs + B Z with the packed codes, from the pre-scaled input of
+    ttq_prescale; Y is fp16 unless out / out_dtype say otherwise."""
+    torch = _torch()
+    xs, dt, T, ldxs = _x_args(Xs, "Xs")
+    if dt != TTQ_F16:
+        raise TypeError("Xs must be float16 (the output of ttq_prescale)")
+    d_in = Xs.shape[1]
     r = 0 if B is None else B.shape[1]
-    out = torch.empty((T, d_out), dtype=X.dtype, device=X.device) if out is None else out
+    if out is None:
+        out = torch.empty((T, d_out), dtype=out_dtype or torch.float16, device=Xs.device)
     if out.dim() != 2 or out.stride(1) != 1:
         raise ValueError("out must be 2-D with unit column stride")
+    ydt = {torch.float16: TTQ_F16, torch.float32: TTQ_F32}[out.dtype]
     ldy = out.stride(0) if T > 1 else d_out
     bp = _dev(B, "B", torch.float32) if r else None
     zp = _dev(Z, "Z", torch.float32) if r else None
-    check(load().ttq_wlowbit_gemm(T, d_in, d_out, q, g, r, x, dt, ldx,
-                                  _dev(dinvsqrt, "dinvsqrt", torch.float32),
+    check(load().ttq_wlowbit_gemm(T, d_in, d_out, q, g, r, xs, ldxs,
                                   _dev(codes, "codes", torch.int32), _dev(scales, "scales", torch.float16),
                                   _dev(zeros, "zeros", torch.float16), bp, zp,
-                                  ctypes.c_void_p(out.data_ptr()), ldy, _stream()), "ttq_wlowbit_gemm")
+                                  ctypes.c_void_p(out.data_ptr()), ydt, ldy, _stream()), "ttq_wlowbit_gemm")
     return out
 
 
@@ -243,13 +264,15 @@ class TTQLinear:
             self.B = torch.as_tensor(np.ascontiguousarray(B), dtype=torch.float32).to(dev)
             self.A = torch.as_tensor(np.ascontiguousarray(A), dtype=torch.float32).to(dev)
             self.wres = torch.empty_like(W)
-            self.z = torch.empty((T_max, r), dtype=torch.float32, device=dev)
         else:
-            self.B = self.A = self.wres = self.z = None
+            self.B = self.A = self.wres = None
+        # the projection's workspace (pre-scaled input, and Z when r > 0), reused
+        # by every call on the current stream and grown on demand
+        self.linear_workspace = torch.empty(max(1, sz.linear_workspace_bytes), dtype=torch.uint8, device=dev)
         ptr = lambda t: None if t is None else t.data_ptr()
         self._bufs = _capi.ttq_buffers(ptr(self.codes), ptr(self.scales), ptr(self.zeros), ptr(self.D),
                                        ptr(self.dinvsqrt), ptr(self.wres), ptr(self.B), ptr(self.A),
-                                       ptr(self.z), ptr(self.workspace), T_max, self.workspace.numel() * 4)
+                                       ptr(self.workspace), T_max, self.workspace.numel() * 4)
         h = ctypes.c_void_p()
         check(lib.ttq_create(ctypes.byref(self._cfg), ctypes.byref(self._bufs), ctypes.byref(h)), "ttq_create")
         self._h = h
@@ -272,8 +295,12 @@ class TTQLinear:
         if out.dtype != X.dtype or out.dim() != 2 or out.stride(1) != 1 or out.shape != (T, self.d_out):
             raise ValueError("out must be [T][d_out] with X's dtype and unit column stride")
         ldy = out.stride(0) if T > 1 else self.d_out
-        check(load().ttq_linear(self._h, x, dt, T, ldx, ctypes.c_void_p(out.data_ptr()), ldy, _stream()),
-              "ttq_linear")
+        need = ttq_linear_workspace_bytes(T, self.d_in, self.r)
+        if self.linear_workspace.numel() < need:
+            self.linear_workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        ws = self.linear_workspace
+        check(load().ttq_linear(self._h, x, dt, T, ldx, ctypes.c_void_p(out.data_ptr()), ldy,
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()), "ttq_linear")
         return out
 
     def close(self) -> None:

@@ -31,14 +31,13 @@ class ttq_config(ctypes.Structure):
 class ttq_sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "codes_bytes", "scales_bytes", "zeros_bytes", "d_bytes", "dinvsqrt_bytes",
-        "wres_bytes", "z_bytes", "workspace_bytes")]
+        "wres_bytes", "workspace_bytes", "linear_workspace_bytes")]
 
 
 class ttq_buffers(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
                 ("D", ctypes.c_void_p), ("dinvsqrt", ctypes.c_void_p), ("wres", ctypes.c_void_p),
-                ("B", ctypes.c_void_p), ("A", ctypes.c_void_p), ("z", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("T_max", ctypes.c_int64),
+                ("B", ctypes.c_void_p), ("A", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("T_max", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -59,14 +58,16 @@ SIGNATURES = {
     "ttq_destroy": (None, [_P]),
     "ttq_set_weight": (ctypes.c_int, [_P, _P, _P]),
     "ttq_prepare": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P]),
-    "ttq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P]),
+    "ttq_linear_workspace_bytes": (_S, [_I64, _I32, _I32]),
+    "ttq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, _S, _P]),
     "ttq_colstats_workspace_bytes": (_S, [_I64, _I64]),
     "ttq_colstats": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P, _S, _P]),
     "ttq_quantize_pack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "ttq_residual": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "ttq_lowrank_z": (ctypes.c_int, [_I64, _I32, _I32, _P, ctypes.c_int, _I64, _P, _P, _P]),
-    "ttq_wlowbit_gemm": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, ctypes.c_int, _I64,
-                                        _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "ttq_prescale": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
+    "ttq_wlowbit_gemm": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
+                                        _P, _P, _P, ctypes.c_int, _I64, _P]),
 }
 
 _lib = None

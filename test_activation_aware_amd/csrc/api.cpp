@@ -105,6 +105,20 @@ size_t colstats_ws_bytes(int64_t T, int64_t d) {
   return (size_t)ttq::colstats_chunks(T < 1 ? 1 : T) * (size_t)d * sizeof(float);
 }
 
+// ttq_linear's workspace: Xs (fp16 [T][d_in]) then, for r > 0, Z (fp32 [T][r])
+size_t xs_bytes(int64_t T, int64_t d) { return ((size_t)T * (size_t)d * 2 + 255) & ~(size_t)255; }
+size_t linear_ws_bytes(int64_t T, int64_t d, int32_t r) {
+  return xs_bytes(T, d) + (r > 0 ? (size_t)T * (size_t)r * 4 : 0);
+}
+
+ttq_status check_y(const void* Y, ttq_dtype ydt, int64_t T, int64_t d_out, int64_t ldy) {
+  if (ydt != TTQ_F16 && ydt != TTQ_F32) return fail(TTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)ydt);
+  if (ldy < d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%lld", (long long)ldy, (long long)d_out);
+  if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
+  if (T > 0) TTQ_NEED(Y);
+  return TTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,8 +157,8 @@ ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out)
   out->d_bytes = din * 4;
   out->dinvsqrt_bytes = din * 4;
   out->wres_bytes = cfg->r > 0 ? dout * din * 2 : 0;
-  out->z_bytes = cfg->r > 0 ? (size_t)T_max * (size_t)cfg->r * 4 : 0;
   out->workspace_bytes = colstats_ws_bytes(T_max, cfg->d_in);
+  out->linear_workspace_bytes = linear_ws_bytes(T_max, cfg->d_in, cfg->r);
   return ok();
 }
 
@@ -166,7 +180,6 @@ ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle
     TTQ_NEED(bufs->wres);
     TTQ_NEED(bufs->B);
     TTQ_NEED(bufs->A);
-    TTQ_NEED(bufs->z);
   }
   ttq_handle* h = new (std::nothrow) ttq_handle;
   if (h == nullptr) return fail(TTQ_ERR_INVALID_ARG, "host allocation of the handle failed");
@@ -255,35 +268,47 @@ ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_
   if (T == 0) return ok();
   TTQ_NEED(A);
   TTQ_NEED(Z);
-  hipError_t e = ttq::launch_lowrank_z(T, d_in, r, X, xdt == TTQ_F32, ldx, A, Z, static_cast<hipStream_t>(stream));
+  hipError_t e = ttq::launch_prescale_z(T, d_in, X, xdt == TTQ_F32, ldx, nullptr, nullptr, A, Z,
+                                        static_cast<hipStream_t>(stream));
   return hip_status(e, "lowrank_z launch");
 }
 
+ttq_status ttq_prescale(const void* X, ttq_dtype xdt, int64_t T, int32_t d_in, int64_t ldx,
+                        const float* dinvsqrt, void* Xs, void* stream) {
+  if (d_in <= 0 || d_in % 64 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%d must be a positive multiple of 64", d_in);
+  ttq_status s = check_x(X, xdt, T, d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (T == 0) return ok();
+  TTQ_NEED(dinvsqrt);
+  TTQ_NEED(Xs);
+  hipError_t e = ttq::launch_prescale_z(T, d_in, X, xdt == TTQ_F32, ldx, dinvsqrt, Xs, nullptr, nullptr,
+                                        static_cast<hipStream_t>(stream));
+  return hip_status(e, "prescale launch");
+}
+
 ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g, int32_t r,
-                            const void* X, ttq_dtype xdt, int64_t ldx, const float* dinvsqrt,
-                            const uint32_t* codes, const void* scales, const void* zeros,
-                            const float* B, const float* Z, void* Y, int64_t ldy, void* stream) {
+                            const void* Xs, int64_t ldxs, const uint32_t* codes, const void* scales,
+                            const void* zeros, const float* B, const float* Z, void* Y, ttq_dtype ydt,
+                            int64_t ldy, void* stream) {
   ttq_status s = check_qgr(q, g, r);
   if (s != TTQ_OK) return s;
   s = check_dims(d_in, d_out, g);
   if (s != TTQ_OK) return s;
-  s = check_x(X, xdt, T, d_in, ldx);
+  s = check_x(Xs, TTQ_F16, T, d_in, ldxs);
   if (s != TTQ_OK) return s;
-  if (ldy < d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%d", (long long)ldy, d_out);
-  if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
+  if (ldxs > (int64_t(1) << 22)) return fail(TTQ_ERR_SHAPE, "ldxs=%lld too large", (long long)ldxs);
+  s = check_y(Y, ydt, T, d_out, ldy);
+  if (s != TTQ_OK) return s;
   if (T == 0) return ok();
-  TTQ_NEED(dinvsqrt);
   TTQ_NEED(codes);
   TTQ_NEED(scales);
   TTQ_NEED(zeros);
-  TTQ_NEED(Y);
   if (r > 0) {
     TTQ_NEED(B);
     TTQ_NEED(Z);
   }
-  hipError_t e = ttq::launch_wlowbit_gemm(T, d_in, d_out, q, g, r, X, xdt == TTQ_F32, ldx, dinvsqrt,
-                                          codes, scales, zeros, B, Z, Y, ldy,
-                                          static_cast<hipStream_t>(stream));
+  hipError_t e = ttq::launch_wlowbit_gemm(T, d_in, d_out, q, g, r, Xs, ldxs, codes, scales, zeros, B, Z,
+                                          Y, ydt == TTQ_F32, ldy, static_cast<hipStream_t>(stream));
   return hip_status(e, "wlowbit_gemm launch");
 }
 
@@ -307,27 +332,32 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   return ok();
 }
 
+size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t r) {
+  if (T < 0 || d_in <= 0 || r < 0) return 0;
+  return linear_ws_bytes(T, d_in, r);
+}
+
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
-                      void* Y, int64_t ldy, void* stream) {
+                      void* Y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
   if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
   if (!h->prepared) return fail(TTQ_ERR_INVALID_ARG, "ttq_prepare has not been called on this handle");
   const ttq_config& c = h->cfg;
   ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
   if (s != TTQ_OK) return s;
-  if (ldy < c.d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%d", (long long)ldy, c.d_out);
-  if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
-  if (c.r > 0 && T > h->buf.T_max)
-    return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld (Z buffer)", (long long)T, (long long)h->buf.T_max);
+  s = check_y(Y, xdt, T, c.d_out, ldy);
+  if (s != TTQ_OK) return s;
   if (T == 0) return ok();
-  TTQ_NEED(Y);
+  TTQ_NEED(workspace);
+  if (workspace_bytes < linear_ws_bytes(T, c.d_in, c.r))
+    return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, linear_ws_bytes(T, c.d_in, c.r));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (c.r > 0) {
-    hipError_t e = ttq::launch_lowrank_z(T, c.d_in, c.r, X, xdt == TTQ_F32, ldx, h->buf.A, h->buf.z, st);
-    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
-  }
-  hipError_t e = ttq::launch_wlowbit_gemm(T, c.d_in, c.d_out, c.q, c.g, c.r, X, xdt == TTQ_F32, ldx,
-                                          h->buf.dinvsqrt, h->buf.codes, h->buf.scales, h->buf.zeros,
-                                          h->buf.B, h->buf.z, Y, ldy, st);
+  void* xs = workspace;
+  float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
+  hipError_t e = ttq::launch_prescale_z(T, c.d_in, X, xdt == TTQ_F32, ldx, h->buf.dinvsqrt, xs,
+                                        c.r > 0 ? h->buf.A : nullptr, z, st);
+  if (e != hipSuccess) return hip_status(e, "prescale launch");
+  e = ttq::launch_wlowbit_gemm(T, c.d_in, c.d_out, c.q, c.g, c.r, xs, c.d_in, h->buf.codes, h->buf.scales,
+                               h->buf.zeros, h->buf.B, z, Y, xdt == TTQ_F32, ldy, st);
   return hip_status(e, "wlowbit_gemm launch");
 }
 

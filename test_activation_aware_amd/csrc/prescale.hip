@@ -1,0 +1,146 @@
+// The two per-call passes over the raw input X of the TTQ projection
+//   Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X)
+// (paper-daily.com deep reading, section 2: the closed form Q[W D^(1/2)] D^(-1/2)
+// and the static low-rank term B A applied to the raw input):
+//
+//   Xs = fp16(D^(-1/2) X)   the pre-scaled input the low-bit GEMM streams;
+//   Z  = X A^T              fp32 [T][16], the rank-16 input of the epilogue.
+//
+// One kernel does either or both: X is read from HBM once.  Xs is stored in
+// the channel order 0 4 1 5 2 6 3 7 within every 8 consecutive channels (the
+// order in which the GEMM's dequantisation produces weight pairs), rows of
+// d fp16 values.
+//
+// Layout of the work: a workgroup owns 16 tokens; its 4 waves take 32-channel
+// chunks round-robin, so at any time the workgroup streams 128 contiguous
+// channels of 16 rows.  Lane l holds token l%16 and channels 8*(l/16)..+8 of
+// the chunk: exactly the A operand of a 16x16x32 fp16 MFMA, whose B operand
+// is the matching slice of A^T (fp32 A split into two fp16 parts so that Z
+// keeps about 22 bits; fp32 X uses the 16x16x4 fp32 MFMA instead).  The four
+// waves' partial Z are summed through LDS at the end.
+#include "ttq_internal.h"
+
+namespace ttq {
+
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRank = 16;
+constexpr int kTok = 16;    // tokens per workgroup
+constexpr int kChunk = 32;  // channels per wave step
+
+template <typename TX>
+__device__ __forceinline__ void load8(const TX* p, float v[8]) {
+  if constexpr (sizeof(TX) == 2) {
+    const h8 h = *reinterpret_cast<const h8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <typename TX, bool XS, bool ZZ>
+__global__ __launch_bounds__(256) void prescale_z_kernel(int64_t T, int d, const TX* __restrict__ X,
+                                                         int64_t ldx, const float* __restrict__ dinvsqrt,
+                                                         _Float16* __restrict__ Xs,
+                                                         const float* __restrict__ A,
+                                                         float* __restrict__ Z) {
+  __shared__ f4 zred[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kb = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int64_t t = t0 + row;
+  const int64_t tl = t < T ? t : T - 1;  // rows past T are read clamped and not stored
+  const TX* xr = X + tl * ldx + 8 * kb;
+  const float* ar = A + (int64_t)row * d + 8 * kb;  // A^T column j = row of A
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nchunks = d / kChunk;
+
+  for (int c = wave; c < nchunks; c += 4) {
+    const int k0 = c * kChunk;
+    float x[8];
+    load8<TX>(xr + k0, x);
+    if constexpr (XS) {
+      const float4 da = *reinterpret_cast<const float4*>(dinvsqrt + k0 + 8 * kb);
+      const float4 db = *reinterpret_cast<const float4*>(dinvsqrt + k0 + 8 * kb + 4);
+      const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+      h8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = (_Float16)(x[e] * dv[e]);
+        o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+      }
+      if (t < T) *reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb) = o;
+    }
+    if constexpr (ZZ) {
+      float a[8];
+      load8<float>(ar + k0, a);
+      if constexpr (sizeof(TX) == 2) {
+        h8 xh, ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[e] = (_Float16)x[e];  // exact: x came from fp16
+          ahi[e] = (_Float16)a[e];
+          alo[e] = (_Float16)(a[e] - (float)ahi[e]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ahi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, alo, acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], a[e], acc, 0, 0, 0);
+      }
+    }
+  }
+
+  if constexpr (ZZ) {
+    // lane l holds Z[t0 + 4*(l/16) + i][l % 16], i = 0..3, for this wave's chunks
+    zred[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      f4 s = zred[0][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f4 v = zred[w][lane];
+        s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tz = t0 + 4 * kb + i;
+        if (tz < T) Z[tz * kRank + row] = s[i];
+      }
+    }
+  }
+}
+
+template <typename TX>
+hipError_t launch_tx(int64_t T, int d, const void* X, int64_t ldx, const float* dinv, void* Xs,
+                     const float* A, float* Z, hipStream_t s) {
+  const dim3 grid((unsigned)((T + kTok - 1) / kTok));
+  const TX* x = static_cast<const TX*>(X);
+  _Float16* xs = static_cast<_Float16*>(Xs);
+  if (Xs && Z)
+    hipLaunchKernelGGL((prescale_z_kernel<TX, true, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+  else if (Xs)
+    hipLaunchKernelGGL((prescale_z_kernel<TX, true, false>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+  else
+    hipLaunchKernelGGL((prescale_z_kernel<TX, false, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prescale_z(int64_t T, int d, const void* X, bool x_f32, int64_t ldx,
+                             const float* dinvsqrt, void* Xs, const float* A, float* Z,
+                             hipStream_t s) {
+  if (T <= 0 || (!Xs && !Z)) return hipSuccess;
+  if (x_f32) return launch_tx<float>(T, d, X, ldx, dinvsqrt, Xs, A, Z, s);
+  return launch_tx<_Float16>(T, d, X, ldx, dinvsqrt, Xs, A, Z, s);
+}
+
+}  // namespace ttq

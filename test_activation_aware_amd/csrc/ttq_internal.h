@@ -21,13 +21,15 @@ hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W
 hipError_t launch_residual(int d_out, int d_in, int r, const void* W, const float* B,
                            const float* A, void* W_res, hipStream_t s);
 
-hipError_t launch_lowrank_z(int64_t T, int d_in, int r, const void* X, bool x_f32, int64_t ldx,
-                            const float* A, float* Z, hipStream_t s);
+// Xs = fp16(D^(-1/2) X) in the GEMM's channel order and/or Z = X A^T
+// (either output may be NULL), one read of X.
+hipError_t launch_prescale_z(int64_t T, int d, const void* X, bool x_f32, int64_t ldx,
+                             const float* dinvsqrt, void* Xs, const float* A, float* Z,
+                             hipStream_t s);
 
-hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r,
-                               const void* X, bool x_f32, int64_t ldx, const float* dinvsqrt,
-                               const uint32_t* codes, const void* scales, const void* zeros,
-                               const float* B, const float* Z, void* Y, int64_t ldy,
-                               hipStream_t s);
+hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
+                               int64_t ldxs, const uint32_t* codes, const void* scales,
+                               const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,
+                               int64_t ldy, hipStream_t s);
 
 }  // namespace ttq

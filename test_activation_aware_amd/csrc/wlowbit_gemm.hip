@@ -1,45 +1,53 @@
 // ttq_wlowbit_gemm: the TTQ low-bit projection
-//   Y[t][n] = sum_k V_hat[n][k] * (dinvsqrt[k] * X[t][k])  +  sum_j B[n][j] Z[t][j]
-// with V_hat[n][k] = (code[n][k] - z[n][k/g]) * s[n][k/g], i.e.
+//   Y[t][n] = sum_k V_hat[n][k] * Xs[t][k]  +  sum_j B[n][j] Z[t][j]
+// with V_hat[n][k] = (code[n][k] - z[n][k/g]) * s[n][k/g], Xs = D^(-1/2) X
+// (pre-scaled by the prescale pass) and Z = A X, i.e.
 //   Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X)
 // (TTQ paper: paper-daily.com deep reading, section 2, closed form
-// Q[W D^(1/2)] D^(-1/2) and low-rank compensation; section 5, a custom kernel
-// that fuses the pre-scaling of X).
+// Q[W D^(1/2)] D^(-1/2) and low-rank compensation; section 5, a low-bit kernel
+// that consumes the pre-scaled input).
 //
 // CDNA4 design (gfx950, wave64, MFMA v_mfma_f32_32x32x16_f16):
 //   * A workgroup of 4 waves computes a 256 (output channels) x 128 (tokens)
 //     tile of Y^T; wave w owns channels [64w, 64w + 64) x all 128 tokens as
-//     2 x 4 fragments of 32x32 with fp32 accumulators.  Two workgroups fit on
-//     a CU (<= 256 registers per lane, <= 54 KB LDS each), so one workgroup's
-//     loads and barrier overlap the other's MFMAs.
+//     2 x 4 fragments of 32x32.  The fp32 accumulators live in the
+//     accumulator registers (AGPRs), 128 per lane, leaving 128 VGPRs for
+//     operands and prefetches: two workgroups fit on a CU.
 //   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
 //     input (columns = tokens): accumulator lanes hold 4 consecutive output
 //     channels of one token, stored as 8 or 16 bytes.
-//   * K loop in steps of 64 input channels, two LDS stages:
-//       codes, scales, zeros  in the tiled storage order one step of one
-//                 32-row tile is a contiguous chunk, so every wave load
-//                 instruction moves 1 KB of contiguous bytes;
-//       X         8 lanes per 128-byte row segment -> registers -> multiplied
-//                 by D^(-1/2) in fp32 and rounded to fp16 (one v_fma_mix per
-//                 element) -> LDS, in a permuted channel order with an XOR
-//                 swizzle of 16-byte chunks (conflict-free both ways);
-//       D^(-1/2)  64 floats per step through a two-slot LDS ring.
-//     Loads for step k+1 are issued before the MFMAs of step k.
-//   * Rows past T or d_out are read clamped to valid rows; a token's output
-//     depends only on its own row, and padding outputs are never stored.
+//   * K loop in steps of 64 input channels through a three-stage ring:
+//       Xs tile   128 rows x 128 bytes, global -> LDS by direct-to-LDS loads,
+//                 an XOR swizzle of 16-byte chunks applied through the source
+//                 addresses (conflict-free MFMA operand reads);
+//       scales and zeros of the step, global -> LDS the same way;
+//       codes     global -> registers: one 32-row tile's step is a contiguous
+//                 chunk (tiled storage order), so a wave's load of a fragment's
+//                 codes moves 1 KB of contiguous bytes.
+//     Step k+2 is requested while step k runs; a single barrier per step.
+//     Operands of the first sub-step of step k+1 (codes, scales, X fragments)
+//     are fetched and dequantised under the last MFMAs of step k, so the
+//     matrix cores do not wait at step boundaries.
+//   * Inside a step, each 16-channel sub-step issues its 8 MFMAs interleaved
+//     with the LDS reads and the dequantisation of the next sub-step.
 //   * Dequantisation in registers: code c becomes the fp16 1024 + c by OR-ing
 //     the exponent bits 0x6400 (v_and_or_b32, two codes per register);
 //     (1024 + c) - (1024 + z) = c - z exactly, times s gives the fp16 weight
 //     with one rounding (packed fp16 add and multiply).  The OR trick pairs
-//     code j with code j+4 of each 8-code group, so the X tile is stored in
-//     the channel order 0 4 1 5 2 6 3 7 within every 8 channels: the MFMA
-//     only needs A and B to agree on the order of the reduction.
+//     code j with code j+4 of each 8-code group; the prescale pass stores Xs in
+//     the channel order 0 4 1 5 2 6 3 7 within every 8 channels to match (the
+//     MFMA only needs A and B to agree on the order of the reduction).
 //   * Rank-r term: before the K loop each fragment gets two extra MFMAs,
 //     B16 x Z_hi and B16 x Z_lo with Z = Z_hi + Z_lo split into two fp16
 //     parts, so the fp32 Z keeps about 22 bits.
+//   * Rows past T or d_out are read clamped to valid rows; a token's output
+//     depends only on its own row, and padding outputs are never stored.
 //   * Workgroup ids go round-robin over the 8 XCDs; ids are regrouped so each
 //     XCD gets a contiguous band of tiles, walked in groups of 4 token tiles
 //     x all channel tiles, keeping the XCD's L2 on few X rows and W rows.
+#include <type_traits>
+#include <utility>
+
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -49,6 +57,8 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int BN = 256;  // output channels per workgroup
@@ -57,6 +67,20 @@ constexpr int BK = 64;   // input channels per step
 constexpr int FN = 2;    // 32-row fragments per wave
 constexpr int FM = 4;    // 32-token fragments per wave
 constexpr int kXcds = 8;
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// f(ic<0>{}), ..., f(ic<N-1>{}): every index is a compile-time constant, so
+// the register arrays indexed with it never need memory.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -68,39 +92,34 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-// fp16 pair (low half of xa times da, low half of xb times db) or the high
-// halves (HI = 1): one v_fma_mix per element, fp32 product rounded to fp16
-template <int HI>
-__device__ __forceinline__ uint32_t mix_pair(uint32_t xa, uint32_t xb, float da, float db) {
-  uint32_t r;
-  if constexpr (HI == 0) {
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(xa), "v"(da));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(xb), "v"(db));
-  } else {
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(xa), "v"(da));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(xb), "v"(db));
-  }
-  return r;
+// The code words one lane holds for one fragment and one step: q = 4, this
+// lane half's 4 words (one per sub-step); q = 2, the row's 4 words; q = 3, the
+// row's 6 words (words 4 and 5 in b).
+struct CodeFrag {
+  u4v a;
+  u2v b;
+};
+
+__device__ __forceinline__ uint32_t code_word(const CodeFrag& c, int i) {
+  return i < 4 ? c.a[i] : c.b[i - 4];
 }
 
-// The 4 code pairs (fp16 1024 + c in each half) a lane feeds to one MFMA.
-// `rw` holds the row's step words as read from LDS (q = 4: this lane half's
-// 4 words, one per sub-step; q = 2: the 4 words of the step; q = 3: the 6
-// words of the step); s = 16-channel sub-step, hh = lane half.
-template <int Q>
-__device__ __forceinline__ void code_pairs(const uint32_t* rw, int s, int hh, uint32_t mask,
-                                           uint32_t magic, uint32_t out[4]) {
+// The 4 code pairs (fp16 1024 + c in each half) a lane feeds to one MFMA of
+// sub-step S (16 channels), lane half hh.
+template <int Q, int S>
+__device__ __forceinline__ void code_pairs(const CodeFrag& c, int hh, uint32_t mask, uint32_t magic,
+                                           uint32_t out[4]) {
   uint32_t u;
   if constexpr (Q == 4) {
-    u = rw[s];
+    u = c.a[S];
   } else if constexpr (Q == 2) {
     // the 8 two-bit codes of this lane half; spread its two bytes 16 bits apart
-    u = __builtin_amdgcn_perm(0u, rw[s] >> (16 * hh), 0x0C010C00u);
+    u = __builtin_amdgcn_perm(0u, c.a[S] >> (16 * hh), 0x0C010C00u);
   } else {
-    const int bit = 3 * (16 * (s & 1) + 8 * hh);  // 0, 24, 48, 72 within the block
+    const int bit = 3 * (16 * (S & 1) + 8 * hh);  // 0, 24, 48, 72 within the block
     const int w = bit >> 5, off = bit & 31;
-    const uint32_t lo = rw[3 * (s >> 1) + w];
-    const uint32_t hi = (w < 2) ? rw[3 * (s >> 1) + w + 1] : 0u;
+    const uint32_t lo = code_word(c, 3 * (S >> 1) + w);
+    const uint32_t hi = (w < 2) ? code_word(c, 3 * (S >> 1) + w + 1) : 0u;
     const uint32_t win = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)off);  // 8 codes, 24 bits
     u = (win & 0xFFFu) | ((win << 4) & 0x0FFF0000u);                       // codes 4..7 to bit 16
   }
@@ -110,9 +129,9 @@ __device__ __forceinline__ void code_pairs(const uint32_t* rw, int s, int hh, ui
   for (int j = 1; j < 4; ++j) out[j] = and_or(u >> (SH * j), mask, magic);
 }
 
-template <typename TX>
-__device__ __forceinline__ void store4(TX* p, const float* v) {
-  if constexpr (sizeof(TX) == 2) {
+template <typename TY>
+__device__ __forceinline__ void store4(TY* p, const float* v) {
+  if constexpr (sizeof(TY) == 2) {
     h2 a = {(_Float16)v[0], (_Float16)v[1]};
     h2 b = {(_Float16)v[2], (_Float16)v[3]};
     *reinterpret_cast<uint2*>(p) = make_uint2(as_u32(a), as_u32(b));
@@ -121,26 +140,68 @@ __device__ __forceinline__ void store4(TX* p, const float* v) {
   }
 }
 
-template <int Q, int G, typename TX, bool LOWRANK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ X, int64_t ldx,
-                         const float* __restrict__ dinvsqrt, const uint32_t* __restrict__ codes,
-                         const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-                         const float* __restrict__ Bf, const float* __restrict__ Z,
-                         TX* __restrict__ Y, int64_t ldy, int tiles_n, int tiles) {
-  constexpr int GPK = (G <= BK) ? BK / G : 1;   // groups per step
-  constexpr int SW = 2 * Q;                      // code words per row per step
-  constexpr int CW = 8 * 32 * SW;                // code words per step (8 row tiles)
-  constexpr int SZ = 8 * GPK * 32;               // scales (and zeros) per step
-  constexpr int XV = (int)sizeof(TX) / 2;        // 16-byte loads per 8 channels
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min<int64_t>(bytes, (int64_t)0x7FFFFFF0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
 
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint32_t cs[2][CW];
-  __shared__ __attribute__((aligned(16))) _Float16 szs[2][2 * SZ];  // scales then zeros
-  __shared__ __attribute__((aligned(16))) float dvs[2][BK];
+// 16 bytes per lane from a buffer into LDS; lane l lands at
+// lds_wave_base + 16 * l (the base is the same for the whole wave)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           voff, soff, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of an X row in LDS: rows r and r+1 share
+// a 256-byte bank window, so the pair index picks the permutation and any 16
+// consecutive rows read at one logical chunk hit 16 distinct bank groups
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's buffer loads
+// (direct-to-LDS ones included) are still in flight, and its LDS reads are done
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);
+}
+
+// Workgroup barrier without a memory fence (the waits above order the
+// memory traffic); the empty asm statements stop the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int Q, int G, typename TY, bool LOWRANK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
+                         const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
+                         const _Float16* __restrict__ zeros, const float* __restrict__ Bf,
+                         const float* __restrict__ Z, TY* __restrict__ Y, int64_t ldy, int tiles_n,
+                         int tiles) {
+  constexpr int GPK = (G <= BK) ? BK / G : 1;  // groups per step
+  constexpr int SW = 2 * Q;                     // code words per row per step
+  constexpr int SZ = 8 * GPK * 32;              // scales (and zeros) per step
+  constexpr int SLOTS = SZ / 8;                 // 16-byte slots per scales / zeros
+  constexpr int XSL = BM * BK * 2 / 16;         // 16-byte slots per X tile
+  constexpr int CW = 8 * 32 * SW;               // code words per step (8 row tiles)
+  constexpr int CSL = CW / 4;                   // 16-byte slots of codes per step
+  constexpr int CJ = (CSL + kThreads - 1) / kThreads;
+  static_assert(XSL % kThreads == 0 && CSL % 64 == 0 && SLOTS <= 64, "slot split");
+
+  // One array per stage: an LDS read of one array does not have to wait for
+  // direct-to-LDS loads still landing in another.
+  __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * BK], xs1[BM * BK], xs2[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint32_t cs0[CW], cs1[CW], cs2[CW];
+  __shared__ __attribute__((aligned(16))) _Float16 sz0[2 * SZ], sz1[2 * SZ], sz2[2 * SZ];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
 
   int tile = blockIdx.x;
@@ -160,15 +221,13 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
   uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);  // code bits
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(mask), "+v"(magic));  // keep both in VGPRs for v_and_or_b32
+  asm volatile("; accumulators in AGPRs" ::"a"(0.0f));
 
+  // ---- accumulators: born from MFMAs so they live in AGPRs ----
   f16x acc[FN][FM];
+  f16x c0;
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
+  for (int e = 0; e < 16; ++e) c0[e] = 0.f;
   if constexpr (LOWRANK) {
     h8 bfr[FN];
 #pragma unroll
@@ -196,193 +255,225 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, c0, 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zl, acc[i][j], 0, 0, 0);
       }
     }
+  } else {
+    uint32_t zr = 0u;
+    asm volatile("" : "+v"(zr));
+    const h2 zp = as_h2(zr);
+    const h8 z8 = {zp[0], zp[1], zp[0], zp[1], zp[0], zp[1], zp[0], zp[1]};
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(z8, z8, c0, 0, 0, 0);
   }
 
-  // ---- X staging: thread -> 8-channel chunk xc, rows (tid >> 3) + 32u ----
-  const int xc = tid & 7;
-  const TX* xrow[4];
+  auto xstage = [&](auto st) -> _Float16* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return xs0;
+    else if constexpr (S == 1) return xs1;
+    else return xs2;
+  };
+  auto csstage = [&](auto st) -> uint32_t* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return cs0;
+    else if constexpr (S == 1) return cs1;
+    else return cs2;
+  };
+  auto szstage = [&](auto st) -> _Float16* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return sz0;
+    else if constexpr (S == 1) return sz1;
+    else return sz2;
+  };
+
+  // ---- requests for one step: X, codes, scales and zeros -> LDS ----
+  // Only direct-to-LDS loads run inside the K loop, and one wait per step
+  // (for the loads issued a step earlier) covers them all.  Per-lane byte
+  // offsets are fixed; the step enters as a scalar offset.  Rows past T and
+  // row tiles past d_out fall outside the resources and read as zeros (their
+  // outputs are never stored).
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(Xs + m0 * ldxs, (T - m0) * ldxs * 2);
+  const int64_t ctile = (int64_t)ksteps * 32 * SW;  // words per 32-row tile
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(codes + ntile0 * ctile, (ntiles - ntile0) * ctile * 4);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(scales + (int64_t)ntile0 * ng * 32, (int64_t)(ntiles - ntile0) * ng * 64);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(zeros + (int64_t)ntile0 * ng * 32, (int64_t)(ntiles - ntile0) * ng * 64);
+  // X slot p -> row p / 8, physical chunk p % 8 holding logical chunk
+  // (p % 8) ^ swz(row); slot p + 256 j is row + 32 j with the same swizzle,
+  // so the per-lane offset is shared and j enters the scalar offset
+  const int xrow = wave * 8 + (lane >> 3);
+  const int xoff = (int)(xrow * ldxs * 2) + 16 * ((lane & 7) ^ swz(xrow));
+  const int xjstride = (int)(32 * ldxs * 2);
+  // codes slot p -> row tile p / (16q), 16-byte piece p % (16q) of that
+  // tile's contiguous step chunk
+  int coff[CJ];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t t = min(m0 + (tid >> 3) + 32 * u, T - 1);
-    xrow[u] = X + t * ldx + 8 * xc;
+  for (int j = 0; j < CJ; ++j) {
+    const int p = (wave + 4 * j) * 64 + lane;
+    coff[j] = (int)(((p / (16 * Q)) * ctile + 4 * (p % (16 * Q))) * 4);
   }
-  uint4 xr[4][XV];
-  float4 dvr;  // D^(-1/2) of the step after next (threads < 16 keep it)
+  // scales (wave 0) and zeros (wave 1): lane l < SLOTS moves 8 halfs
+  const int soff = ((lane / (4 * GPK)) * ng * 32 + 8 * (lane % (4 * GPK))) * 2;
 
-  // codes, scales and zeros of one step: 16-byte slots, slot p handled by
-  // thread p % 256; registers now, LDS after the MFMAs of the current step.
-  // (Copying them straight to LDS would make the compiler wait for every
-  // outstanding load before the step's first LDS read.)
-  constexpr int CSL = CW / 4;                        // code slots per step
-  constexpr int CPT = (CSL + kThreads - 1) / kThreads;
-  constexpr int SLOTS = SZ / 8;                      // slots per scales / zeros array
-  static_assert(CPT <= 2, "code slots per thread");
-  uint4 cr0, cr1;  // code slots tid and tid + 256 (scalars: an indexed array
-                   // would be moved out of registers)
-  uint4 sr;
-  // Every thread issues every load (indices clamped into range) and only the
-  // LDS stores are predicated: no divergent branch sits between a load and
-  // its use, so the compiler's wait counts stay exact.
-  auto load_w = [&](int kt) {
-    // a tile's step chunk is 32 * 2Q words = 16Q slots: slot p -> row tile
-    // p / 16Q, words 4 (p % 16Q) of that chunk
-    {
-      const int p = min(tid, CSL - 1);
-      const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
-      cr0 = *reinterpret_cast<const uint4*>(codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q)));
-    }
-    if constexpr (CPT > 1) {
-      const int p = min(tid + kThreads, CSL - 1);
-      const int t = min(ntile0 + p / (16 * Q), ntiles - 1);
-      cr1 = *reinterpret_cast<const uint4*>(codes + ((int64_t)t * ksteps + kt) * (32 * SW) + 4 * (p % (16 * Q)));
-    }
-    const int p = min(tid, 2 * SLOTS - 1);  // slots < SLOTS: scales, then zeros
-    const int arr = p / SLOTS, q8 = p % SLOTS;
-    const int t = min(ntile0 + q8 / (4 * GPK), ntiles - 1);
-    const int within = 8 * (q8 % (4 * GPK));  // halfs inside the tile's GPK x 32 chunk
-    const int gk = (kt * BK) / G;
-    sr = *reinterpret_cast<const uint4*>((arr == 0 ? scales : zeros) + ((int64_t)t * ng + gk) * 32 + within);
-  };
-  auto store_w = [&](int buf) {
-    if (tid < CSL) *reinterpret_cast<uint4*>(&cs[buf][4 * tid]) = cr0;
-    if constexpr (CPT > 1) {
-      if (tid + kThreads < CSL) *reinterpret_cast<uint4*>(&cs[buf][4 * (tid + kThreads)]) = cr1;
-    }
-    if (tid < 2 * SLOTS) *reinterpret_cast<uint4*>(&szs[buf][8 * tid]) = sr;
+  auto load_lds = [&](int kt, _Float16* xs, uint32_t* cs, _Float16* sz) {
+#pragma unroll
+    for (int j = 0; j < XSL / kThreads; ++j)
+      lds_dma16(rs_x, xoff, kt * BK * 2 + j * xjstride, reinterpret_cast<char*>(xs) + 16 * (wave + 4 * j) * 64);
+#pragma unroll
+    for (int j = 0; j < CJ; ++j)
+      if ((wave + 4 * j) * 64 < CSL) lds_dma16(rs_c, coff[j], kt * 32 * SW * 4, cs + 4 * (wave + 4 * j) * 64);
+    if (wave < 2 && lane < SLOTS)
+      lds_dma16(wave == 0 ? rs_s : rs_z, soff, (kt * BK / G) * 32 * 2, sz + wave * SZ);
   };
 
-  auto load_x = [&](int kt) {
-    const int k0 = kt * BK;
+  // ---- operands from LDS ----
+  // per fragment i and group gi (k = i * GPK + gi): the scale s at element k
+  // and -(1024 + z) at element 4 + k
+  typedef h8 Scales;
+  auto read_scales = [&](const _Float16* sz, Scales& out) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < XV; ++v) xr[u][v] = reinterpret_cast<const uint4*>(xrow[u] + k0)[v];
-  };
-
-  auto store_x = [&](int buf) {
-    const float4 da = *reinterpret_cast<const float4*>(&dvs[buf][8 * xc]);
-    const float4 db = *reinterpret_cast<const float4*>(&dvs[buf][8 * xc + 4]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = (tid >> 3) + 32 * u;
-      uint32_t o[4];
-      if constexpr (sizeof(TX) == 2) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(&xr[u][0]);
-        // channel pairs (0,4) (1,5) (2,6) (3,7): halves of words (0,2) (0,2) (1,3) (1,3)
-        o[0] = mix_pair<0>(w[0], w[2], da.x, db.x);
-        o[1] = mix_pair<1>(w[0], w[2], da.y, db.y);
-        o[2] = mix_pair<0>(w[1], w[3], da.z, db.z);
-        o[3] = mix_pair<1>(w[1], w[3], da.w, db.w);
-      } else {
-        const float* e = reinterpret_cast<const float*>(&xr[u][0]);
-        const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          h2 y = {(_Float16)(e[p] * dd[p]), (_Float16)(e[p + 4] * dd[p + 4])};
-          o[p] = as_u32(y);
-        }
-      }
-      *reinterpret_cast<uint4*>(&xs[buf][row * BK + ((xc ^ (row & 7)) * 8)]) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  };
-
-  // ---- prologue: D^(-1/2) of steps 0 and 1, stage 0 ----
-  {
-    const float4 d0 = reinterpret_cast<const float4*>(dinvsqrt)[tid & 15];
-    dvr = reinterpret_cast<const float4*>(dinvsqrt + min(1, ksteps - 1) * BK)[tid & 15];
-    if (tid < 16) *reinterpret_cast<float4*>(&dvs[0][4 * tid]) = d0;
-  }
-  load_w(0);
-  load_x(0);
-  __syncthreads();
-  store_w(0);
-  store_x(0);
-  if (tid < 16 && ksteps > 1) *reinterpret_cast<float4*>(&dvs[1][4 * tid]) = dvr;
-  __syncthreads();
-
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ksteps) {
-      load_w(kt + 1);
-      load_x(kt + 1);
-      dvr = reinterpret_cast<const float4*>(dinvsqrt + min(kt + 2, ksteps - 1) * BK)[tid & 15];
-    }
-    // keep the next step's LDS stores after this step's MFMAs: hoisted next to
-    // their loads they would make every step wait out the load latency
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-
-    // this wave's code words and group parameters for the step
-    uint32_t rw[FN][(Q == 3) ? 6 : 4];
-    h2 sc[FN][GPK], nz[FN][GPK];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int tl = wave * 2 + i;  // row tile inside the workgroup
-      const uint32_t* rowp = &cs[buf][(tl * 32 + l32) * SW];
-      if constexpr (Q == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(rowp + 4 * hh);
-        rw[i][0] = v.x; rw[i][1] = v.y; rw[i][2] = v.z; rw[i][3] = v.w;
-      } else if constexpr (Q == 2) {
-        const uint4 v = *reinterpret_cast<const uint4*>(rowp);
-        rw[i][0] = v.x; rw[i][1] = v.y; rw[i][2] = v.z; rw[i][3] = v.w;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const uint2 v = *reinterpret_cast<const uint2*>(rowp + 2 * k);
-          rw[i][2 * k] = v.x;
-          rw[i][2 * k + 1] = v.y;
-        }
-      }
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int gi = 0; gi < GPK; ++gi) {
-        const _Float16 s = szs[buf][(tl * GPK + gi) * 32 + l32];
-        const _Float16 z = szs[buf][SZ + (tl * GPK + gi) * 32 + l32];
-        const _Float16 n = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
-        sc[i][gi] = h2{s, s};
-        nz[i][gi] = h2{n, n};
+        const int tl = wave * 2 + i;
+        const _Float16 sv = sz[(tl * GPK + gi) * 32 + l32];
+        const _Float16 z = sz[SZ + (tl * GPK + gi) * 32 + l32];
+        out[i * GPK + gi] = sv;
+        out[4 + i * GPK + gi] = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
+      }
+  };
+  auto dequant = [&](auto sc_, const CodeFrag& cf, const Scales& sv, int i) -> h8 {
+    constexpr int S = decltype(sc_)::value;
+    constexpr int gi = (G == 32) ? (S >> 1) : 0;
+    uint32_t pr[4];
+    code_pairs<Q, S>(cf, hh, mask, magic, pr);
+    const h2 sc = {sv[i * GPK + gi], sv[i * GPK + gi]};
+    const h2 nz = {sv[4 + i * GPK + gi], sv[4 + i * GPK + gi]};
+    h8 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h2 wv = (as_h2(pr[j]) + nz) * sc;
+      a[2 * j] = wv[0];
+      a[2 * j + 1] = wv[1];
+    }
+    return a;
+  };
+  auto read_codes = [&](const uint32_t* cs, CodeFrag* cf) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const uint32_t* rowp = cs + ((wave * 2 + i) * 32 + l32) * SW;
+      if constexpr (Q == 4) {
+        cf[i].a = *reinterpret_cast<const u4v*>(rowp + 4 * hh);
+      } else if constexpr (Q == 2) {
+        cf[i].a = *reinterpret_cast<const u4v*>(rowp);
+      } else {
+        const u2v w01 = *reinterpret_cast<const u2v*>(rowp);
+        const u2v w23 = *reinterpret_cast<const u2v*>(rowp + 2);
+        cf[i].b = *reinterpret_cast<const u2v*>(rowp + 4);
+        cf[i].a = u4v{w01[0], w01[1], w23[0], w23[1]};
       }
     }
+  };
+  auto read_b = [&](auto sc_, const _Float16* xs, int j) -> h8 {
+    constexpr int S = decltype(sc_)::value;
+    const int row = j * 32 + l32;
+    const int c = (2 * S + hh) ^ swz(row);
+    return *reinterpret_cast<const h8*>(&xs[row * BK + c * 8]);
+  };
 
+  // ---- pipeline state carried across steps ----
+  // Codes: two register sets, step kt in set kt % 2, read from LDS together
+  // with the scales one sub-step before the first dequantisation that needs
+  // them.
+  CodeFrag cset0[FN], cset1[FN];
+  auto cset = [&](auto c) -> CodeFrag* {
+    if constexpr (decltype(c)::value == 0) return cset0;
+    else return cset1;
+  };
+  h8 aop[2][FN], bop[2][FM];  // operands of even / odd sub-steps
+  Scales szcur, sznext;
+
+  // ---- prologue: steps 0 and 1 requested, step 0's first operands ready ----
+  load_lds(0, xs0, cs0, sz0);
+  if (ksteps > 1) load_lds(1, xs1, cs1, sz1);
+  wait_vmem<0>();
+  block_barrier();
+  read_codes(cs0, cset0);
+  read_scales(sz0, szcur);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      h8 bx[FM];
+  for (int i = 0; i < FN; ++i) aop[0][i] = dequant(ic<0>{}, cset0[i], szcur, i);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = j * 32 + l32;
-        const int c = (2 * s + hh) ^ (row & 7);
-        bx[j] = *reinterpret_cast<const h8*>(&xs[buf][row * BK + c * 8]);
-      }
-      const int gi = (G == 32) ? (s >> 1) : 0;
+  for (int j = 0; j < FM; ++j) bop[0][j] = read_b(ic<0>{}, xs0, j);
+
+  // ---- one K step: LDS stage ST = kt % 3, code set CS = kt % 2 ----
+  auto step = [&](auto stc, auto csc, int kt) {
+    constexpr int ST = decltype(stc)::value, CS = decltype(csc)::value;
+    constexpr int N1 = (ST + 1) % 3, N2 = (ST + 2) % 3;
+    _Float16* xcur = xstage(ic<ST>{});
+    _Float16* xnext = xstage(ic<N1>{});
+    if (kt + 2 < ksteps) load_lds(kt + 2, xstage(ic<N2>{}), csstage(ic<N2>{}), szstage(ic<N2>{}));
+    const CodeFrag* ccur = cset(ic<CS>{});
+    CodeFrag* cnext = cset(ic<CS ^ 1>{});
+    unroll<4>([&](auto sc_) {
+      constexpr int S = decltype(sc_)::value;
+      constexpr int P = S & 1, PN = P ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
+      // The next sub-step's operands.  After the last step these reads fetch
+      // stale, in-bounds data that is never used (no branch, so the reads and
+      // the dequantisation interleave with this sub-step's MFMAs).
+      if constexpr (S < 3) {
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        uint32_t pr[4];
-        code_pairs<Q>(rw[i], s, hh, mask, magic, pr);
-        h8 a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h2 wv = (as_h2(pr[j]) + nz[i][gi]) * sc[i][gi];
-          a[2 * j] = wv[0];
-          a[2 * j + 1] = wv[1];
+        for (int j = 0; j < FM; ++j) bop[PN][j] = read_b(ic<S + 1>{}, xcur, j);
+        if constexpr (S == 2) {
+          read_codes(csstage(ic<N1>{}), cnext);
+          read_scales(szstage(ic<N1>{}), sznext);
         }
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bx[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<S + 1>{}, ccur[i], szcur, i);
+      } else {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) bop[PN][j] = read_b(ic<0>{}, xnext, j);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<0>{}, cnext[i], sznext, i);
       }
-    }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[P][i], bop[P][j], acc[i][j], 0, 0, 0);
+      // one MFMA, then an LDS read and a few VALU operations, eight times
+#pragma unroll
+      for (int m = 0; m < FN * FM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (S == 2) ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    });
+    szcur = sznext;
+    // This wave's share of step kt+2 has landed; after the barrier every wave
+    // sees all of it, and nobody reads stage ST any more.
+    wait_vmem<0>();
+    block_barrier();
+  };
 
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < ksteps) {
-      store_w(buf ^ 1);
-      store_x(buf ^ 1);
-      if (tid < 16 && kt + 2 < ksteps) *reinterpret_cast<float4*>(&dvs[buf][4 * tid]) = dvr;
-    }
-    __syncthreads();
+  // Unrolled by 6 = lcm(3 stages, 2 code sets).  Leaving the loop after any
+  // step (rather than skipping the rest of the body) keeps every path through
+  // the body in one order, so the compiler's wait counts stay exact.
+  for (int kt = 0;; kt += 6) {
+    step(ic<0>{}, ic<0>{}, kt);
+    if (kt + 1 >= ksteps) break;
+    step(ic<1>{}, ic<1>{}, kt + 1);
+    if (kt + 2 >= ksteps) break;
+    step(ic<2>{}, ic<0>{}, kt + 2);
+    if (kt + 3 >= ksteps) break;
+    step(ic<0>{}, ic<1>{}, kt + 3);
+    if (kt + 4 >= ksteps) break;
+    step(ic<1>{}, ic<0>{}, kt + 4);
+    if (kt + 5 >= ksteps) break;
+    step(ic<2>{}, ic<1>{}, kt + 5);
+    if (kt + 6 >= ksteps) break;
   }
 
   // ---- epilogue: lane holds token t = l32, channels 8*(e/4) + 4*hh + e%4 ----
@@ -398,66 +489,66 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const TX* __restrict__ 
         if (n < d_out) {
           float v[4] = {acc[i][j][4 * e4 + 0], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
                         acc[i][j][4 * e4 + 3]};
-          store4<TX>(Y + t * ldy + n, v);
+          store4<TY>(Y + t * ldy + n, v);
         }
       }
     }
   }
 }
 
-template <int Q, int G, typename TX, bool LR>
-hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
+template <int Q, int G, typename TY, bool LR>
+hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
                       const uint32_t* codes, const void* scales, const void* zeros,
                       const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
   const int tiles_n = (d_out + BN - 1) / BN;
   const int64_t tiles_m = (T + BM - 1) / BM;
   const int64_t tiles = tiles_n * tiles_m;
-  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TX, LR>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
-                     d_in, d_out, static_cast<const TX*>(X), ldx, dinv, codes,
+  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
+                     d_in, d_out, static_cast<const _Float16*>(Xs), ldxs, codes,
                      static_cast<const _Float16*>(scales), static_cast<const _Float16*>(zeros), B, Z,
-                     static_cast<TX*>(Y), ldy, tiles_n, (int)tiles);
+                     static_cast<TY*>(Y), ldy, tiles_n, (int)tiles);
   return hipGetLastError();
 }
 
-template <int Q, int G, typename TX>
-hipError_t launch_lr(int r, int64_t T, int d_in, int d_out, const void* X, int64_t ldx,
-                     const float* dinv, const uint32_t* codes, const void* scales, const void* zeros,
-                     const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
-  if (r > 0) return launch_cfg<Q, G, TX, true>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
-  return launch_cfg<Q, G, TX, false>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
+template <int Q, int G, typename TY>
+hipError_t launch_lr(int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
+                     const uint32_t* codes, const void* scales, const void* zeros, const float* B,
+                     const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+  if (r > 0) return launch_cfg<Q, G, TY, true>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+  return launch_cfg<Q, G, TY, false>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
 }
 
-template <int Q, typename TX>
-hipError_t launch_g(int g, int r, int64_t T, int d_in, int d_out, const void* X, int64_t ldx,
-                    const float* dinv, const uint32_t* codes, const void* scales, const void* zeros,
-                    const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+template <int Q, typename TY>
+hipError_t launch_g(int g, int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
+                    const uint32_t* codes, const void* scales, const void* zeros, const float* B,
+                    const float* Z, void* Y, int64_t ldy, hipStream_t s) {
   switch (g) {
-    case 32: return launch_lr<Q, 32, TX>(r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
-    case 64: return launch_lr<Q, 64, TX>(r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
-    default: return launch_lr<Q, 128, TX>(r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 32: return launch_lr<Q, 32, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 64: return launch_lr<Q, 64, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    default: return launch_lr<Q, 128, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   }
 }
 
-template <typename TX>
-hipError_t launch_q(int q, int g, int r, int64_t T, int d_in, int d_out, const void* X, int64_t ldx,
-                    const float* dinv, const uint32_t* codes, const void* scales, const void* zeros,
-                    const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+template <typename TY>
+hipError_t launch_q(int q, int g, int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
+                    const uint32_t* codes, const void* scales, const void* zeros, const float* B,
+                    const float* Z, void* Y, int64_t ldy, hipStream_t s) {
   switch (q) {
-    case 2: return launch_g<2, TX>(g, r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
-    case 3: return launch_g<3, TX>(g, r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
-    default: return launch_g<4, TX>(g, r, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 2: return launch_g<2, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 3: return launch_g<3, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    default: return launch_g<4, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* X,
-                               bool x_f32, int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
-                               const void* scales, const void* zeros, const float* B, const float* Z,
-                               void* Y, int64_t ldy, hipStream_t s) {
-  if (x_f32)
-    return launch_q<float>(q, g, r, T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, B, Z, Y, ldy, s);
-  return launch_q<_Float16>(q, g, r, T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, B, Z, Y, ldy, s);
+hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
+                               int64_t ldxs, const uint32_t* codes, const void* scales,
+                               const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,
+                               int64_t ldy, hipStream_t s) {
+  if (y_f32)
+    return launch_q<float>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+  return launch_q<_Float16>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
 }
 
 }  // namespace ttq

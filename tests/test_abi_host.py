@@ -54,10 +54,13 @@ def test_query_sizes_cfg5(lib):
     assert sz.codes_bytes == 8192 * 160 * 4 * 4          # 20.97 MB of 4-bit codes
     assert sz.scales_bytes == sz.zeros_bytes == 8192 * 160 * 2
     assert sz.d_bytes == sz.dinvsqrt_bytes == 5120 * 4
-    assert sz.wres_bytes == 0 and sz.z_bytes == 0
+    assert sz.wres_bytes == 0
     assert sz.workspace_bytes == lib.ttq_colstats_workspace_bytes(16384, 5120) > 0
+    assert sz.linear_workspace_bytes == lib.ttq_linear_workspace_bytes(16384, 5120, 0) == 16384 * 5120 * 2
     assert lib.ttq_query_sizes(ctypes.byref(_cfg(r=16, q=2)), 100, ctypes.byref(sz)) == 0
-    assert sz.wres_bytes == 8192 * 5120 * 2 and sz.z_bytes == 100 * 16 * 4
+    assert sz.wres_bytes == 8192 * 5120 * 2
+    # pre-scaled input rounded up to 256 bytes, then Z
+    assert sz.linear_workspace_bytes == 100 * 5120 * 2 + 100 * 16 * 4
     assert sz.codes_bytes == 8192 * 160 * 2 * 4
 
 
@@ -99,13 +102,22 @@ def test_null_and_alignment(lib):
     assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.0, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
     assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 4, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_colstats(P, 7, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
-    # gemm: ldy too small, r = 16 without Z, T = 0 is an accepted no-op
-    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 1, 128, P, P, P, P, None, None, P, 32, None) \
+    # gemm: ldy too small, r = 16 without Z, bad output dtype, T = 0 is an accepted no-op
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 128, P, P, P, None, None, P, 1, 32, None) \
         == _capi.TTQ_ERR_SHAPE
-    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 16, P, 1, 128, P, P, P, P, P, None, P, 64, None) \
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 16, P, 128, P, P, P, P, None, P, 1, 64, None) \
         == _capi.TTQ_ERR_NULL
-    assert lib.ttq_wlowbit_gemm(0, 128, 64, 4, 32, 0, None, 1, 128, None, None, None, None, None, None,
-                                None, 64, None) == _capi.TTQ_OK
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 128, P, P, P, None, None, P, 7, 64, None) \
+        == _capi.TTQ_ERR_INVALID_ARG
+    assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 120, P, P, P, None, None, P, 1, 64, None) \
+        == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_wlowbit_gemm(0, 128, 64, 4, 32, 0, None, 128, None, None, None, None, None,
+                                None, 1, 64, None) == _capi.TTQ_OK
+    # prescale: d not a multiple of 64, NULL dinvsqrt, misaligned Xs, T = 0 no-op
+    assert lib.ttq_prescale(P, 1, 4, 96, 96, P, P, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_prescale(P, 1, 4, 128, 128, None, P, None) == _capi.TTQ_ERR_NULL
+    assert lib.ttq_prescale(P, 1, 4, 128, 128, P, MIS, None) == _capi.TTQ_ERR_ALIGN
+    assert lib.ttq_prescale(None, 1, 0, 128, 128, None, None, None) == _capi.TTQ_OK
     # residual and lowrank_z are built for r = 16 only
     assert lib.ttq_residual(64, 128, 8, P, P, P, P, None) == _capi.TTQ_ERR_UNSUPPORTED
     assert lib.ttq_lowrank_z(4, 128, 0, P, 1, 128, P, P, None) == _capi.TTQ_ERR_INVALID_ARG
@@ -113,9 +125,9 @@ def test_null_and_alignment(lib):
 
 
 def _buffers(T_max, r=0, workspace_bytes=1 << 30):
-    z = P if r else None
-    return _capi.ttq_buffers(P.value, P.value, P.value, P.value, P.value, z and P.value,
-                             z and P.value, z and P.value, z and P.value, P.value, T_max, workspace_bytes)
+    f = P.value if r else None
+    return _capi.ttq_buffers(P.value, P.value, P.value, P.value, P.value, f, f, f, P.value, T_max,
+                             workspace_bytes)
 
 
 def test_handle_lifecycle_errors(lib):
@@ -129,7 +141,7 @@ def test_handle_lifecycle_errors(lib):
     try:
         # prepare before the weight is bound, linear before prepare
         assert lib.ttq_prepare(h, P, 1, 4, 128, None) == _capi.TTQ_ERR_INVALID_ARG
-        assert lib.ttq_linear(h, P, 1, 4, 128, P, 64, None) == _capi.TTQ_ERR_INVALID_ARG
+        assert lib.ttq_linear(h, P, 1, 4, 128, P, 64, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
         # r = 0: binding the weight is pure host work (the handle borrows W)
         assert lib.ttq_set_weight(h, P, None) == _capi.TTQ_OK
         assert lib.ttq_set_weight(h, MIS, None) == _capi.TTQ_ERR_ALIGN

@@ -210,7 +210,34 @@ def test_lowrank_z(cfg, T):
 # ---------------------------------------------------------------------------
 # wlowbit_gemm given the oracle's codes
 # ---------------------------------------------------------------------------
-def _gemm_case(cfg, T, q, g, r, sample_rows=None):
+def unpermute8(xs):
+    """Undo the prescale layout: within every 8 channels the stored order is
+    0 4 1 5 2 6 3 7 (include/ttq.h, ttq_prescale)."""
+    T, d = xs.shape
+    blk = xs.reshape(T, d // 8, 8)
+    out = np.empty_like(blk)
+    out[:, :, 0:4] = blk[:, :, 0::2]
+    out[:, :, 4:8] = blk[:, :, 1::2]
+    return out.reshape(T, d)
+
+
+@pytest.mark.parametrize("cfg,T", [(1, 333), (2, 2048), (5, 4097), (3, 1)])
+def test_prescale(cfg, T):
+    w = wl.CONFIGS[cfg]
+    X, _ = cfg_inputs(cfg, T=T, d_out=64)
+    D = oracle.colstats(X, w.p, w.lam, w.alpha)
+    R = oracle_dinvsqrt(D)
+    say(f"prescale cfg={cfg} T={T}")
+    Xs = host(ttq.ttq_prescale(dev(X), dev(R)))
+    assert Xs.dtype == np.float16 and Xs.shape == X.shape
+    ref = X.astype(np.float64) * R.astype(np.float64)[None, :]
+    got = unpermute8(Xs).astype(np.float64)
+    # one fp32 rounding, then one fp16 rounding (normal range)
+    bound = np.abs(ref) * (2.0 ** -11 + 2.0 ** -23) + 2.0 ** -25
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0):
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg, T=T)
     D = oracle.colstats(X, w.p, w.lam, w.alpha)
@@ -224,9 +251,14 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None):
     say(f"gemm cfg={cfg} T={T} q={q} g={g} r={r}")
     Xd = dev(X)
     Zd = ttq.ttq_lowrank_z(Xd, dev(A)) if r else None
-    Yd = ttq.ttq_wlowbit_gemm(Xd, dev(oracle_dinvsqrt(D)), dev(oracle.tile_codes(oracle.pack(c, q), q)),
+    Xs = ttq.ttq_prescale(Xd, dev(oracle_dinvsqrt(D)))
+    if pad_ld:  # the GEMM on a row-strided view of the pre-scaled input
+        wide = torch.zeros((T, X.shape[1] + pad_ld), dtype=torch.float16, device="cuda")
+        wide[:, :X.shape[1]] = Xs
+        Xs = wide[:, :X.shape[1]]
+    Yd = ttq.ttq_wlowbit_gemm(Xs, dev(oracle.tile_codes(oracle.pack(c, q), q)),
                               dev(oracle.tile_groups(s)), dev(oracle.tile_groups(z)), q, g,
-                              W.shape[0], B=dev(B) if r else None, Z=Zd)
+                              W.shape[0], B=dev(B) if r else None, Z=Zd, out_dtype=Xd.dtype)
     Yg = host(Yd)
     assert Yg.dtype == X.dtype and Yg.shape == (T, W.shape[0])
     rows = np.arange(T) if sample_rows is None else sample_rows
@@ -246,6 +278,10 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None):
 ])
 def test_gemm_parity(cfg, T, q, g, r):
     _gemm_case(cfg, T, q, g, r)
+
+
+def test_gemm_parity_strided_input():
+    _gemm_case(3, 300, 4, 32, 0, pad_ld=64)
 
 
 @pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16)])
