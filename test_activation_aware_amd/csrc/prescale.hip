@@ -11,7 +11,8 @@
 // order in which the GEMM's dequantisation produces weight pairs), rows of
 // d fp16 values.
 //
-// Layout of the work: a workgroup owns 16 tokens; its 4 waves take 32-channel
+// Xs alone streams rows (8 channels per thread, D^(-1/2) held in registers).
+// With Z: a workgroup owns 16 tokens; its 4 waves take 32-channel
 // chunks round-robin, so at any time the workgroup streams 128 contiguous
 // channels of 16 rows.  Lane l holds token l%16 and channels 8*(l/16)..+8 of
 // the chunk: exactly the A operand of a 16x16x32 fp16 MFMA, whose B operand
@@ -118,6 +119,38 @@ __global__ __launch_bounds__(256) void prescale_z_kernel(int64_t T, int d, const
   }
 }
 
+// Xs only (r = 0): a pure stream.  Thread = 8 channels (one 16-byte piece of
+// Xs), D^(-1/2) of its channels held in registers across kRows rows; a wave
+// moves 1 KB of contiguous row bytes per load and per store.
+constexpr int kRows = 32;
+
+template <typename TX>
+__global__ __launch_bounds__(256) void prescale_kernel(int64_t T, int d, const TX* __restrict__ X,
+                                                       int64_t ldx, const float* __restrict__ dinvsqrt,
+                                                       _Float16* __restrict__ Xs) {
+  const int c8 = blockIdx.y * 256 + threadIdx.x;  // 8-channel piece
+  if (c8 * 8 >= d) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kRows;
+  const int rows = (int)min<int64_t>(kRows, T - t0);
+  const float4 da = *reinterpret_cast<const float4*>(dinvsqrt + 8 * c8);
+  const float4 db = *reinterpret_cast<const float4*>(dinvsqrt + 8 * c8 + 4);
+  const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+  const TX* xp = X + t0 * ldx + 8 * c8;
+  _Float16* yp = Xs + t0 * d + 8 * c8;
+#pragma unroll 8
+  for (int i = 0; i < rows; ++i) {
+    float x[8];
+    load8<TX>(xp + i * ldx, x);
+    h8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (_Float16)(x[e] * dv[e]);
+      o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+    }
+    *reinterpret_cast<h8*>(yp + (int64_t)i * d) = o;
+  }
+}
+
 template <typename TX>
 hipError_t launch_tx(int64_t T, int d, const void* X, int64_t ldx, const float* dinv, void* Xs,
                      const float* A, float* Z, hipStream_t s) {
@@ -127,7 +160,8 @@ hipError_t launch_tx(int64_t T, int d, const void* X, int64_t ldx, const float* 
   if (Xs && Z)
     hipLaunchKernelGGL((prescale_z_kernel<TX, true, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
   else if (Xs)
-    hipLaunchKernelGGL((prescale_z_kernel<TX, true, false>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+    hipLaunchKernelGGL((prescale_kernel<TX>), dim3((unsigned)((T + kRows - 1) / kRows), (unsigned)((d / 8 + 255) / 256)),
+                       dim3(256), 0, s, T, d, x, ldx, dinv, xs);
   else
     hipLaunchKernelGGL((prescale_z_kernel<TX, false, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
   return hipGetLastError();

@@ -30,7 +30,9 @@
 // Codes use a reciprocal fast path: with r = 1/s (one IEEE division per
 // group), u = fma(v, r, z) lies within 2^-18 of v/s + z, so whenever u is
 // more than 2^-16 away from every half-integer, rint(u) equals
-// rint(fl(v/s)) + z exactly.  Otherwise the element takes the IEEE division.
+// rint(fl(v/s)) + z exactly.  If any element of a thread's 32-channel block
+// comes closer, the whole block is redone with the IEEE division (rare; the
+// fast codes of the other elements would have been the same).
 #include "ttq_internal.h"
 
 #pragma clang fp contract(off)
@@ -158,18 +160,27 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       const float rcp = 1.0f / s;
 
       uint32_t word[Q];
-#pragma unroll
-      for (int i = 0; i < Q; ++i) word[i] = 0u;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float u = __builtin_fmaf(v[k], rcp, zf);
-        float c = rintf(u);
-        if (fabsf(u - c) > 0.5f - 0x1p-16f) c = rintf(v[k] / s) + zf;  // near a tie: exact path
-        c = fminf(fmaxf(c, 0.0f), N);
-        const uint32_t ci = (uint32_t)c;
+      auto put = [&](int k, float c) {
+        const uint32_t ci = (uint32_t)fminf(fmaxf(c, 0.0f), N);
         const int bit = Q * k;
         word[bit >> 5] |= ci << (bit & 31);
         if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
+      };
+#pragma unroll
+      for (int i = 0; i < Q; ++i) word[i] = 0u;
+      bool near_tie = false;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float u = __builtin_fmaf(v[k], rcp, zf);
+        const float c = rintf(u);
+        near_tie |= fabsf(u - c) > 0.5f - 0x1p-16f;
+        put(k, c);
+      }
+      if (near_tie) {  // rare: redo the block with the IEEE division
+#pragma unroll
+        for (int i = 0; i < Q; ++i) word[i] = 0u;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) put(k, rintf(v[k] / s) + zf);
       }
       uint32_t* dst = &outc[(ksl * 32 + r) * SW];
 #pragma unroll
