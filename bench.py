@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels")
+    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels; "
+                    "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
+                    "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -126,11 +128,30 @@ def main():
             "wlowbit_gemm": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
                              "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
         }
+        # context: torch's dense fp16 GEMM (hipBLASLt) of the same shape on the
+        # same activations, i.e. what an unquantised q_proj costs on this GPU
+        Wd = torch.randn((d_out, d), dtype=torch.float16, device="cuda") * 0.01
+        for _ in range(3):
+            torch.nn.functional.linear(X, Wd)
+        t_dense = time_loop(lambda: torch.nn.functional.linear(X, Wd), n_k, torch)
+        kernels["dense_fp16_gemm_context"] = {"us": t_dense * 1e6, "TFLOPs": gm_flops / t_dense / 1e12}
+        del Wd
         result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS,
                               "traffic": None, "kernel": "ttq_wlowbit_gemm"}
         log(f"bench: kernels {json.dumps(kernels)}")
+
+    # ---- a plain copy of known size: calibrates the byte counters ----
+    if "copy" in only:
+        nbytes = 512 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {nbytes} bytes 3 times")
+        del src, dst
 
     # ---- r = 16: the same step with the rank-16 factors ----
     r16 = None

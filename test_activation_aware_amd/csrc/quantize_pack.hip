@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   __shared__ __attribute__((aligned(16))) _Float16 wt[32 * kRowPitch];
   __shared__ float sq[kCols];
   __shared__ __attribute__((aligned(16))) uint32_t outc[4 * 32 * SW];
-  __shared__ _Float16 outs[GPW * 32], outz[GPW * 32];
+  __shared__ __attribute__((aligned(16))) _Float16 outs[GPW * 32], outz[GPW * 32];
   __shared__ float red_mn[8][32], red_mx[8][32];
 
   const int tid = threadIdx.x;
@@ -87,16 +87,21 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   // sqrt(D) of this workgroup's channels, correctly rounded, once
   if (tid < width) sq[tid] = sqrtf(D[c0 + tid]);
 
-  // slab loader: 1024 16-byte pieces, piece p -> row p / 32, column 8 * (p % 32)
-  uint4 pre[4];
+  // slab loader: 1024 16-byte pieces, piece p -> row p / 32, column 8 * (p % 32).
+  // Four named registers, not an array: an array captured by reference would
+  // be placed in scratch memory.
+  uint4 pre0 = make_uint4(0, 0, 0, 0), pre1 = pre0, pre2 = pre0, pre3 = pre0;
+  auto piece_ptr = [&](int nt, int i) -> const uint4* {
+    const int p = tid + i * kThreads;
+    const int row = p >> 5, col = (p & 31) * 8;
+    return reinterpret_cast<const uint4*>(W + (int64_t)(nt * 32 + row) * d_in + c0 + col);
+  };
+  auto piece_ok = [&](int i) { return ((tid + i * kThreads) & 31) * 8 < width; };
   auto load_tile = [&](int nt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = tid + i * kThreads;
-      const int row = p >> 5, col = (p & 31) * 8;
-      if (col < width)
-        pre[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(nt * 32 + row) * d_in + c0 + col);
-    }
+    if (piece_ok(0)) pre0 = *piece_ptr(nt, 0);
+    if (piece_ok(1)) pre1 = *piece_ptr(nt, 1);
+    if (piece_ok(2)) pre2 = *piece_ptr(nt, 2);
+    if (piece_ok(3)) pre3 = *piece_ptr(nt, 3);
   };
   if (t_begin < t_end) load_tile(t_begin);
 
@@ -107,12 +112,15 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
 
   for (int nt = t_begin; nt < t_end; ++nt) {
     __syncthreads();  // previous tile's LDS reads and stores are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    auto park = [&](int i, const uint4& v) {
       const int p = tid + i * kThreads;
       const int row = p >> 5, col = (p & 31) * 8;
-      if (col < width) *reinterpret_cast<uint4*>(&wt[row * kRowPitch + col]) = pre[i];
-    }
+      if (col < width) *reinterpret_cast<uint4*>(&wt[row * kRowPitch + col]) = v;
+    };
+    park(0, pre0);
+    park(1, pre1);
+    park(2, pre2);
+    park(3, pre3);
     __syncthreads();
     if (nt + 1 < t_end) load_tile(nt + 1);
 
@@ -199,14 +207,15 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       for (int i = tid; i < words / 4; i += kThreads)
         reinterpret_cast<uint4*>(gdst)[i] = reinterpret_cast<const uint4*>(outc)[i];
     }
-    // scales / zeros: groups [c0/G, c0/G + width/G) of tile nt are contiguous
+    // scales / zeros: groups [c0/G, c0/G + width/G) of tile nt are contiguous;
+    // 16-byte pieces, the first threads take the scales, the next the zeros
     {
-      const int n = (width / G) * 32;
+      const int pieces = (width / G) * 32 / 8;
       const int64_t off = ((int64_t)nt * (d_in / G) + c0 / G) * 32;
-      for (int i = tid; i < n; i += kThreads) {
-        scales[off + i] = outs[i];
-        zeros[off + i] = outz[i];
-      }
+      if (tid < pieces)
+        reinterpret_cast<uint4*>(scales + off)[tid] = reinterpret_cast<const uint4*>(outs)[tid];
+      else if (tid < 2 * pieces)
+        reinterpret_cast<uint4*>(zeros + off)[tid - pieces] = reinterpret_cast<const uint4*>(outz)[tid - pieces];
     }
   }
 }

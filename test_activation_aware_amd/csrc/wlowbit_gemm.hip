@@ -8,11 +8,12 @@
 // that consumes the pre-scaled input).
 //
 // CDNA4 design (gfx950, wave64, MFMA v_mfma_f32_32x32x16_f16):
-//   * A workgroup of 4 waves computes a 256 (output channels) x 128 (tokens)
-//     tile of Y^T; wave w owns channels [64w, 64w + 64) x all 128 tokens as
-//     2 x 4 fragments of 32x32.  The fp32 accumulators live in the
-//     accumulator registers (AGPRs), 128 per lane, leaving 128 VGPRs for
-//     operands and prefetches: two workgroups fit on a CU.
+//   * A workgroup of 4 waves computes a 256 (output channels) x 32*FM
+//     (tokens) tile of Y^T; wave w owns channels [64w, 64w + 64) x all the
+//     tokens as 2 x FM fragments of 32x32.  The fp32 accumulators live in the
+//     accumulator registers (AGPRs).  Long prompts use FM = 8 (256 AGPRs, one
+//     workgroup per CU: each weight fragment dequantised once feeds 8 MFMAs);
+//     short ones FM = 4 (128 AGPRs, two workgroups per CU).
 //   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
 //     input (columns = tokens): accumulator lanes hold 4 consecutive output
 //     channels of one token, stored as 8 or 16 bytes.
@@ -62,10 +63,8 @@ typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int BN = 256;  // output channels per workgroup
-constexpr int BM = 128;  // tokens per workgroup
 constexpr int BK = 64;   // input channels per step
 constexpr int FN = 2;    // 32-row fragments per wave
-constexpr int FM = 4;    // 32-token fragments per wave
 constexpr int kXcds = 8;
 
 template <int I>
@@ -176,13 +175,18 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int Q, int G, typename TY, bool LOWRANK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+// FM 32-token fragments per wave: FM = 8 (256 tokens per workgroup, one
+// workgroup per CU, 256 accumulator registers per lane) for long prompts,
+// FM = 4 (128 tokens, two workgroups per CU) for short ones.
+template <int Q, int G, typename TY, bool LOWRANK, int FM>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(FM == 8 ? 1 : 2, FM == 8 ? 1 : 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
                          const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
                          const _Float16* __restrict__ zeros, const float* __restrict__ Bf,
                          const float* __restrict__ Z, TY* __restrict__ Y, int64_t ldy, int tiles_n,
                          int tiles) {
+  constexpr int BM = 32 * FM;                   // tokens per workgroup
   constexpr int GPK = (G <= BK) ? BK / G : 1;  // groups per step
   constexpr int SW = 2 * Q;                     // code words per row per step
   constexpr int SZ = 8 * GPK * 32;              // scales (and zeros) per step
@@ -448,7 +452,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
       for (int m = 0; m < FN * FM; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, (S == 2) ? 2 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FM == 8 ? 2 : 4, 0);
       }
     });
     szcur = sznext;
@@ -496,18 +500,30 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   }
 }
 
-template <int Q, int G, typename TY, bool LR>
-hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                      const uint32_t* codes, const void* scales, const void* zeros,
-                      const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+template <int Q, int G, typename TY, bool LR, int FM>
+hipError_t launch_fm(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
+                     const uint32_t* codes, const void* scales, const void* zeros,
+                     const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+  constexpr int BM = 32 * FM;
   const int tiles_n = (d_out + BN - 1) / BN;
   const int64_t tiles_m = (T + BM - 1) / BM;
   const int64_t tiles = tiles_n * tiles_m;
-  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
+  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR, FM>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
                      d_in, d_out, static_cast<const _Float16*>(Xs), ldxs, codes,
                      static_cast<const _Float16*>(scales), static_cast<const _Float16*>(zeros), B, Z,
                      static_cast<TY*>(Y), ldy, tiles_n, (int)tiles);
   return hipGetLastError();
+}
+
+// 256-token tiles once there are enough of them to give every CU a few
+template <int Q, int G, typename TY, bool LR>
+hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
+                      const uint32_t* codes, const void* scales, const void* zeros,
+                      const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+  const int64_t tiles8 = ((d_out + BN - 1) / BN) * ((T + 255) / 256);
+  if (tiles8 >= 1024)
+    return launch_fm<Q, G, TY, LR, 8>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+  return launch_fm<Q, G, TY, LR, 4>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
 }
 
 template <int Q, int G, typename TY>
