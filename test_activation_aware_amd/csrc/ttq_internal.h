@@ -27,6 +27,14 @@ hipError_t launch_prescale_z(int64_t T, int d, const void* X, bool x_f32, int64_
                              const float* dinvsqrt, void* Xs, const float* A, float* Z,
                              hipStream_t s);
 
+// Few-token (decode) form of the projection: split-K weight streaming.
+constexpr int kDecodeMaxT = 64;
+hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
+                                 int64_t ldxs, const uint32_t* codes, const void* scales, const void* zeros,
+                                 const float* B, const float* Z, void* Y, bool y_f32, int64_t ldy,
+                                 hipStream_t s);
+
+// The projection; T <= kDecodeMaxT goes to the decode kernel.
 hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
                                int64_t ldxs, const uint32_t* codes, const void* scales,
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,

@@ -562,6 +562,8 @@ hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int
                                int64_t ldxs, const uint32_t* codes, const void* scales,
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,
                                int64_t ldy, hipStream_t s) {
+  if (T <= kDecodeMaxT)
+    return launch_wlowbit_decode(T, d_in, d_out, q, g, r, Xs, ldxs, codes, scales, zeros, B, Z, Y, y_f32, ldy, s);
   if (y_f32)
     return launch_q<float>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   return launch_q<_Float16>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);

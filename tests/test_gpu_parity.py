@@ -280,8 +280,19 @@ def test_gemm_parity(cfg, T, q, g, r):
     _gemm_case(cfg, T, q, g, r)
 
 
+@pytest.mark.parametrize("cfg,T,q,g,r", [
+    (1, 1, 4, 32, 0), (1, 5, 4, 32, 0), (2, 2, 3, 32, 16), (2, 33, 3, 32, 16),
+    (3, 7, 4, 64, 0), (3, 64, 4, 128, 0), (3, 31, 2, 32, 0), (4, 16, 4, 32, 16), (4, 63, 2, 64, 0),
+    (5, 1, 4, 32, 0), (5, 64, 4, 32, 16),
+])
+def test_decode_parity(cfg, T, q, g, r):
+    """T <= 64 takes the split-K decode kernel."""
+    _gemm_case(cfg, T, q, g, r)
+
+
 def test_gemm_parity_strided_input():
     _gemm_case(3, 300, 4, 32, 0, pad_ld=64)
+    _gemm_case(3, 40, 4, 32, 0, pad_ld=64)
 
 
 @pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16)])
