@@ -34,7 +34,8 @@ typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRound = 8;  // steps whose codes and scales a wave holds at once
+constexpr int kRound = 16;  // steps whose codes a wave holds at once
+
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -112,8 +113,11 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     const _Float16* __restrict__ zeros, const float* __restrict__ Bf, const float* __restrict__ Z,
     TY* __restrict__ Y, int64_t ldy) {
   constexpr int SW = 2 * Q;                     // code words per row per step
-  constexpr int GPK = (G <= 64) ? 64 / G : 1;   // groups per step
+  constexpr int kXAhead = (NF == 1) ? 4 : 2;    // steps of input requested ahead of use
+  // groups a round of kRound steps can touch, in 16-byte pieces of 8 halfs
+  constexpr int kGroupPieces = ((kRound * 64 + 2 * G - 2) / G + 1 + 15) / 16 * 64;
   __shared__ f16x part[kWaves][NF][64];
+  __shared__ __attribute__((aligned(16))) _Float16 sgrp[kWaves][2][kGroupPieces * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,55 +137,84 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
 
+  // Wave w takes the contiguous steps [kb, ke): its codes are one contiguous
+  // run of (ke - kb) KB (q = 4), its scales and zeros one run of groups.
+  const int per = (ksteps + kWaves - 1) / kWaves;
+  const int kb = min(wave * per, ksteps), ke = min(kb + per, ksteps);
   const uint32_t* ctile = codes + (int64_t)nt * ksteps * 32 * SW + l32 * SW;
-  const _Float16* stile = scales + (int64_t)nt * ng * 32 + l32;
-  const _Float16* ztile = zeros + (int64_t)nt * ng * 32 + l32;
+  const _Float16* stile = scales + (int64_t)nt * ng * 32;
+  const _Float16* ztile = zeros + (int64_t)nt * ng * 32;
   // this lane's token rows (rows past T read row T - 1; never stored)
   const _Float16* xrow[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) xrow[f] = Xs + (int64_t)min(32 * f + l32, T - 1) * ldxs + 8 * hh;
+  auto load_x = [&](int k, h8 (&xb)[4][NF]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
+  };
+  _Float16* ssc = &sgrp[wave][0][0];
+  _Float16* szr = &sgrp[wave][1][0];
 
-  for (int k0 = wave; k0 < ksteps; k0 += kWaves * kRound) {
-    // codes and scales of up to kRound steps k0, k0 + 8, ... in flight at once
+  for (int k0 = kb; k0 < ke; k0 += kRound) {
+    const int nk = min(kRound, ke - k0);
+    // Requests in the order they are needed: the round's scales and zeros
+    // (groups [g0, g1] of this tile, 32 halfs each, contiguous; 16-byte
+    // pieces into this wave's LDS slice), then the codes, then the input.
+    const int g0 = (k0 * 64) / G, g1 = ((k0 + nk - 1) * 64 + 63) / G;
+    const int pieces = (g1 - g0 + 1) * 4;
+    constexpr int SJ = kGroupPieces / 64;
+    uint4 sreg[SJ], zreg[SJ];
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) {
+      const int p = min(64 * j + lane, pieces - 1);
+      sreg[j] = reinterpret_cast<const uint4*>(stile + (int64_t)g0 * 32)[p];
+      zreg[j] = reinterpret_cast<const uint4*>(ztile + (int64_t)g0 * 32)[p];
+    }
+    // codes of up to kRound steps in flight at once
     CodeStep cs[kRound];
-    h2 sc[kRound][GPK], nz[kRound][GPK];
 #pragma unroll
-    for (int i = 0; i < kRound; ++i) {
-      const int k = min(k0 + kWaves * i, ksteps - 1);
-      cs[i] = load_codes<Q>(ctile + (int64_t)k * 32 * SW, hh);
+    for (int i = 0; i < kRound; ++i) cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, ke - 1) * 32 * SW, hh);
+    // the pre-scaled input of the next kXAhead steps in flight (it comes from
+    // L2; one step of MFMAs is far shorter than an L2 round trip)
+    h8 xr[kXAhead][4][NF];
 #pragma unroll
-      for (int gi = 0; gi < GPK; ++gi) {
-        const int grp = (k * 64) / G + gi;
-        const _Float16 s = stile[grp * 32];
-        const _Float16 z = ztile[grp * 32];
-        const _Float16 n = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
-        sc[i][gi] = h2{s, s};
-        nz[i][gi] = h2{n, n};
+    for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
+    // scales and zeros land first: park them in LDS, where every lane finds
+    // its row's values
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) {
+      const int p = 64 * j + lane;
+      if (p < pieces) {
+        reinterpret_cast<uint4*>(ssc)[p] = sreg[j];
+        reinterpret_cast<uint4*>(szr)[p] = zreg[j];
       }
     }
 #pragma unroll
     for (int i = 0; i < kRound; ++i) {
-      const int k = k0 + kWaves * i;
-      if (k >= ksteps) continue;
-      h8 xb[4][NF];
+      const int k = k0 + i;
+      if (i < nk) {
+        const h8 (&xb)[4][NF] = xr[i % kXAhead];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+          const int grp = (k * 64 + 16 * s) / G - g0;
+          const _Float16 sv = ssc[grp * 32 + l32];
+          const _Float16 nv = (_Float16)(-1024.0f) - szr[grp * 32 + l32];  // -(1024 + z), exact
+          const h2 sc = {sv, sv}, nz = {nv, nv};
+          uint32_t pr[4];
+          code_pairs<Q>(cs[i], s, hh, mask, magic, pr);
+          h8 a;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
+          for (int j = 0; j < 4; ++j) {
+            const h2 wv = (as_h2(pr[j]) + nz) * sc;
+            a[2 * j] = wv[0];
+            a[2 * j + 1] = wv[1];
+          }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int gi = (G == 32) ? (s >> 1) : 0;
-        uint32_t pr[4];
-        code_pairs<Q>(cs[i], s, hh, mask, magic, pr);
-        h8 a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const h2 wv = (as_h2(pr[j]) + nz[i][gi]) * sc[i][gi];
-          a[2 * j] = wv[0];
-          a[2 * j + 1] = wv[1];
+          for (int f = 0; f < NF; ++f) acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, xb[s][f], acc[f], 0, 0, 0);
         }
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, xb[s][f], acc[f], 0, 0, 0);
+        if (i + kXAhead < nk) load_x(k + kXAhead, xr[i % kXAhead]);
       }
     }
   }
