@@ -18,8 +18,10 @@ bounded sample as a baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,6 +43,25 @@ def parse():
                     "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
                     "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qwen3_32b_qproj_q4g32r0.md")
+GEMM_SOURCE = os.path.join(ROOT, "test_activation_aware_amd", "csrc", "wlowbit_gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter runs, or None when
+    the GEMM source has changed since they were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    sha = re.search(r"source sha256 of wlowbit_gemm\.hip: ([0-9a-f]{64})", text)
+    val = re.search(r"traffic bytes per launch: (\d+)", text)
+    if not sha or not val or sha.group(1) != src:
+        return None
+    return int(val.group(1))
 
 
 def log(msg):
@@ -139,7 +160,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                              "traffic": None, "kernel": "ttq_wlowbit_gemm"}
+                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm"}
         log(f"bench: kernels {json.dumps(kernels)}")
 
     # ---- a plain copy of known size: calibrates the byte counters ----

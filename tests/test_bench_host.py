@@ -1,0 +1,28 @@
+"""Host-side checks of bench.py: the roofline traffic figure is read from the
+committed counter summary only while the GEMM source it was measured on is
+unchanged, and more than one GPU is refused."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_traffic_matches_committed_kernel():
+    t = bench.gemm_traffic()
+    assert t is not None and t > 0
+
+
+def test_traffic_is_null_for_another_source(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text(open(bench.GEMM_SOURCE).read() + "\n// changed\n")
+    monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
+    assert bench.gemm_traffic() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
