@@ -83,8 +83,8 @@ def time_loop(fn, n, torch):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU sharding of the path is "
-              "described, not implemented (use --gpus 1)", file=sys.stderr)
+        print("bench.py: this implementation runs on one GPU only; the multi-GPU sharding of the path "
+              "is described, not implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels"}
 
