@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed steps run for this long before the warmup steps, so that the GPU's "
+                         "clock and power state is the steady one of continuous work")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
     ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels; "
                     "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
@@ -80,6 +83,20 @@ def time_loop(fn, n, torch):
     return e0.elapsed_time(e1) / n * 1e-3  # seconds
 
 
+def settle(fn, ms, torch):
+    """Run fn() back to back for about ms milliseconds (untimed).  After an idle
+    spell the first GEMMs run up to 30 % slower while the power controller
+    settles; without this the timed steps would measure that transient."""
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        n += 4
+    return n
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,10 +112,10 @@ def main():
     import workloads as wl
 
     torch.cuda.set_device(0)
-    w = wl.CONFIGS[5]
+    w = wl.by_name("qwen3_32b_qproj")
     T, d, d_out, q, g = w.T, w.d, w.d_out, 4, 32
     log(f"bench: generating inputs T={T} d={d} d'={d_out}")
-    X_np, W_np = wl.config_inputs(5)
+    X_np, W_np = wl.config_inputs(w.cfg)
     X = torch.from_numpy(X_np).cuda()
     W = torch.from_numpy(W_np).cuda()
     Y = torch.empty((T, d_out), dtype=torch.float16, device="cuda")
@@ -111,6 +128,8 @@ def main():
 
     result = {}
     # ---- the headline step: prepare + prefill projection, r = 0 ----
+    n_settle = settle(step, args.settle_ms, torch)
+    log(f"bench: {n_settle} settling steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -123,7 +142,29 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     value = T * args.steps / elapsed / 1e3
 
-    # ---- per-kernel times (same inputs, same launch configuration) ----
+    # ---- the GEMM's own duration inside the step ----
+    # The step again, composed of the two entry points ttq_linear is made of
+    # (ttq_prescale, then ttq_wlowbit_gemm on the same buffers and launch
+    # configuration), with HIP events on the launching stream around the
+    # GEMM: its average duration in the step's own power and cache state.
+    gemm_flops = 2.0 * T * d * d_out
+    t_gm_step = None
+    if "kernels" in only:
+        s = torch.cuda.current_stream()
+        Xs_step = torch.empty((T, d), dtype=torch.float16, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            layer.prepare(X)
+            ttq.ttq_prescale(X, layer.dinvsqrt, out=Xs_step)
+            e0.record(s)
+            ttq.ttq_wlowbit_gemm(Xs_step, layer.codes, layer.scales, layer.zeros, q, g, d_out, out=Y)
+            e1.record(s)
+        torch.cuda.synchronize()
+        t_gm_step = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) * 1e-3
+        del Xs_step
+
+    # ---- per-kernel times, back to back (same inputs, same launch configuration) ----
     kernels = {}
     n_k = max(10, args.steps)
     if "kernels" in only:
@@ -138,7 +179,7 @@ def main():
         cs_bytes = T * d * 2 + 8 * d
         qp_bytes = 2 * d_out * d + 4 * d + q * d_out * d // 8 + 4 * d_out * d // g
         ps_bytes = 4 * T * d + 4 * d
-        gm_flops = 2.0 * T * d * d_out
+        gm_flops = gemm_flops
         kernels = {
             "colstats": {"us": t_cs * 1e6, "GBs": cs_bytes / t_cs / 1e9,
                          "frac_hbm": cs_bytes / t_cs / 1e9 / HBM_PEAK_GBS},
@@ -148,6 +189,8 @@ def main():
                          "frac_hbm": ps_bytes / t_ps / 1e9 / HBM_PEAK_GBS},
             "wlowbit_gemm": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
                              "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
+            "wlowbit_gemm_in_step": {"us": t_gm_step * 1e6, "TFLOPs": gm_flops / t_gm_step / 1e12,
+                                     "frac_mfma": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS},
         }
         # context: torch's dense fp16 GEMM (hipBLASLt) of the same shape on the
         # same activations, i.e. what an unquantised q_proj costs on this GPU
@@ -157,10 +200,11 @@ def main():
         t_dense = time_loop(lambda: torch.nn.functional.linear(X, Wd), n_k, torch)
         kernels["dense_fp16_gemm_context"] = {"us": t_dense * 1e6, "TFLOPs": gm_flops / t_dense / 1e12}
         del Wd
-        result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm / 1e12,
+        result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm_step / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm"}
+                              "frac": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm",
+                              "launch_us": t_gm_step * 1e6}
         log(f"bench: kernels {json.dumps(kernels)}")
 
     # ---- a plain copy of known size: calibrates the byte counters ----
@@ -185,6 +229,7 @@ def main():
         def step16():
             layer16.prepare(X)
             layer16.linear(X, out=Y)
+        settle(step16, args.settle_ms, torch)
         for _ in range(args.warmup):
             step16()
         t16 = time_loop(step16, args.steps, torch)
@@ -199,7 +244,7 @@ def main():
     if "decode" in only:
         layer.prepare(X)
         for Td in w.decode_T:
-            Xn = torch.from_numpy(wl.decode_inputs(5, Td, step=Td)).cuda()
+            Xn = torch.from_numpy(wl.decode_inputs(w.cfg, Td, step=Td)).cuda()
             Yn = torch.empty((Td, d_out), dtype=torch.float16, device="cuda")
             for _ in range(3):
                 layer.linear(Xn, out=Yn)
@@ -242,6 +287,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",

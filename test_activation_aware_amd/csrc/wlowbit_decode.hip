@@ -8,14 +8,16 @@
 // Qwen3-32B q_proj at q = 4): the kernel is HBM-bound, so it is built for
 // memory parallelism rather than for matrix-core occupancy.
 //   * One workgroup of 8 waves per 32-row tile of W (d_out / 32 workgroups);
-//     wave w takes the tile's 64-channel steps w, w + 8, w + 16, ...  The
-//     tiled code layout makes a step of a tile one contiguous 1 KB chunk, so
-//     the 8 waves stream 8 KB of contiguous codes at a time.
-//   * A wave requests the codes and scales of up to 8 of its steps at once
-//     (registers), then runs them: per 16-channel sub-step one
-//     v_mfma_f32_32x32x16_f16 per 32 tokens, A = dequantised weights (same
-//     register dequantisation as the prefill kernel), B = the pre-scaled
-//     input read straight from global memory (it is small and stays in L2).
+//     wave w takes a contiguous range of the tile's 64-channel steps.  The
+//     tiled code layout makes a step of a tile one contiguous 1 KB chunk
+//     (q = 4), so a wave's codes are one contiguous run, and its scales and
+//     zeros another.
+//   * A wave first requests its scales and zeros (16-byte loads, parked in
+//     LDS for per-step reads), then the codes of up to 16 steps at once
+//     (registers), and keeps the pre-scaled input of the next 2 - 4 steps in
+//     flight.  Per 16-channel sub-step: one v_mfma_f32_32x32x16_f16 per 32
+//     tokens, A = dequantised weights (the register dequantisation of the
+//     prefill kernel), B = the pre-scaled input (small; it stays in L2).
 //   * The 8 partial products meet in LDS in a fixed order (deterministic) and
 //     are stored as fp16 or fp32.
 //   * Rank-16 term: B16 x Z_hi + B16 x Z_lo (Z split into two fp16 parts)

@@ -17,15 +17,18 @@
 //   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
 //     input (columns = tokens): accumulator lanes hold 4 consecutive output
 //     channels of one token, stored as 8 or 16 bytes.
-//   * K loop in steps of 64 input channels through a three-stage ring:
-//       Xs tile   128 rows x 128 bytes, global -> LDS by direct-to-LDS loads,
-//                 an XOR swizzle of 16-byte chunks applied through the source
-//                 addresses (conflict-free MFMA operand reads);
-//       scales and zeros of the step, global -> LDS the same way;
-//       codes     global -> registers: one 32-row tile's step is a contiguous
-//                 chunk (tiled storage order), so a wave's load of a fragment's
-//                 codes moves 1 KB of contiguous bytes.
-//     Step k+2 is requested while step k runs; a single barrier per step.
+//   * K loop in steps of 64 input channels through a three-stage LDS ring,
+//     filled only by direct-to-LDS buffer loads:
+//       Xs tile   32*FM rows x 128 bytes, an XOR swizzle of 16-byte chunks
+//                 applied through the source addresses (conflict-free MFMA
+//                 operand reads);
+//       codes     one 32-row tile's step is a contiguous chunk (tiled storage
+//                 order), so each wave load moves 1 KB of contiguous bytes;
+//       scales and zeros of the step.
+//     Step k+2 is requested while step k runs; one wait and one barrier per
+//     step.  Keeping every load of the loop direct-to-LDS keeps the compiler's
+//     wait counts exact: it does not order register loads against LDS DMA and
+//     would otherwise wait for the whole ring before using a register load.
 //     Operands of the first sub-step of step k+1 (codes, scales, X fragments)
 //     are fetched and dequantised under the last MFMAs of step k, so the
 //     matrix cores do not wait at step boundaries.

@@ -66,6 +66,14 @@ CONFIGS = {
 }
 
 
+def by_name(name: str) -> Workload:
+    """The configuration with the given name (e.g. "qwen3_32b_qproj")."""
+    for w in CONFIGS.values():
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
 def seed(cfg: int, role: int, prompt: int = 0) -> int:
     return SEED_BASE + 1000 * cfg + 10 * role + prompt
 
