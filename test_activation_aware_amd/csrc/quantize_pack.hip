@@ -26,7 +26,8 @@
 //     from LDS; groups of 64 / 128 channels meet through an LDS min/max
 //     exchange;
 //   * codes are placed in LDS in the tiled order and leave as one contiguous
-//     store of 2 steps x 32 rows x 2q words; scales and zeros likewise.
+//     store of 2 steps x 32 rows x 2q words; scales and zeros likewise (all
+//     with nontemporal stores, which measured about 5 % faster here).
 // v = w * sq is one v_fma_mix_f32 (fp16 operand, fp32 arithmetic) and the
 // codes are packed bytewise with v_cvt_pk_u8_f32.
 //
@@ -47,6 +48,7 @@ namespace ttq {
 
 namespace {
 
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 128;
 constexpr int kCols = 128;                   // channels per workgroup
 constexpr int kPR = kCols / 8;               // 16-byte pieces per slab row
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const int words = (width / 64) * 32 * SW;
     uint32_t* gdst = codes + ((int64_t)nt * (d_in / 64) + c0 / 64) * 32 * SW;
     for (int i = tid; i < words / 4; i += kThreads)
-      reinterpret_cast<uint4*>(gdst)[i] = reinterpret_cast<const uint4*>(outc)[i];
+      __builtin_nontemporal_store(reinterpret_cast<const u4v*>(outc)[i], reinterpret_cast<u4v*>(gdst) + i);
   }
   // scales / zeros: groups [c0/G, c0/G + width/G) of tile nt are contiguous;
   // 16-byte pieces, the first threads take the scales, the next the zeros
@@ -255,9 +257,9 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const int pieces = (width / G) * 32 / 8;
     const int64_t off = ((int64_t)nt * (d_in / G) + c0 / G) * 32;
     if (tid < pieces)
-      reinterpret_cast<uint4*>(scales + off)[tid] = reinterpret_cast<const uint4*>(outs)[tid];
+      __builtin_nontemporal_store(reinterpret_cast<const u4v*>(outs)[tid], reinterpret_cast<u4v*>(scales + off) + tid);
     else if (tid < 2 * pieces)
-      reinterpret_cast<uint4*>(zeros + off)[tid - pieces] = reinterpret_cast<const uint4*>(outz)[tid - pieces];
+      __builtin_nontemporal_store(reinterpret_cast<const u4v*>(outz)[tid - pieces], reinterpret_cast<u4v*>(zeros + off) + (tid - pieces));
   }
 }
 
