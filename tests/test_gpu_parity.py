@@ -154,6 +154,14 @@ def test_quantize_pack_edge_cases(q, g):
         vals[::g] = -1.5
         vals[1::g] = 6.0
         W[r] = vals
+    # zero-point ties: with D = 1, -min/s is a half-integer (q4: s = 0.5,
+    # -mn/s = 2.5; q2: s = 2.5, -mn/s = 0.5; q3: s = 0.5, -mn/s = 3.5)
+    lo, hi = (-1.75, 1.75) if q == 3 else (-1.25, 6.25)
+    for r in range(24, 40):
+        vals = rng.integers(int(lo * 4), int(hi * 4) + 1, size=d) * 0.25
+        vals[::g] = lo
+        vals[1::g] = hi
+        W[r] = vals
     W16 = W.astype(np.float16)
     D = np.exp(rng.standard_normal(d) * 2.0).astype(np.float32)
     D[:] = np.where(np.arange(d) % 3 == 0, 1.0, D)   # exact ones next to wide-range values
@@ -168,8 +176,8 @@ def test_quantize_ragged_rows():
     D = oracle.colstats(X[:256], alpha=0.75)
     _check_quant(W[:96], D, 4, 32, "rows96")
     _check_quant(W[:32], D, 3, 128, "rows32")
-    # channel counts that leave a partial 256-channel workgroup (64, 128, 192)
-    for d in (320, 384, 448):
+    # channel counts that leave a partial 128-channel workgroup (64 channels)
+    for d in (192, 320, 384, 448):
         _check_quant(np.ascontiguousarray(W[:64, :d]), D[:d], 4, 64 if d % 128 else 128, f"d{d}")
 
 
