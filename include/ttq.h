@@ -169,10 +169,13 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
  * quantisation.  Runs ttq_prescale (fused with ttq_lowrank_z when r > 0:
- * one read of X) into `workspace`, then ttq_wlowbit_gemm.  workspace: device
- * memory of at least ttq_linear_workspace_bytes(T, d_in, r) bytes, owned by
- * the caller; the handle itself is only read, so calls on one handle may run
- * concurrently on different streams when each has its own workspace. */
+ * one read of X) into `workspace`, then ttq_wlowbit_gemm; for T <= 4 with
+ * r = 0 a single kernel pre-scales the few input rows itself (the same
+ * arithmetic, bit-identical output) and `workspace` is not touched.
+ * workspace: device memory of at least ttq_linear_workspace_bytes(T, d_in, r)
+ * bytes, owned by the caller (required for every T >= 1); the handle itself
+ * is only read, so calls on one handle may run concurrently on different
+ * streams when each has its own workspace. */
 size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t r);
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
                       int64_t ldx, void* Y, int64_t ldy, void* workspace,

@@ -351,6 +351,13 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   if (workspace_bytes < linear_ws_bytes(T, c.d_in, c.r))
     return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, linear_ws_bytes(T, c.d_in, c.r));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c.r == 0 && T <= ttq::kFuseMaxT) {
+    // a few tokens: one kernel pre-scales the input itself (same results)
+    hipError_t e = ttq::launch_wlowbit_decode_raw(T, c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, ldx,
+                                                  h->buf.dinvsqrt, h->buf.codes, h->buf.scales, h->buf.zeros,
+                                                  Y, ldy, st);
+    return hip_status(e, "wlowbit_decode launch");
+  }
   void* xs = workspace;
   float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
   hipError_t e = ttq::launch_prescale_z(T, c.d_in, X, xdt == TTQ_F32, ldx, h->buf.dinvsqrt, xs,

@@ -34,6 +34,16 @@ hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, i
                                  const float* B, const float* Z, void* Y, bool y_f32, int64_t ldy,
                                  hipStream_t s);
 
+// The same for T <= kFuseMaxT and r = 0, straight from the raw input X
+// (fp16 or fp32, row stride ldx) and D^(-1/2): one launch, the pre-scaling
+// done inside; Y has X's dtype.  Bit-identical to launch_prescale_z followed
+// by launch_wlowbit_decode.
+constexpr int kFuseMaxT = 4;
+hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
+                                     int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
+                                     const void* scales, const void* zeros, void* Y, int64_t ldy,
+                                     hipStream_t s);
+
 // The projection; T <= kDecodeMaxT goes to the decode kernel.
 hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
                                int64_t ldxs, const uint32_t* codes, const void* scales,

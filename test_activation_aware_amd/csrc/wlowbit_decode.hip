@@ -12,16 +12,19 @@
 //     tiled code layout makes a step of a tile one contiguous 1 KB chunk
 //     (q = 4), so a wave's codes are one contiguous run, and its scales and
 //     zeros another.
-//   * A wave first requests its scales and zeros (16-byte loads, parked in
-//     LDS for per-step reads), then the codes of up to 16 steps at once
+//   * A wave first requests its scales and zeros (direct-to-LDS loads, read
+//     per step from LDS), then the codes of up to 16 steps at once
 //     (registers), and keeps the pre-scaled input of the next 2 - 4 steps in
-//     flight.  Per 16-channel sub-step: one v_mfma_f32_32x32x16_f16 per 32
+//     flight; requests are kept in order of use, since waiting for one load
+//     waits for every older one.  Per 16-channel sub-step: one v_mfma_f32_32x32x16_f16 per 32
 //     tokens, A = dequantised weights (the register dequantisation of the
 //     prefill kernel), B = the pre-scaled input (small; it stays in L2).
 //   * The 8 partial products meet in LDS in a fixed order (deterministic) and
 //     are stored as fp16 or fp32.
 //   * Rank-16 term: B16 x Z_hi + B16 x Z_lo (Z split into two fp16 parts)
 //     added to wave 0's accumulators.
+#include <type_traits>
+
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -38,6 +41,43 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRound = 16;  // steps whose codes a wave holds at once
 
+
+// 8 consecutive raw input values held in registers (fused input path)
+template <typename TX>
+struct XRaw {
+  h8 v;
+  __device__ __forceinline__ void load(const TX* p) { v = *reinterpret_cast<const h8*>(p); }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  }
+};
+template <>
+struct XRaw<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+template <>
+struct XRaw<void> {};
+
+// raw buffer resource over [base, base + bytes) (loads past the end read 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nrec = (int)min<int64_t>(bytes, (int64_t)0x7FFFFFF0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer into LDS; lane l lands at lds_wave_base + 16 l
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           voff, 0, 0, 0);
+}
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -107,18 +147,31 @@ __device__ __forceinline__ void store4(TY* p, const float* v) {
   }
 }
 
-// NF = token fragments of 32 (T <= 32 * NF)
-template <int Q, int G, typename TY, bool LOWRANK, int NF>
+// NF = token fragments of 32 (T <= 32 * NF).  TX = void: the input is the
+// pre-scaled Xs.  TX = _Float16 / float: the input is the raw X (row stride
+// ldx) and D^(-1/2); each wave pre-scales the rows it needs into LDS itself
+// (T <= kFuseMaxT, r = 0), with the prescale pass's arithmetic, so one launch
+// does the whole call.
+template <int Q, int G, typename TY, bool LOWRANK, int NF, typename TX>
 __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     int T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
-    const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
+    const TX* __restrict__ Xr, int64_t ldx, const float* __restrict__ dinv,
+    // (codes deliberately not __restrict__: loads from a restrict read-only
+    // pointer count as invariant, and the compiler then re-issues one next to
+    // its use instead of keeping the early request, which waits for all)
+    const uint32_t* codes, const _Float16* __restrict__ scales,
     const _Float16* __restrict__ zeros, const float* __restrict__ Bf, const float* __restrict__ Z,
     TY* __restrict__ Y, int64_t ldy) {
+  constexpr bool FUSED = !std::is_void<TX>::value;
+  static_assert(!FUSED || (NF == 1 && !LOWRANK), "the fused input path is for T <= kFuseMaxT, r = 0");
   constexpr int SW = 2 * Q;                     // code words per row per step
   constexpr int kXAhead = (NF == 1) ? 4 : 2;    // steps of input requested ahead of use
   // groups a round of kRound steps can touch, in 16-byte pieces of 8 halfs
   constexpr int kGroupPieces = ((kRound * 64 + 2 * G - 2) / G + 1 + 15) / 16 * 64;
-  __shared__ f16x part[kWaves][NF][64];
+  // per wave: the pre-scaled rows of a round (fused path), later the wave's
+  // partial products (NF x 64 lanes x 64 bytes)
+  constexpr int kWaveBuf = kFuseMaxT * kRound * 64 * 2 > NF * 64 * 64 ? kFuseMaxT * kRound * 64 * 2 : NF * 64 * 64;
+  __shared__ __attribute__((aligned(16))) char wbuf[kWaves][kWaveBuf];
   __shared__ __attribute__((aligned(16))) _Float16 sgrp[kWaves][2][kGroupPieces * 8];
 
   const int tid = threadIdx.x;
@@ -150,11 +203,20 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
   const _Float16* xrow[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) xrow[f] = Xs + (int64_t)min(32 * f + l32, T - 1) * ldxs + 8 * hh;
+  // fused path: pre-scaled row t of the round at xsl[t * kRound * 8 + 8 (k - k0) + piece]
+  h8* xsl = reinterpret_cast<h8*>(&wbuf[wave][0]);
+  const int tl = min(l32, T - 1);
+  int kcur0 = 0;  // first step of the current round (fused path)
   auto load_x = [&](int k, h8 (&xb)[4][NF]) {
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s) xb[s][0] = xsl[tl * kRound * 8 + 8 * (k - kcur0) + 2 * s + hh];
+    } else {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
+    }
   };
   _Float16* ssc = &sgrp[wave][0][0];
   _Float16* szr = &sgrp[wave][1][0];
@@ -167,32 +229,84 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     const int g0 = (k0 * 64) / G, g1 = ((k0 + nk - 1) * 64 + 63) / G;
     const int pieces = (g1 - g0 + 1) * 4;
     constexpr int SJ = kGroupPieces / 64;
-    uint4 sreg[SJ], zreg[SJ];
+    // Scales and zeros go straight to LDS (direct-to-LDS buffer loads, piece p
+    // of 16 bytes at slot p; slots past the round's pieces get copies of the
+    // last one).  Loads into registers would be moved by the compiler behind
+    // the codes, next to their use, and then waiting for them would wait for
+    // every code load too.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous round's LDS reads are done
+    {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stile + (int64_t)g0 * 32, (int64_t)pieces * 16);
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(ztile + (int64_t)g0 * 32, (int64_t)pieces * 16);
 #pragma unroll
-    for (int j = 0; j < SJ; ++j) {
-      const int p = min(64 * j + lane, pieces - 1);
-      sreg[j] = reinterpret_cast<const uint4*>(stile + (int64_t)g0 * 32)[p];
-      zreg[j] = reinterpret_cast<const uint4*>(ztile + (int64_t)g0 * 32)[p];
+      for (int j = 0; j < SJ; ++j) {
+        const int voff = min(64 * j + lane, pieces - 1) * 16;
+        lds_dma16(rs, voff, ssc + 64 * j * 8);
+        lds_dma16(rz, voff, szr + 64 * j * 8);
+      }
+    }
+    // the request order is the order of use (a wait for a load waits for every
+    // older one): keep the scheduler from interleaving the groups of loads
+    __builtin_amdgcn_sched_barrier(0);
+    // fused path: this round's channels of the T raw rows and of D^(-1/2)
+    // (lane takes the 8-channel pieces cp = lane, lane + 64), requested before
+    // the codes so that pre-scaling them waits for these loads only
+    constexpr int kPJ = kRound * 8 / 64;
+    XRaw<TX> xraw[FUSED ? kPJ : 1][FUSED ? kFuseMaxT : 1];
+    float4 dva[FUSED ? kPJ : 1], dvb[FUSED ? kPJ : 1];
+    if constexpr (FUSED) {
+      kcur0 = k0;
+#pragma unroll
+      for (int j = 0; j < kPJ; ++j) {  // clamped, unconditional loads (see the codes)
+        const int c = k0 * 64 + 8 * min(64 * j + lane, nk * 8 - 1);
+        dva[j] = *reinterpret_cast<const float4*>(dinv + c);
+        dvb[j] = *reinterpret_cast<const float4*>(dinv + c + 4);
+#pragma unroll
+        for (int t = 0; t < kFuseMaxT; ++t) xraw[j][t].load(Xr + (int64_t)min(t, T - 1) * ldx + c);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the pre-scaled input of the next kXAhead steps in flight (from L2,
+    // requested before the codes; on the fused path from LDS, once written)
+    h8 xr[kXAhead][4][NF];
+    if constexpr (!FUSED) {
+#pragma unroll
+      for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // codes of up to kRound steps in flight at once
     CodeStep cs[kRound];
 #pragma unroll
-    for (int i = 0; i < kRound; ++i) cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, ke - 1) * 32 * SW, hh);
-    // the pre-scaled input of the next kXAhead steps in flight (it comes from
-    // L2; one step of MFMAs is far shorter than an L2 round trip)
-    h8 xr[kXAhead][4][NF];
+    for (int i = 0; i < kRound; ++i)  // (unconditional: a load under a branch costs a full wait)
+      cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, ke - 1) * 32 * SW, hh);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FUSED) {
+      // pre-scale into the wave's LDS slice with the prescale pass's
+      // arithmetic: fp16(fp32(x) * D^(-1/2)), channel order 0 4 1 5 2 6 3 7
+      // (every slot of the slice is written, the unused ones with copies: a
+      // store under a branch would let the compiler sink the loads)
 #pragma unroll
-    for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
-    // scales and zeros land first: park them in LDS, where every lane finds
-    // its row's values
+      for (int j = 0; j < kPJ; ++j) {
+        const float dv[8] = {dva[j].x, dva[j].y, dva[j].z, dva[j].w, dvb[j].x, dvb[j].y, dvb[j].z, dvb[j].w};
 #pragma unroll
-    for (int j = 0; j < SJ; ++j) {
-      const int p = 64 * j + lane;
-      if (p < pieces) {
-        reinterpret_cast<uint4*>(ssc)[p] = sreg[j];
-        reinterpret_cast<uint4*>(szr)[p] = zreg[j];
+        for (int t = 0; t < kFuseMaxT; ++t) {
+          float x[8];
+          xraw[j][t].get(x);
+          h8 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[2 * e] = (_Float16)(x[e] * dv[e]);
+            o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+          }
+          xsl[t * kRound * 8 + 64 * j + lane] = o;
+        }
       }
     }
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
+    }
+
 #pragma unroll
     for (int i = 0; i < kRound; ++i) {
       const int k = k0 + i;
@@ -249,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
 
   // ---- the 8 waves' partial sums, added in wave order ----
 #pragma unroll
-  for (int f = 0; f < NF; ++f) part[wave][f][lane] = acc[f];
+  for (int f = 0; f < NF; ++f) reinterpret_cast<f16x*>(&wbuf[wave][0])[f * 64 + lane] = acc[f];
   __syncthreads();
   // wave w: fragment f = w / 4, the 4 consecutive accumulator values e4 = w % 4
   // (lane holds token 32 f + l32, channels 8 e4 + 4 hh + 0..3)
@@ -258,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const f16x p = part[w][f][lane];
+      const f16x p = reinterpret_cast<const f16x*>(&wbuf[w][0])[f * 64 + lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += p[4 * e4 + e];
     }
@@ -277,13 +391,54 @@ hipError_t launch_nf(int T, int d_in, int d_out, const void* Xs, int64_t ldxs, c
   const _Float16* sc = static_cast<const _Float16*>(scales);
   const _Float16* ze = static_cast<const _Float16*>(zeros);
   TY* y = static_cast<TY*>(Y);
+  const void* none = nullptr;
   if (T <= 32)
-    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 1>), grid, dim3(kThreads), 0, s, T, d_in, d_out, xs,
-                       ldxs, codes, sc, ze, B, Z, y, ldy);
+    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 1, void>), grid, dim3(kThreads), 0, s, T, d_in, d_out,
+                       xs, ldxs, none, (int64_t)0, (const float*)nullptr, codes, sc, ze, B, Z, y, ldy);
   else
-    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 2>), grid, dim3(kThreads), 0, s, T, d_in, d_out, xs,
-                       ldxs, codes, sc, ze, B, Z, y, ldy);
+    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 2, void>), grid, dim3(kThreads), 0, s, T, d_in, d_out,
+                       xs, ldxs, none, (int64_t)0, (const float*)nullptr, codes, sc, ze, B, Z, y, ldy);
   return hipGetLastError();
+}
+
+// raw input, r = 0, T <= kFuseMaxT: Y has the input's dtype
+template <int Q, typename TX>
+hipError_t launch_fused(int g, int T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
+                        const uint32_t* codes, const void* scales, const void* zeros, void* Y, int64_t ldy,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)(d_out / 32));
+  const _Float16* none = nullptr;
+  const TX* x = static_cast<const TX*>(X);
+  const _Float16* sc = static_cast<const _Float16*>(scales);
+  const _Float16* ze = static_cast<const _Float16*>(zeros);
+  TX* y = static_cast<TX*>(Y);
+  const float* nf = nullptr;
+  switch (g) {
+    case 32:
+      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 32, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
+                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
+      break;
+    case 64:
+      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 64, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
+                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
+      break;
+    default:
+      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 128, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
+                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <typename TX>
+hipError_t launch_fused_q(int q, int g, int T, int d_in, int d_out, const void* X, int64_t ldx,
+                          const float* dinv, const uint32_t* codes, const void* scales, const void* zeros,
+                          void* Y, int64_t ldy, hipStream_t s) {
+  switch (q) {
+    case 2: return launch_fused<2, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
+    case 3: return launch_fused<3, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
+    default: return launch_fused<4, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
+  }
 }
 
 template <int Q, int G, typename TY>
@@ -326,6 +481,16 @@ hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, i
   if (y_f32)
     return launch_q<float>(q, g, r, (int)T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   return launch_q<_Float16>(q, g, r, (int)T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+}
+
+hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
+                                     int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
+                                     const void* scales, const void* zeros, void* Y, int64_t ldy,
+                                     hipStream_t s) {
+  if (T <= 0 || T > kFuseMaxT) return hipErrorInvalidValue;
+  if (x_f32)
+    return launch_fused_q<float>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
+  return launch_fused_q<_Float16>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
 }
 
 }  // namespace ttq

@@ -376,6 +376,37 @@ def test_e2e_cfg5_prefill_and_decode(q):
     _e2e(5, q, 32, 0, sample_rows=rows, decode_T=(1, 16, 64))
 
 
+@pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (3, 4, 64), (3, 3, 128), (5, 2, 32), (5, 4, 32)])
+def test_linear_few_tokens_single_launch(cfg, q, g):
+    # ttq_linear with T <= 4 and r = 0 pre-scales inside the decode kernel: the
+    # output must equal ttq_prescale + ttq_wlowbit_gemm bit for bit (same
+    # arithmetic), for contiguous and strided input rows, and the oracle
+    # within the tolerance
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg, T=256)
+    say(f"few-token linear cfg={cfg} q={q} g={g}")
+    layer = ttq.TTQLinear(dev(W), q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=256)
+    layer.prepare(dev(X))
+    D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
+    c0, s0, z0 = oracle.quantize(W, D0, q, g)
+    d, d_out = W.shape[1], W.shape[0]
+    for Td in (1, 2, 3, 4):
+        Xn = wl.decode_inputs(cfg, Td, step=Td)
+        Xd = dev(Xn)
+        Y1 = layer.linear(Xd)
+        Xs = ttq.ttq_prescale(Xd, layer.dinvsqrt)
+        Y2 = ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out, out_dtype=Xd.dtype)
+        assert host(Y1).tobytes() == host(Y2).tobytes(), f"T={Td}: single launch differs from prescale + gemm"
+        Xp = torch.zeros((Td, d + 64), dtype=Xd.dtype, device=Xd.device)
+        Xp[:, :d] = Xd
+        Y3 = layer.linear(Xp[:, :d])
+        assert host(Y3).tobytes() == host(Y1).tobytes(), f"T={Td}: strided rows differ"
+        e = rel_fro(host(Y1), oracle.linear(Xn, c0, s0, z0, D0, g))
+        say(f"  T={Td} rel_fro={e:.3e}")
+        assert e <= Y_TOL
+    layer.close()
+
+
 def test_alpha_zero_gives_rtn_on_gpu():
     X, W = cfg_inputs(2, T=512)
     layer = ttq.TTQLinear(dev(W), q=3, g=32, alpha=0.0, lam=0.4, r=0, T_max=512)
