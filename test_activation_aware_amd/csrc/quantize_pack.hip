@@ -110,22 +110,25 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   const int width = min(kCols, d_in - c0);  // 64 or 128
   const int nt = blockIdx.y;                // row tile
 
-  // the slab: piece p -> row p / kPR, column 8 (p % kPR)
+  // D of this workgroup's channels, then the slab (piece p -> row p / kPR,
+  // column 8 (p % kPR)).  All loads are unconditional, with columns past the
+  // range clamped to its last piece (their LDS copies are never read): a load
+  // under a branch made the compiler wait for it before issuing the next one.
+  const float dj = D[c0 + min(tid, width - 1)];
   uint4 pre[kPieces];
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
     const int p = tid + i * kThreads;
-    const int row = p / kPR, col = (p % kPR) * 8;
-    pre[i] = col < width ? *reinterpret_cast<const uint4*>(W + (int64_t)(nt * 32 + row) * d_in + c0 + col)
-                         : make_uint4(0, 0, 0, 0);
+    const int row = p / kPR, col = min((p % kPR) * 8, width - 8);
+    pre[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(nt * 32 + row) * d_in + c0 + col);
   }
-  // sqrt(D) of this workgroup's channels, correctly rounded
-  if (tid < width) sq[tid] = sqrtf(D[c0 + tid]);
+  // sqrt(D), correctly rounded
+  sq[tid] = sqrtf(dj);
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
     const int p = tid + i * kThreads;
     const int row = p / kPR, col = (p % kPR) * 8;
-    if (col < width) *reinterpret_cast<uint4*>(&wt[row * kRowPitch + col]) = pre[i];
+    *reinterpret_cast<uint4*>(&wt[row * kRowPitch + col]) = pre[i];
   }
   __syncthreads();
 
