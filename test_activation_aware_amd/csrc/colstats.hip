@@ -98,11 +98,17 @@ __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict
                                                          float* __restrict__ dinvsqrt) {
   const int cx = threadIdx.x & 31, sl = threadIdx.x >> 5;
   const int64_t j = (int64_t)blockIdx.x * 32 + cx;
+  // all of this slice's chunk partials are requested at once (clamped,
+  // unconditional loads), then added in chunk order
+  constexpr int kPerSlice = kColstatsMaxChunks / 8;
+  const int64_t jc = j < d ? j : d - 1;
+  float v[kPerSlice];
+#pragma unroll
+  for (int i = 0; i < kPerSlice; ++i) v[i] = partial[(int64_t)min(sl + 8 * i, chunks - 1) * d + jc];
   double s = 0.0;
-  if (j < d) {
-#pragma unroll 4
-    for (int c = sl; c < chunks; c += 8) s += (double)partial[(int64_t)c * d + j];
-  }
+#pragma unroll
+  for (int i = 0; i < kPerSlice; ++i)
+    if (sl + 8 * i < chunks) s += (double)v[i];
   __shared__ double red[8][32];
   red[sl][cx] = s;
   __syncthreads();

@@ -50,73 +50,109 @@ __device__ __forceinline__ void load8(const TX* p, float v[8]) {
   }
 }
 
-template <typename TX, bool XS, bool ZZ>
+template <typename TX, bool XS, bool ZZ, int TG>
 __global__ __launch_bounds__(256) void prescale_z_kernel(int64_t T, int d, const TX* __restrict__ X,
                                                          int64_t ldx, const float* __restrict__ dinvsqrt,
                                                          _Float16* __restrict__ Xs,
                                                          const float* __restrict__ A,
                                                          float* __restrict__ Z) {
-  __shared__ f4 zred[4][64];
+  // TG groups of 16 tokens per workgroup: each slice of A (and of D^(-1/2))
+  // a wave loads serves TG groups, so A is read from L2 once per 16 TG tokens
+  __shared__ f4 zred[4][TG][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kb = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * kTok;
-  const int64_t t = t0 + row;
-  const int64_t tl = t < T ? t : T - 1;  // rows past T are read clamped and not stored
-  const TX* xr = X + tl * ldx + 8 * kb;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok * TG;
+  const TX* xr[TG];
+#pragma unroll
+  for (int g = 0; g < TG; ++g) {
+    const int64_t t = t0 + kTok * g + row;
+    xr[g] = X + (t < T ? t : T - 1) * ldx + 8 * kb;  // rows past T are read clamped and not stored
+  }
   const float* ar = A + (int64_t)row * d + 8 * kb;  // A^T column j = row of A
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  f4 acc[TG];
+#pragma unroll
+  for (int g = 0; g < TG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = d / kChunk;
 
-  for (int c = wave; c < nchunks; c += 4) {
-    const int k0 = c * kChunk;
-    float x[8];
-    load8<TX>(xr + k0, x);
+  // kU chunks per pass, all their loads requested before any is used (one
+  // memory round trip per pass instead of per chunk); chunks are still
+  // accumulated in order c = wave, wave + 4, ...
+  auto chunk = [&](int k0, const float (&x)[TG][8], const float (&dv)[8], const float (&a)[8]) {
     if constexpr (XS) {
-      const float4 da = *reinterpret_cast<const float4*>(dinvsqrt + k0 + 8 * kb);
-      const float4 db = *reinterpret_cast<const float4*>(dinvsqrt + k0 + 8 * kb + 4);
-      const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-      h8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = (_Float16)(x[e] * dv[e]);
-        o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+      for (int g = 0; g < TG; ++g) {
+        h8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] = (_Float16)(x[g][e] * dv[e]);
+          o[2 * e + 1] = (_Float16)(x[g][e + 4] * dv[e + 4]);
+        }
+        const int64_t t = t0 + kTok * g + row;
+        if (t < T) __builtin_nontemporal_store(o, reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb));
       }
-      if (t < T) __builtin_nontemporal_store(o, reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb));
     }
     if constexpr (ZZ) {
-      float a[8];
-      load8<float>(ar + k0, a);
       if constexpr (sizeof(TX) == 2) {
-        h8 xh, ahi, alo;
+        h8 ahi, alo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xh[e] = (_Float16)x[e];  // exact: x came from fp16
           ahi[e] = (_Float16)a[e];
           alo[e] = (_Float16)(a[e] - (float)ahi[e]);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ahi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, alo, acc, 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+          h8 xh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xh[e] = (_Float16)x[g][e];  // exact: x came from fp16
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ahi, acc[g], 0, 0, 0);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, alo, acc[g], 0, 0, 0);
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], a[e], acc, 0, 0, 0);
+        for (int g = 0; g < TG; ++g)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[g][e], a[e], acc[g], 0, 0, 0);
       }
     }
+  };
+  auto load_chunk = [&](int k0, float (&x)[TG][8], float (&dv)[8], float (&a)[8]) {
+#pragma unroll
+    for (int g = 0; g < TG; ++g) load8<TX>(xr[g] + k0, x[g]);
+    if constexpr (XS) load8<float>(dinvsqrt + k0 + 8 * kb, dv);
+    if constexpr (ZZ) load8<float>(ar + k0, a);
+  };
+  constexpr int kU = TG >= 4 ? 2 : 4;
+  int c = wave;
+  for (; c + 4 * (kU - 1) < nchunks; c += 4 * kU) {
+    float x[kU][TG][8], dv[kU][8], a[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load_chunk((c + 4 * u) * kChunk, x[u], dv[u], a[u]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) chunk((c + 4 * u) * kChunk, x[u], dv[u], a[u]);
+  }
+  for (; c < nchunks; c += 4) {
+    float x[TG][8], dv[8], a[8];
+    load_chunk(c * kChunk, x, dv, a);
+    chunk(c * kChunk, x, dv, a);
   }
 
   if constexpr (ZZ) {
-    // lane l holds Z[t0 + 4*(l/16) + i][l % 16], i = 0..3, for this wave's chunks
-    zred[wave][lane] = acc;
+    // lane l holds Z[t0 + 16 g + 4*(l/16) + i][l % 16], i = 0..3, for this
+    // wave's chunks; the 4 waves' partials are added in wave order
+#pragma unroll
+    for (int g = 0; g < TG; ++g) zred[wave][g][lane] = acc[g];
     __syncthreads();
-    if (wave == 0) {
-      f4 s = zred[0][lane];
+    if (wave < TG) {
+      const int g = wave;
+      f4 s = zred[0][g][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
-        const f4 v = zred[w][lane];
+        const f4 v = zred[w][g][lane];
         s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t tz = t0 + 4 * kb + i;
+        const int64_t tz = t0 + kTok * g + 4 * kb + i;
         if (tz < T) Z[tz * kRank + row] = s[i];
       }
     }
@@ -158,16 +194,27 @@ __global__ __launch_bounds__(256) void prescale_kernel(int64_t T, int d, const T
 template <typename TX>
 hipError_t launch_tx(int64_t T, int d, const void* X, int64_t ldx, const float* dinv, void* Xs,
                      const float* A, float* Z, hipStream_t s) {
-  const dim3 grid((unsigned)((T + kTok - 1) / kTok));
   const TX* x = static_cast<const TX*>(X);
   _Float16* xs = static_cast<_Float16*>(Xs);
-  if (Xs && Z)
-    hipLaunchKernelGGL((prescale_z_kernel<TX, true, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
-  else if (Xs)
+  if (Xs && !Z) {
     hipLaunchKernelGGL((prescale_kernel<TX>), dim3((unsigned)((T + kRows - 1) / kRows), (unsigned)((d / 8 + 255) / 256)),
                        dim3(256), 0, s, T, d, x, ldx, dinv, xs);
-  else
-    hipLaunchKernelGGL((prescale_z_kernel<TX, false, true>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+    return hipGetLastError();
+  }
+  // 64 tokens per workgroup while that still leaves a workgroup per CU, else 16
+  const bool wide = T >= 64 * 256;
+  const dim3 grid((unsigned)((T + kTok * (wide ? 4 : 1) - 1) / (kTok * (wide ? 4 : 1))));
+  if (Xs) {
+    if (wide)
+      hipLaunchKernelGGL((prescale_z_kernel<TX, true, true, 4>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+    else
+      hipLaunchKernelGGL((prescale_z_kernel<TX, true, true, 1>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((prescale_z_kernel<TX, false, true, 4>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+    else
+      hipLaunchKernelGGL((prescale_z_kernel<TX, false, true, 1>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+  }
   return hipGetLastError();
 }
 
