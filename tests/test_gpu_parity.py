@@ -407,6 +407,37 @@ def test_linear_few_tokens_single_launch(cfg, q, g):
     layer.close()
 
 
+def test_long_prompt_past_2gb():
+    # a 262144-token prompt (X 2.7 GB, Xs 2.7 GB, Y 4.3 GB: past the 2 GB a
+    # 32-bit offset reaches) built by repeating a 4096-token block 64 times;
+    # D of the repetition is D of the block (a mean), so the oracle's
+    # statistic, codes and projection come from the block alone
+    w = wl.CONFIGS[5]
+    reps, Tb = 64, 4096
+    X, W = cfg_inputs(5, T=Tb)
+    T = reps * Tb
+    say(f"long prompt T={T} (block of {Tb} x {reps})")
+    layer = ttq.TTQLinear(dev(W), q=4, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+    Xd = dev(X).repeat(reps, 1)
+    layer.prepare(Xd)
+    D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
+    Dg = host(layer.D)
+    assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+    c0, s0, z0 = oracle.quantize(W, Dg, 4, 32)          # codes given the GPU's own D: bit-exact
+    assert host(layer.codes).view(np.uint32).tobytes() == oracle.tile_codes(oracle.pack(c0, 4), 4).tobytes()
+    Y = layer.linear(Xd)
+    rows = np.array([0, 1, 4095, 4096, T // 2 + 7, T - 4097, T - 2, T - 1])
+    Yg = host(Y[torch.from_numpy(rows).to(Y.device)])
+    del Y, Xd
+    c1, s1, z1 = oracle.quantize(W, D0, 4, 32)
+    e = rel_fro(Yg, oracle.linear(X[rows % Tb], c1, s1, z1, D0, 32))
+    say(f"  sampled rows rel_fro={e:.3e}")
+    assert e <= Y_TOL
+    # repeated rows give identical outputs
+    assert np.array_equal(Yg[0], Yg[3]) and np.array_equal(Yg[2], Yg[5]) and np.array_equal(Yg[2], Yg[7])
+    layer.close()
+
+
 def test_alpha_zero_gives_rtn_on_gpu():
     X, W = cfg_inputs(2, T=512)
     layer = ttq.TTQLinear(dev(W), q=3, g=32, alpha=0.0, lam=0.4, r=0, T_max=512)
