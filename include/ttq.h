@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTQ_ABI_VERSION 1
+#define TTQ_ABI_VERSION 2
 
 typedef enum ttq_status {
   TTQ_OK = 0,
@@ -107,7 +107,7 @@ typedef struct ttq_sizes {
   size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2)                    */
   size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */
   size_t workspace_bytes; /* prepare: column-statistic partial sums      */
-  size_t linear_workspace_bytes; /* ttq_linear on T_max tokens            */
+  size_t linear_workspace_bytes; /* ttq_linear on any T <= T_max          */
 } ttq_sizes;
 
 /* Device buffers a handle works in (all caller-owned, see ttq_sizes).
@@ -169,14 +169,18 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
  * quantisation.  Runs ttq_prescale (fused with ttq_lowrank_z when r > 0:
- * one read of X) into `workspace`, then ttq_wlowbit_gemm; for T <= 4 with
- * r = 0 a single kernel pre-scales the few input rows itself (the same
- * arithmetic, bit-identical output) and `workspace` is not touched.
- * workspace: device memory of at least ttq_linear_workspace_bytes(T, d_in, r)
- * bytes, owned by the caller (required for every T >= 1); the handle itself
- * is only read, so calls on one handle may run concurrently on different
- * streams when each has its own workspace. */
-size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t r);
+ * one read of X) into `workspace`, then ttq_wlowbit_gemm.  With r = 0 and
+ * few tokens the input is pre-scaled inside the projection kernels (the same
+ * arithmetic): T <= 4, one kernel, `workspace` untouched; 4 < T <= 64, a
+ * split-K kernel whose 256-row workgroups share their input slice, fp32
+ * partial products in `workspace`, then a reduction in a fixed order (for
+ * d_in <= 5120 the output equals ttq_wlowbit_gemm's bit for bit).
+ * workspace: device memory of at least
+ * ttq_linear_workspace_bytes(T, d_in, d_out, r) bytes, owned by the caller
+ * (required for every T >= 1); the handle itself is only read, so calls on
+ * one handle may run concurrently on different streams when each has its own
+ * workspace. */
+size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_t r);
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
                       int64_t ldx, void* Y, int64_t ldy, void* workspace,
                       size_t workspace_bytes, void* stream);

@@ -88,8 +88,8 @@ def ttq_colstats_workspace_bytes(T: int, d: int) -> int:
     return load().ttq_colstats_workspace_bytes(T, d)
 
 
-def ttq_linear_workspace_bytes(T: int, d: int, r: int) -> int:
-    return load().ttq_linear_workspace_bytes(T, d, r)
+def ttq_linear_workspace_bytes(T: int, d: int, d_out: int, r: int) -> int:
+    return load().ttq_linear_workspace_bytes(T, d, d_out, r)
 
 
 def ttq_query_sizes(d_in, d_out, q, g, r, alpha, lam, p, T_max) -> dict:
@@ -295,7 +295,7 @@ class TTQLinear:
         if out.dtype != X.dtype or out.dim() != 2 or out.stride(1) != 1 or out.shape != (T, self.d_out):
             raise ValueError("out must be [T][d_out] with X's dtype and unit column stride")
         ldy = out.stride(0) if T > 1 else self.d_out
-        need = ttq_linear_workspace_bytes(T, self.d_in, self.r)
+        need = ttq_linear_workspace_bytes(T, self.d_in, self.d_out, self.r)
         if self.linear_workspace.numel() < need:
             self.linear_workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
         ws = self.linear_workspace

@@ -58,7 +58,7 @@ SIGNATURES = {
     "ttq_destroy": (None, [_P]),
     "ttq_set_weight": (ctypes.c_int, [_P, _P, _P]),
     "ttq_prepare": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P]),
-    "ttq_linear_workspace_bytes": (_S, [_I64, _I32, _I32]),
+    "ttq_linear_workspace_bytes": (_S, [_I64, _I32, _I32, _I32]),
     "ttq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, _S, _P]),
     "ttq_colstats_workspace_bytes": (_S, [_I64, _I64]),
     "ttq_colstats": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P, _S, _P]),
@@ -71,6 +71,9 @@ SIGNATURES = {
 }
 
 _lib = None
+
+
+ABI_VERSION = 2  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
 
 
 def load() -> ctypes.CDLL:
@@ -86,6 +89,9 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.ttq_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.ttq_abi_version()}, the binding expects "
+                               f"{ABI_VERSION}: rebuild the library")
         _lib = lib
     return _lib
 

@@ -5,6 +5,7 @@
 // exception crosses the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -105,10 +106,14 @@ size_t colstats_ws_bytes(int64_t T, int64_t d) {
   return (size_t)ttq::colstats_chunks(T < 1 ? 1 : T) * (size_t)d * sizeof(float);
 }
 
-// ttq_linear's workspace: Xs (fp16 [T][d_in]) then, for r > 0, Z (fp32 [T][r])
+// ttq_linear's workspace: Xs (fp16 [T][d_in]) then, for r > 0, Z (fp32 [T][r]);
+// for r = 0 and a few tokens (kFuseMaxT < T <= kDecodeMaxT) the split-K
+// partial products instead, when they are larger
 size_t xs_bytes(int64_t T, int64_t d) { return ((size_t)T * (size_t)d * 2 + 255) & ~(size_t)255; }
-size_t linear_ws_bytes(int64_t T, int64_t d, int32_t r) {
-  return xs_bytes(T, d) + (r > 0 ? (size_t)T * (size_t)r * 4 : 0);
+size_t linear_ws_bytes(int64_t T, int64_t d, int64_t d_out, int32_t r) {
+  size_t b = xs_bytes(T, d) + (r > 0 ? (size_t)T * (size_t)r * 4 : 0);
+  if (r == 0 && d >= 64 && d_out > 0) b = std::max(b, ttq::decode_splitk_ws_bytes(T, (int)d, (int)d_out));
+  return b;
 }
 
 ttq_status check_y(const void* Y, ttq_dtype ydt, int64_t T, int64_t d_out, int64_t ldy) {
@@ -158,7 +163,11 @@ ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out)
   out->dinvsqrt_bytes = din * 4;
   out->wres_bytes = cfg->r > 0 ? dout * din * 2 : 0;
   out->workspace_bytes = colstats_ws_bytes(T_max, cfg->d_in);
-  out->linear_workspace_bytes = linear_ws_bytes(T_max, cfg->d_in, cfg->r);
+  // the largest need over 1 <= T <= T_max: the prefill form grows with T, the
+  // split-K form with T up to kDecodeMaxT
+  out->linear_workspace_bytes =
+      std::max(linear_ws_bytes(T_max, cfg->d_in, cfg->d_out, cfg->r),
+               linear_ws_bytes(std::min<int64_t>(T_max, ttq::kDecodeMaxT), cfg->d_in, cfg->d_out, cfg->r));
   return ok();
 }
 
@@ -332,9 +341,9 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   return ok();
 }
 
-size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t r) {
-  if (T < 0 || d_in <= 0 || r < 0) return 0;
-  return linear_ws_bytes(T, d_in, r);
+size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_t r) {
+  if (T < 0 || d_in <= 0 || d_out < 0 || r < 0) return 0;
+  return linear_ws_bytes(T, d_in, d_out, r);
 }
 
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
@@ -348,8 +357,8 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   if (s != TTQ_OK) return s;
   if (T == 0) return ok();
   TTQ_NEED(workspace);
-  if (workspace_bytes < linear_ws_bytes(T, c.d_in, c.r))
-    return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, linear_ws_bytes(T, c.d_in, c.r));
+  const size_t need = linear_ws_bytes(T, c.d_in, c.d_out, c.r);
+  if (workspace_bytes < need) return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (c.r == 0 && T <= ttq::kFuseMaxT) {
     // a few tokens: one kernel pre-scales the input itself (same results)
@@ -357,6 +366,13 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
                                                   h->buf.dinvsqrt, h->buf.codes, h->buf.scales, h->buf.zeros,
                                                   Y, ldy, st);
     return hip_status(e, "wlowbit_decode launch");
+  }
+  if (c.r == 0 && T <= ttq::kDecodeMaxT) {
+    // up to 64 tokens: split-K over 256-row workgroups, partials in the workspace
+    hipError_t e = ttq::launch_wlowbit_decode_splitk(T, c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, ldx,
+                                                     h->buf.dinvsqrt, h->buf.codes, h->buf.scales,
+                                                     h->buf.zeros, Y, ldy, workspace, st);
+    return hip_status(e, "wlowbit_decode_splitk launch");
   }
   void* xs = workspace;
   float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;

@@ -44,6 +44,16 @@ hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int 
                                      const void* scales, const void* zeros, void* Y, int64_t ldy,
                                      hipStream_t s);
 
+// The same for kFuseMaxT < T <= kDecodeMaxT and r = 0 from the raw input:
+// split-K over 256-row workgroups that share one pre-scaled copy of their
+// input slice, fp32 partials in `workspace` (decode_splitk_ws_bytes), then a
+// reduction in split order.  Y has X's dtype.
+size_t decode_splitk_ws_bytes(int64_t T, int d_in, int d_out);
+hipError_t launch_wlowbit_decode_splitk(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
+                                        int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
+                                        const void* scales, const void* zeros, void* Y, int64_t ldy,
+                                        void* workspace, hipStream_t s);
+
 // The projection; T <= kDecodeMaxT goes to the decode kernel.
 hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
                                int64_t ldxs, const uint32_t* codes, const void* scales,

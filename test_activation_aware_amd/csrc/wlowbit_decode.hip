@@ -382,6 +382,190 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K form for kFuseMaxT < T <= kDecodeMaxT (r = 0, raw input).  With 32
+// rows per workgroup every workgroup re-reads the whole input, T x d_in x 2
+// bytes from L2 (168 MB per call at T = 64 on the Qwen3-32B shape, six times
+// the packed weight).  Here workgroup (row group, split) covers 8 tiles = 256
+// rows and one range of K: its 8 waves share one pre-scaled copy of that
+// input slice in LDS (the input is read once per 256 rows), each wave streams
+// its own tile's codes, and the split's fp32 partial products go to the
+// caller's workspace.  A second kernel adds the splits in split order.  The
+// splits are the K ranges of the 8-wave kernel's waves (for d_in <= 5120), so
+// the result equals that kernel's bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kSplitPerMax = 10;               // steps per split at most
+constexpr int kSplitPitch = kSplitPerMax * 64 + 8;  // fp16 per LDS input row (16-byte pad)
+
+__host__ __device__ inline int splitk_per(int ksteps) {
+  const int ks0 = max(kWaves, (ksteps + kSplitPerMax - 1) / kSplitPerMax);
+  return (ksteps + ks0 - 1) / ks0;
+}
+__host__ __device__ inline int splitk_count(int ksteps) {
+  const int per = splitk_per(ksteps);
+  return (ksteps + per - 1) / per;
+}
+
+template <int Q, int G, int NF, typename TX>
+__global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
+    int T, int d_in, int d_out, const TX* Xr, int64_t ldx, const float* dinv,
+    const uint32_t* codes,  // (input pointers not __restrict__: see wlowbit_decode_kernel)
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros, float* __restrict__ P) {
+  constexpr int SW = 2 * Q;
+  constexpr int kPieces = 128;  // scale / zero pieces of 16 bytes a split can touch, per wave
+  constexpr int kTokPerThread = (kDecodeMaxT + 5) / 6;  // >= 6 thread groups stage the input
+  __shared__ __attribute__((aligned(16))) _Float16 xsl[kDecodeMaxT * kSplitPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 sgrp[kWaves][2][kPieces * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int ksteps = d_in / 64, ng = d_in / G, ntiles = d_out / 32;
+  const int per = splitk_per(ksteps);
+  const int k0 = blockIdx.y * per, nk = min(per, ksteps - k0);  // nk >= 1
+  const bool tile_ok = (int)blockIdx.x * kWaves + wave < ntiles;
+  const int nt = min((int)blockIdx.x * kWaves + wave, ntiles - 1);  // waves past the end duplicate, never store
+
+  uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(mask), "+v"(magic));
+
+  // 1. the raw input slice and D^(-1/2), first: thread (tg, cp) takes the
+  //    8-channel piece cp of rows tg, tg + ngrp, ... (clamped, unconditional)
+  const int CP = nk * 8;
+  const int ngrp = kThreads / CP;
+  const int cp = tid % CP, tg = tid / CP;
+  const int c = (k0 + cp / 8) * 64 + 8 * (cp % 8);
+  const float4 da = *reinterpret_cast<const float4*>(dinv + c);
+  const float4 db = *reinterpret_cast<const float4*>(dinv + c + 4);
+  XRaw<TX> xraw[kTokPerThread];
+#pragma unroll
+  for (int j = 0; j < kTokPerThread; ++j) xraw[j].load(Xr + (int64_t)min(tg + ngrp * j, T - 1) * ldx + c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. this wave's scales and zeros (groups of its tile over the split),
+  //    direct to LDS
+  const int g0 = (k0 * 64) / G, g1 = ((k0 + nk) * 64 - 1) / G;
+  const int pieces = (g1 - g0 + 1) * 4;
+  _Float16* ssc = &sgrp[wave][0][0];
+  _Float16* szr = &sgrp[wave][1][0];
+  {
+    const _Float16* st = scales + ((int64_t)nt * ng + g0) * 32;
+    const _Float16* zt = zeros + ((int64_t)nt * ng + g0) * 32;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, (int64_t)pieces * 16);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zt, (int64_t)pieces * 16);
+#pragma unroll
+    for (int j = 0; j < kPieces / 64; ++j) {
+      const int voff = min(64 * j + lane, pieces - 1) * 16;
+      lds_dma16(rs, voff, ssc + 64 * j * 8);
+      lds_dma16(rz, voff, szr + 64 * j * 8);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the codes of the split's steps, all at once
+  const uint32_t* ctile = codes + (int64_t)nt * ksteps * 32 * SW + l32 * SW;
+  CodeStep cs[kSplitPerMax];
+#pragma unroll
+  for (int i = 0; i < kSplitPerMax; ++i) cs[i] = load_codes<Q>(ctile + (int64_t)(k0 + min(i, nk - 1)) * 32 * SW, hh);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. pre-scale the input slice into LDS (the prescale pass's arithmetic,
+  //    channel order 0 4 1 5 2 6 3 7); the wait is for the input loads only
+  {
+    const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+    for (int j = 0; j < kTokPerThread; ++j) {
+      const int t = tg + ngrp * j;
+      float x[8];
+      xraw[j].get(x);
+      h8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = (_Float16)(x[e] * dv[e]);
+        o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+      }
+      // every thread stores (rows past T and threads past the groups repeat
+      // a row that another thread also writes, with the same values): a
+      // store under a branch would pull the loads down behind the codes
+      *reinterpret_cast<h8*>(&xsl[min(t, T - 1) * kSplitPitch + 8 * cp]) = o;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // 5. per 16-channel sub-step: dequantised weights of this wave's tile times
+  //    the shared input rows
+  f16x acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
+  int xoff[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) xoff[f] = min(32 * f + l32, T - 1) * kSplitPitch + 8 * hh;
+#pragma unroll
+  for (int i = 0; i < kSplitPerMax; ++i) {
+    if (i < nk) {
+      const int k = k0 + i;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int grp = (k * 64 + 16 * s4) / G - g0;
+        const _Float16 sv = ssc[grp * 32 + l32];
+        const _Float16 nv = (_Float16)(-1024.0f) - szr[grp * 32 + l32];  // -(1024 + z), exact
+        const h2 sc = {sv, sv}, nz = {nv, nv};
+        uint32_t pr[4];
+        code_pairs<Q>(cs[i], s4, hh, mask, magic, pr);
+        h8 a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const h2 wv = (as_h2(pr[j]) + nz) * sc;
+          a[2 * j] = wv[0];
+          a[2 * j + 1] = wv[1];
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const h8 xb = *reinterpret_cast<const h8*>(&xsl[xoff[f] + i * 64 + 16 * s4]);
+          acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, xb, acc[f], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // 6. the split's partial products: P[split][t][n], fp32
+  if (tile_ok) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int t = 32 * f + l32;
+      if (t < T) {
+        float* pr = P + ((int64_t)blockIdx.y * T + t) * d_out + nt * 32 + 4 * hh;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          *reinterpret_cast<float4*>(pr + 8 * e4) =
+              make_float4(acc[f][4 * e4], acc[f][4 * e4 + 1], acc[f][4 * e4 + 2], acc[f][4 * e4 + 3]);
+      }
+    }
+  }
+}
+
+// Y[t][n] = sum of the splits' partials, in split order
+template <typename TY>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int T, int d_out, int KS, const float* __restrict__ P,
+                                                            TY* __restrict__ Y, int64_t ldy) {
+  const int n4s = d_out / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * n4s) return;
+  const int t = (int)(i / n4s), n4 = (int)(i % n4s);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < KS; ++s) {
+    const float4 p = reinterpret_cast<const float4*>(P + ((int64_t)s * T + t) * d_out)[n4];
+    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+  }
+  store4<TY>(Y + (int64_t)t * ldy + 4 * n4, v);
+}
+
 template <int Q, int G, typename TY, bool LR>
 hipError_t launch_nf(int T, int d_in, int d_out, const void* Xs, int64_t ldxs, const uint32_t* codes,
                      const void* scales, const void* zeros, const float* B, const float* Z, void* Y,
@@ -471,6 +655,47 @@ hipError_t launch_q(int q, int g, int r, int T, int d_in, int d_out, const void*
   }
 }
 
+
+template <int Q, int G, typename TX>
+hipError_t launch_splitk_g(int T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
+                           const uint32_t* codes, const void* scales, const void* zeros, void* Y, int64_t ldy,
+                           float* P, hipStream_t s) {
+  const int ksteps = d_in / 64;
+  const dim3 grid((unsigned)((d_out / 32 + kWaves - 1) / kWaves), (unsigned)splitk_count(ksteps));
+  const TX* x = static_cast<const TX*>(X);
+  const _Float16* sc = static_cast<const _Float16*>(scales);
+  const _Float16* ze = static_cast<const _Float16*>(zeros);
+  if (T <= 32)
+    hipLaunchKernelGGL((wlowbit_decode_splitk_kernel<Q, G, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in, d_out, x,
+                       ldx, dinv, codes, sc, ze, P);
+  else
+    hipLaunchKernelGGL((wlowbit_decode_splitk_kernel<Q, G, 2, TX>), grid, dim3(kThreads), 0, s, T, d_in, d_out, x,
+                       ldx, dinv, codes, sc, ze, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = (int64_t)T * (d_out / 4);
+  hipLaunchKernelGGL((splitk_reduce_kernel<TX>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, T, d_out,
+                     (int)grid.y, (const float*)P, static_cast<TX*>(Y), ldy);
+  return hipGetLastError();
+}
+
+template <typename TX>
+hipError_t launch_splitk(int q, int g, int T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
+                         const uint32_t* codes, const void* scales, const void* zeros, void* Y, int64_t ldy,
+                         float* P, hipStream_t s) {
+#define TTQ_SPLITK_G(QQ)                                                                                      \
+  switch (g) {                                                                                                \
+    case 32: return launch_splitk_g<QQ, 32, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
+    case 64: return launch_splitk_g<QQ, 64, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
+    default: return launch_splitk_g<QQ, 128, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
+  }
+  switch (q) {
+    case 2: TTQ_SPLITK_G(2)
+    case 3: TTQ_SPLITK_G(3)
+    default: TTQ_SPLITK_G(4)
+  }
+#undef TTQ_SPLITK_G
+}
 }  // namespace
 
 hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
@@ -491,6 +716,22 @@ hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int 
   if (x_f32)
     return launch_fused_q<float>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
   return launch_fused_q<_Float16>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
+}
+
+size_t decode_splitk_ws_bytes(int64_t T, int d_in, int d_out) {
+  if (T <= kFuseMaxT || T > kDecodeMaxT) return 0;
+  return (size_t)splitk_count(d_in / 64) * (size_t)T * (size_t)d_out * sizeof(float);
+}
+
+hipError_t launch_wlowbit_decode_splitk(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
+                                        int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
+                                        const void* scales, const void* zeros, void* Y, int64_t ldy,
+                                        void* workspace, hipStream_t s) {
+  if (T <= kFuseMaxT || T > kDecodeMaxT) return hipErrorInvalidValue;
+  float* P = static_cast<float*>(workspace);
+  if (x_f32)
+    return launch_splitk<float>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, P, s);
+  return launch_splitk<_Float16>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, P, s);
 }
 
 }  // namespace ttq

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.ttq_abi_version() == 1
+    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 2
     for s in range(7):
         assert lib.ttq_status_string(s).decode().startswith("TTQ_")
     assert lib.ttq_status_string(99) == b"unknown ttq_status"
@@ -56,7 +56,16 @@ def test_query_sizes_cfg5(lib):
     assert sz.d_bytes == sz.dinvsqrt_bytes == 5120 * 4
     assert sz.wres_bytes == 0
     assert sz.workspace_bytes == lib.ttq_colstats_workspace_bytes(16384, 5120) > 0
-    assert sz.linear_workspace_bytes == lib.ttq_linear_workspace_bytes(16384, 5120, 0) == 16384 * 5120 * 2
+    assert sz.linear_workspace_bytes == lib.ttq_linear_workspace_bytes(16384, 5120, 8192, 0) == 16384 * 5120 * 2
+    # a few tokens (4 < T <= 64, r = 0): fp32 partials of 8 K splits, when larger than the pre-scaled input
+    assert lib.ttq_linear_workspace_bytes(64, 5120, 8192, 0) == 8 * 64 * 8192 * 4
+    assert lib.ttq_linear_workspace_bytes(5, 5120, 8192, 0) == 8 * 5 * 8192 * 4
+    assert lib.ttq_linear_workspace_bytes(4, 5120, 8192, 0) == (4 * 5120 * 2 + 255) // 256 * 256
+    assert lib.ttq_linear_workspace_bytes(65, 5120, 8192, 0) == (65 * 5120 * 2 + 255) // 256 * 256
+    assert lib.ttq_linear_workspace_bytes(64, 5120, 8192, 16) == 64 * 5120 * 2 + 64 * 16 * 4
+    # T_max below 64: the split-K need at T_max
+    assert lib.ttq_query_sizes(ctypes.byref(_cfg()), 32, ctypes.byref(sz)) == 0
+    assert sz.linear_workspace_bytes == 8 * 32 * 8192 * 4
     assert lib.ttq_query_sizes(ctypes.byref(_cfg(r=16, q=2)), 100, ctypes.byref(sz)) == 0
     assert sz.wres_bytes == 8192 * 5120 * 2
     # pre-scaled input rounded up to 256 bytes, then Z

@@ -378,10 +378,11 @@ def test_e2e_cfg5_prefill_and_decode(q):
 
 @pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (3, 4, 64), (3, 3, 128), (5, 2, 32), (5, 4, 32)])
 def test_linear_few_tokens_single_launch(cfg, q, g):
-    # ttq_linear with T <= 4 and r = 0 pre-scales inside the decode kernel: the
-    # output must equal ttq_prescale + ttq_wlowbit_gemm bit for bit (same
-    # arithmetic), for contiguous and strided input rows, and the oracle
-    # within the tolerance
+    # ttq_linear with T <= 64 and r = 0 pre-scales inside its own kernels (one
+    # kernel for T <= 4, split-K + reduction above): the output must equal
+    # ttq_prescale + ttq_wlowbit_gemm bit for bit (same arithmetic, same K
+    # grouping for d_in <= 5120), for contiguous and strided input rows, and
+    # the oracle within the tolerance
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg, T=256)
     say(f"few-token linear cfg={cfg} q={q} g={g}")
@@ -390,7 +391,7 @@ def test_linear_few_tokens_single_launch(cfg, q, g):
     D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
     c0, s0, z0 = oracle.quantize(W, D0, q, g)
     d, d_out = W.shape[1], W.shape[0]
-    for Td in (1, 2, 3, 4):
+    for Td in (1, 2, 3, 4, 5, 16, 32, 33, 64):
         Xn = wl.decode_inputs(cfg, Td, step=Td)
         Xd = dev(Xn)
         Y1 = layer.linear(Xd)
