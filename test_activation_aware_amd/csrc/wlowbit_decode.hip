@@ -550,18 +550,28 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
   }
 }
 
-// Y[t][n] = sum of the splits' partials, in split order
+// Y[t][n] = sum of the splits' partials, in split order.  Up to 8 splits
+// (d_in <= 5120) all partials of a thread are requested at once.
 template <typename TY>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(int T, int d_out, int KS, const float* __restrict__ P,
-                                                            TY* __restrict__ Y, int64_t ldy) {
+__global__ __launch_bounds__(64) void splitk_reduce_kernel(int T, int d_out, int KS, const float* __restrict__ P,
+                                                           TY* __restrict__ Y, int64_t ldy) {
   const int n4s = d_out / 4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (i >= (int64_t)T * n4s) return;
   const int t = (int)(i / n4s), n4 = (int)(i % n4s);
+  const int64_t sstride = (int64_t)T * n4s;  // float4 between consecutive splits
+  const float4* p0 = reinterpret_cast<const float4*>(P) + (int64_t)t * n4s + n4;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < KS; ++s) {
-    const float4 p = reinterpret_cast<const float4*>(P + ((int64_t)s * T + t) * d_out)[n4];
-    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+  auto add = [&](const float4& p) { v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w; };
+  if (KS <= 8) {
+    float4 p[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) p[s] = p0[min(s, KS - 1) * sstride];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < KS) add(p[s]);
+  } else {
+    for (int s = 0; s < KS; ++s) add(p0[s * sstride]);
   }
   store4<TY>(Y + (int64_t)t * ldy + 4 * n4, v);
 }
@@ -674,7 +684,7 @@ hipError_t launch_splitk_g(int T, int d_in, int d_out, const void* X, int64_t ld
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n4 = (int64_t)T * (d_out / 4);
-  hipLaunchKernelGGL((splitk_reduce_kernel<TX>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, T, d_out,
+  hipLaunchKernelGGL((splitk_reduce_kernel<TX>), dim3((unsigned)((n4 + 63) / 64)), dim3(64), 0, s, T, d_out,
                      (int)grid.y, (const float*)P, static_cast<TX*>(Y), ldy);
   return hipGetLastError();
 }
