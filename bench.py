@@ -42,7 +42,7 @@ def parse():
                     help="untimed steps run for this long before the warmup steps, so that the GPU's "
                          "clock and power state is the steady one of continuous work")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels; "
+    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels,qkv; "
                     "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
                     "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
@@ -128,7 +128,7 @@ def main():
         print("bench.py: this implementation runs on one GPU only; the multi-GPU sharding of the path "
               "is described, not implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels"}
+    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels", "qkv"}
 
     import numpy as np
     import torch
@@ -225,6 +225,7 @@ def main():
         t_dense = time_loop(lambda: torch.nn.functional.linear(X, Wd), n_k, torch)
         kernels["dense_fp16_gemm_context"] = {"us": t_dense * 1e6, "TFLOPs": gm_flops / t_dense / 1e12}
         del Wd
+        result["projection_k_tok_s"] = T / t_gm_step / 1e3
         result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm_step / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
@@ -264,6 +265,37 @@ def main():
         layer16.close()
         del rng
 
+    # ---- q, k, v of one layer sharing one prepare (GQA: k, v have 1024 rows) ----
+    qkv = None
+    if "qkv" in only:
+        Wk = torch.from_numpy(wl.weight(w.cfg, 1024, d, w.w_sigma, part=1)).cuda()
+        Wv = torch.from_numpy(wl.weight(w.cfg, 1024, d, w.w_sigma, part=2)).cuda()
+        Wqkv = torch.cat([W, Wk, Wv]).contiguous()
+        kw = dict(q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+        fused = ttq.TTQLinear(Wqkv, **kw)
+        sep = [ttq.TTQLinear(Wi, **kw) for Wi in (W, Wk, Wv)]
+        Yqkv = torch.empty((T, Wqkv.shape[0]), dtype=torch.float16, device="cuda")
+        Ys = [torch.empty((T, Wi.shape[0]), dtype=torch.float16, device="cuda") for Wi in (W, Wk, Wv)]
+
+        def step_fused():
+            fused.prepare(X)
+            fused.linear(X, out=Yqkv)
+
+        def step_sep():
+            for layer_i, Yi in zip(sep, Ys):
+                layer_i.prepare(X)
+                layer_i.linear(X, out=Yi)
+        settle(step_fused, args.settle_ms / 2, torch)
+        t_f = time_loop(step_fused, args.steps, torch)
+        settle(step_sep, args.settle_ms / 2, torch)
+        t_s = time_loop(step_sep, args.steps, torch)
+        qkv = {"d_out": [d_out, 1024, 1024], "fused_k_tok_s": T / t_f / 1e3, "fused_ms": t_f * 1e3,
+               "separate_k_tok_s": T / t_s / 1e3, "separate_ms": t_s * 1e3}
+        fused.close()
+        for layer_i in sep:
+            layer_i.close()
+        del Wqkv, Yqkv, Ys, Wk, Wv
+
     # ---- decode: reuse the prefill quantisation for T = 1, 16, 64 ----
     decode = {}
     if "decode" in only:
@@ -280,6 +312,30 @@ def main():
             wbytes = q * d_out * d / 8 + 4 * d_out * d / g + 2 * Td * (d + d_out) + 4 * d
             decode[str(Td)] = {"k_tok_s": Td / td / 1e3, "us": td * 1e6, "us_eager": td_eager * 1e6,
                                "GBs": wbytes / td / 1e9, "frac_hbm": wbytes / td / 1e9 / HBM_PEAK_GBS}
+        # cold: 12 layers with their own packed weights (12 x 26 MB = 315 MB, more
+        # than the 256 MB Infinity Cache and the 8 x 4 MB L2) called in turn, so
+        # every call streams its weight from HBM; the calls above reuse one
+        # layer's 26 MB, which the Infinity Cache can hold
+        n_cold = 12
+        cold_layers = []
+        Xp = X[:64].contiguous()
+        for _ in range(n_cold):
+            lc = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=64)
+            lc.prepare(Xp)
+            cold_layers.append(lc)
+        for Td in w.decode_T:
+            Xn = torch.from_numpy(wl.decode_inputs(w.cfg, Td, step=Td)).cuda()
+            Yn = torch.empty((Td, d_out), dtype=torch.float16, device="cuda")
+
+            def calls():
+                for lc in cold_layers:
+                    lc.linear(Xn, out=Yn)
+            tc = time_graph(calls, 4, torch) / n_cold
+            wbytes = q * d_out * d / 8 + 4 * d_out * d / g + 2 * Td * (d + d_out) + 4 * d
+            decode[str(Td)].update({"us_cold": tc * 1e6, "frac_hbm_cold": wbytes / tc / 1e9 / HBM_PEAK_GBS})
+        for lc in cold_layers:
+            lc.close()
+        del cold_layers
 
     # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
@@ -288,9 +344,11 @@ def main():
         cores = len(os.sched_getaffinity(0))
         try:
             from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            pools = threadpool_info()
+            blas_threads = max([i.get("num_threads", 1) for i in pools] or [1])
+            blas_name = ",".join(sorted({str(i.get("internal_api", "?")) for i in pools})) or "?"
         except Exception:
-            blas_threads = cores
+            blas_threads, blas_name = cores, "?"
         log("bench: timing the CPU oracle")
         t0 = time.perf_counter()
         D0 = oracle.colstats(X_np, w.p, w.lam, w.alpha)
@@ -306,7 +364,7 @@ def main():
                "kind": "oracle",
                "sample": (f"one full step of the workload: prepare (colstats + quantize + pack) on the "
                           f"{T}-token prompt ({t_prep:.2f} s) and the fp64 projection of all {n_tok} tokens "
-                          f"({t_lin:.2f} s); numpy, {cores} cores visible")}
+                          f"({t_lin:.2f} s); numpy with {blas_name} ({blas_threads} threads), {cores} cores visible")}
 
     out = {
         "metric": "q_proj prefill k tokens/s (prepare+GEMM) at 4-bit r=0/16; % HBM/MFMA peak",
@@ -328,6 +386,7 @@ def main():
     }
     if "roofline" in result:
         out["roofline"] = result["roofline"]
+        out["projection_k_tok_s"] = result["projection_k_tok_s"]
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if r16 is not None:
@@ -336,6 +395,8 @@ def main():
         out["kernels"] = kernels
     if decode:
         out["decode"] = decode
+    if qkv is not None:
+        out["qkv_shared_prepare"] = qkv
     print(json.dumps(out), flush=True)
     layer.close()
 

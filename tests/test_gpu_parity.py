@@ -439,6 +439,34 @@ def test_long_prompt_past_2gb():
     layer.close()
 
 
+def test_qkv_shared_prepare():
+    # q, k and v projections of one input share D: one handle on the stacked
+    # weight [Wq; Wk; Wv] (GQA shapes: k, v have fewer rows) prepares once and
+    # must give exactly the three separate layers' codes and outputs (prefill,
+    # the single-launch and the split-K decode paths)
+    w = wl.CONFIGS[3]
+    d, T = w.d, 300
+    X, Wq = cfg_inputs(3, T=T)
+    Wk = wl.weight(3, 512, d, w.w_sigma, part=1)
+    Wv = wl.weight(3, 512, d, w.w_sigma, part=2)
+    Wqkv = np.concatenate([Wq, Wk, Wv])
+    kw = dict(q=4, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+    fused = ttq.TTQLinear(dev(Wqkv), **kw)
+    parts = [ttq.TTQLinear(dev(Wi), **kw) for Wi in (Wq, Wk, Wv)]
+    Xd = dev(X)
+    fused.prepare(Xd)
+    for layer in parts:
+        layer.prepare(Xd)
+    assert host(fused.codes).tobytes() == b"".join(host(layer.codes).tobytes() for layer in parts)
+    for Xi in (Xd, dev(wl.decode_inputs(3, 1, step=1)), dev(wl.decode_inputs(3, 16, step=16))):
+        Yf = host(fused.linear(Xi))
+        Ys = np.concatenate([host(layer.linear(Xi)) for layer in parts], axis=1)
+        assert Yf.tobytes() == Ys.tobytes(), f"T={Xi.shape[0]}"
+    fused.close()
+    for layer in parts:
+        layer.close()
+
+
 def test_alpha_zero_gives_rtn_on_gpu():
     X, W = cfg_inputs(2, T=512)
     layer = ttq.TTQLinear(dev(W), q=3, g=32, alpha=0.0, lam=0.4, r=0, T_max=512)

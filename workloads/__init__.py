@@ -115,14 +115,16 @@ def activations(cfg: int, T: int, d: int, dtype: str, n_outliers: int = 0,
 
 
 def weight(cfg: int, d_out: int, d: int, sigma: float, planted_rank: int = 0,
-           planted_rel_norm: float = 0.0) -> np.ndarray:
+           planted_rel_norm: float = 0.0, part: int = 0) -> np.ndarray:
     """W [d'][d] fp16 = N(0, sigma^2) (+ optional planted rank-k component).
+    `part` selects an independent weight of the same layer shape family
+    (0 = q_proj, 1 = k_proj, 2 = v_proj: the seed's prompt slot).
 
     The planted component is P = c * U V^T with U [d'][k], V [d][k] taken as
     the orthonormal Q factors of Gaussian matrices, and c chosen so that
     ||P||_F = planted_rel_norm * ||G||_F, G being the Gaussian part.  All
     its k singular values equal c."""
-    G = _rng(cfg, ROLE_W).standard_normal((d_out, d)) * sigma
+    G = _rng(cfg, ROLE_W, part).standard_normal((d_out, d)) * sigma
     planted_rank = min(planted_rank, d_out, d)   # tiny test shapes
     if planted_rank:
         rng = _rng(cfg, ROLE_PLANTED)
