@@ -44,7 +44,7 @@
  *   word w of block b of row n  ->  index ((nt * (d_in/64) + ks) * 32 + r) * 2q + pos
  *   nt = n / 32, r = n % 32, ks = b / 2, h = b % 2,
  *   pos = 4*(w % 2) + 2*h + w/2 for q = 4 (words b0w0 b0w2 b1w0 b1w2 b0w1
- *   b0w3 b1w1 b1w3), pos = q*h + w for q = 2, 3.
+ *   b0w3 b1w1 b1w3), pos = q*h + w for q = 2, 3, 5.
  * Scales and zeros (fp16, zeros exact integers 0..2^q-1), one per row n and
  * group gi of g channels, are stored at index (nt * (d_in/g) + gi) * 32 + r.
  * codes hold d_out * (d_in/32) * q uint32; scales and zeros d_out * (d_in/g)
@@ -65,7 +65,7 @@ extern "C" {
 typedef enum ttq_status {
   TTQ_OK = 0,
   TTQ_ERR_INVALID_ARG = 1, /* a scalar argument out of its documented range */
-  TTQ_ERR_UNSUPPORTED = 2, /* valid for the method, not built for the GPU (e.g. q=5) */
+  TTQ_ERR_UNSUPPORTED = 2, /* valid for the method, not built for the GPU (e.g. g=16) */
   TTQ_ERR_SHAPE = 3,       /* sizes inconsistent, or a buffer too small */
   TTQ_ERR_NULL = 4,        /* a required pointer is NULL */
   TTQ_ERR_ALIGN = 5,       /* a pointer or stride breaks the alignment rule */
@@ -81,7 +81,7 @@ typedef enum ttq_dtype {
  * (paper-daily.com section 2: alpha 0.5-0.75, lambda 0.4, p = 2).
  *   d_in  (d)  input channels,  multiple of 64 and of g
  *   d_out (d') output channels, multiple of 32
- *   q  bits per code: 2, 3 or 4 on the GPU
+ *   q  bits per code: 2, 3, 4 or 5
  *   g  group size along d_in: 32, 64 or 128
  *   r  low-rank rank: 0 or 16
  *   alpha >= 0, p > 0, lambda > 0 unless alpha == 0 (a dead channel would

@@ -297,6 +297,7 @@ hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W
   switch (q) {
     case 2: return launch_q<2>(d_out, d_in, g, w, D, codes, sc, ze, s);
     case 3: return launch_q<3>(d_out, d_in, g, w, D, codes, sc, ze, s);
+    case 5: return launch_q<5>(d_out, d_in, g, w, D, codes, sc, ze, s);
     default: return launch_q<4>(d_out, d_in, g, w, D, codes, sc, ze, s);
   }
 }

@@ -36,6 +36,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));  // 4 words at a word boundary
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -89,19 +90,29 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 }
 
 // one step's code words of this lane (see the prefill kernel): q = 4, this
-// lane half's 4 words; q = 2, the row's 4 words; q = 3, the row's 6 words
+// lane half's 4 words; q = 2, the row's 4 words; q = 3, the row's 6 words;
+// q = 5, words hh .. hh + 3 of each of the row's two 5-word blocks
+template <int Q>
 struct CodeStep {
   u4v a;
   u2v b;
 };
+template <>
+struct CodeStep<5> {
+  u4v a;
+  u4v b;
+};
 
 template <int Q>
-__device__ __forceinline__ CodeStep load_codes(const uint32_t* p, int hh) {
-  CodeStep c;
+__device__ __forceinline__ CodeStep<Q> load_codes(const uint32_t* p, int hh) {
+  CodeStep<Q> c;
   if constexpr (Q == 4) {
     c.a = *reinterpret_cast<const u4v*>(p + 4 * hh);
   } else if constexpr (Q == 2) {
     c.a = *reinterpret_cast<const u4v*>(p);
+  } else if constexpr (Q == 5) {
+    c.a = *reinterpret_cast<const u4a*>(p + hh);
+    c.b = *reinterpret_cast<const u4a*>(p + 5 + hh);
   } else {
     const u2v w01 = *reinterpret_cast<const u2v*>(p);
     const u2v w23 = *reinterpret_cast<const u2v*>(p + 2);
@@ -111,18 +122,40 @@ __device__ __forceinline__ CodeStep load_codes(const uint32_t* p, int hh) {
   return c;
 }
 
-__device__ __forceinline__ uint32_t code_word(const CodeStep& c, int i) { return i < 4 ? c.a[i] : c.b[i - 4]; }
+__device__ __forceinline__ uint32_t code_word(const CodeStep<3>& c, int i) { return i < 4 ? c.a[i] : c.b[i - 4]; }
 
 // fp16 pairs 1024 + c for sub-step s of the step, this lane half
 template <int Q>
-__device__ __forceinline__ void code_pairs(const CodeStep& c, int s, int hh, uint32_t mask, uint32_t magic,
+__device__ __forceinline__ void code_pairs(const CodeStep<Q>& c, int s, int hh, uint32_t mask, uint32_t magic,
                                            uint32_t out[4]) {
+  if constexpr (Q == 5) {
+    // the 8 codes start at bit 80 (s & 1) + 8 hh of the 4 words held for
+    // block s >> 1; lo / hi: codes 0-3 and 4-7 (20 bits each, from bit 0)
+    const u4v& v = (s >> 1) ? c.b : c.a;
+    const uint32_t o = 8u * (uint32_t)hh;
+    uint32_t lo, hi;
+    if ((s & 1) == 0) {
+      lo = __builtin_amdgcn_alignbit(v[1], v[0], o);
+      hi = __builtin_amdgcn_alignbit(v[1], v[0], o + 20u);
+    } else {
+      lo = __builtin_amdgcn_alignbit(v[3], v[2], o + 16u);
+      hi = v[3] >> (o + 4u);
+    }
+    // codes 0 | 4 at bit 0 and 1 | 5 at bit 5 of ua, 2 | 6 at bit 2 and 3 | 7 at bit 7 of ub
+    const uint32_t ua = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    const uint32_t ub = __builtin_amdgcn_perm(hi, lo, 0x06050201u);
+    out[0] = and_or(ua, mask, magic);
+    out[1] = and_or(ua >> 5, mask, magic);
+    out[2] = and_or(ub >> 2, mask, magic);
+    out[3] = and_or(ub >> 7, mask, magic);
+    return;
+  }
   uint32_t u;
   if constexpr (Q == 4) {
     u = c.a[s];
   } else if constexpr (Q == 2) {
     u = __builtin_amdgcn_perm(0u, c.a[s] >> (16 * hh), 0x0C010C00u);
-  } else {
+  } else if constexpr (Q == 3) {
     const int bit = 3 * (16 * (s & 1) + 8 * hh);
     const int w = bit >> 5, off = bit & 31;
     const uint32_t lo = code_word(c, 3 * (s >> 1) + w);
@@ -182,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
   const int ksteps = d_in / 64;
   const int ng = d_in / G;
 
-  uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);
+  uint32_t mask = ((1u << Q) - 1u) * 0x00010001u;  // code bits in both halves
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(mask), "+v"(magic));
 
@@ -275,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     // codes of up to kRound steps in flight at once
-    CodeStep cs[kRound];
+    CodeStep<Q> cs[kRound];
 #pragma unroll
     for (int i = 0; i < kRound; ++i)  // (unconditional: a load under a branch costs a full wait)
       cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, ke - 1) * 32 * SW, hh);
@@ -427,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
   const bool tile_ok = (int)blockIdx.x * kWaves + wave < ntiles;
   const int nt = min((int)blockIdx.x * kWaves + wave, ntiles - 1);  // waves past the end duplicate, never store
 
-  uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);
+  uint32_t mask = ((1u << Q) - 1u) * 0x00010001u;  // code bits in both halves
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(mask), "+v"(magic));
 
@@ -466,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
 
   // 3. the codes of the split's steps, all at once
   const uint32_t* ctile = codes + (int64_t)nt * ksteps * 32 * SW + l32 * SW;
-  CodeStep cs[kSplitPerMax];
+  CodeStep<Q> cs[kSplitPerMax];
 #pragma unroll
   for (int i = 0; i < kSplitPerMax; ++i) cs[i] = load_codes<Q>(ctile + (int64_t)(k0 + min(i, nk - 1)) * 32 * SW, hh);
   __builtin_amdgcn_sched_barrier(0);
@@ -631,6 +664,7 @@ hipError_t launch_fused_q(int q, int g, int T, int d_in, int d_out, const void* 
   switch (q) {
     case 2: return launch_fused<2, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
     case 3: return launch_fused<3, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
+    case 5: return launch_fused<5, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
     default: return launch_fused<4, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
   }
 }
@@ -661,6 +695,7 @@ hipError_t launch_q(int q, int g, int r, int T, int d_in, int d_out, const void*
   switch (q) {
     case 2: return launch_g<2, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     case 3: return launch_g<3, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 5: return launch_g<5, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     default: return launch_g<4, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   }
 }
@@ -702,6 +737,7 @@ hipError_t launch_splitk(int q, int g, int T, int d_in, int d_out, const void* X
   switch (q) {
     case 2: TTQ_SPLITK_G(2)
     case 3: TTQ_SPLITK_G(3)
+    case 5: TTQ_SPLITK_G(5)
     default: TTQ_SPLITK_G(4)
   }
 #undef TTQ_SPLITK_G

@@ -63,6 +63,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));  // 4 words at a word boundary
 
 constexpr int kThreads = 256;
 constexpr int BN = 256;  // output channels per workgroup
@@ -96,28 +97,59 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 
 // The code words one lane holds for one fragment and one step: q = 4, this
 // lane half's 4 words (one per sub-step); q = 2, the row's 4 words; q = 3, the
-// row's 6 words (words 4 and 5 in b).
+// row's 6 words (words 4 and 5 in b); q = 5, words hh .. hh + 3 of each of
+// the row's two 5-word blocks (a: first block, b: second).
+template <int Q>
 struct CodeFrag {
   u4v a;
   u2v b;
 };
+template <>
+struct CodeFrag<5> {
+  u4v a;
+  u4v b;
+};
 
-__device__ __forceinline__ uint32_t code_word(const CodeFrag& c, int i) {
+__device__ __forceinline__ uint32_t code_word(const CodeFrag<3>& c, int i) {
   return i < 4 ? c.a[i] : c.b[i - 4];
 }
 
 // The 4 code pairs (fp16 1024 + c in each half) a lane feeds to one MFMA of
 // sub-step S (16 channels), lane half hh.
 template <int Q, int S>
-__device__ __forceinline__ void code_pairs(const CodeFrag& c, int hh, uint32_t mask, uint32_t magic,
+__device__ __forceinline__ void code_pairs(const CodeFrag<Q>& c, int hh, uint32_t mask, uint32_t magic,
                                            uint32_t out[4]) {
+  if constexpr (Q == 5) {
+    // The lane half's 8 codes start at bit 80 (S & 1) + 40 hh of block S >> 1,
+    // i.e. at bit 80 (S & 1) + 8 hh of the 4 words held.  lo / hi: codes 0-3
+    // and 4-7 of the 8 (20 bits each, from bit 0).
+    const u4v& v = (S >> 1) ? c.b : c.a;
+    const uint32_t o = 8u * (uint32_t)hh;
+    uint32_t lo, hi;
+    if constexpr ((S & 1) == 0) {
+      lo = __builtin_amdgcn_alignbit(v[1], v[0], o);
+      hi = __builtin_amdgcn_alignbit(v[1], v[0], o + 20u);
+    } else {
+      lo = __builtin_amdgcn_alignbit(v[3], v[2], o + 16u);
+      hi = v[3] >> (o + 4u);
+    }
+    // bytes 0-1 of lo and hi side by side: codes 0 | 4 at bit 0, 1 | 5 at bit 5;
+    // bytes 1-2: codes 2 | 6 at bit 2, 3 | 7 at bit 7
+    const uint32_t ua = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    const uint32_t ub = __builtin_amdgcn_perm(hi, lo, 0x06050201u);
+    out[0] = and_or(ua, mask, magic);
+    out[1] = and_or(ua >> 5, mask, magic);
+    out[2] = and_or(ub >> 2, mask, magic);
+    out[3] = and_or(ub >> 7, mask, magic);
+    return;
+  }
   uint32_t u;
   if constexpr (Q == 4) {
     u = c.a[S];
   } else if constexpr (Q == 2) {
     // the 8 two-bit codes of this lane half; spread its two bytes 16 bits apart
     u = __builtin_amdgcn_perm(0u, c.a[S] >> (16 * hh), 0x0C010C00u);
-  } else {
+  } else if constexpr (Q == 3) {
     const int bit = 3 * (16 * (S & 1) + 8 * hh);  // 0, 24, 48, 72 within the block
     const int w = bit >> 5, off = bit & 31;
     const uint32_t lo = code_word(c, 3 * (S >> 1) + w);
@@ -225,7 +257,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   const int ng = d_in / G;
   const int ntile0 = n0 / 32, ntiles = d_out / 32;
 
-  uint32_t mask = (Q == 4) ? 0x000F000Fu : (Q == 3 ? 0x00070007u : 0x00030003u);  // code bits
+  uint32_t mask = ((1u << Q) - 1u) * 0x00010001u;  // code bits in both halves
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(mask), "+v"(magic));  // keep both in VGPRs for v_and_or_b32
   asm volatile("; accumulators in AGPRs" ::"a"(0.0f));
@@ -351,7 +383,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
         out[4 + i * GPK + gi] = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
       }
   };
-  auto dequant = [&](auto sc_, const CodeFrag& cf, const Scales& sv, int i) -> h8 {
+  auto dequant = [&](auto sc_, const CodeFrag<Q>& cf, const Scales& sv, int i) -> h8 {
     constexpr int S = decltype(sc_)::value;
     constexpr int gi = (G == 32) ? (S >> 1) : 0;
     uint32_t pr[4];
@@ -367,7 +399,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     }
     return a;
   };
-  auto read_codes = [&](const uint32_t* cs, CodeFrag* cf) {
+  auto read_codes = [&](const uint32_t* cs, CodeFrag<Q>* cf) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       const uint32_t* rowp = cs + ((wave * 2 + i) * 32 + l32) * SW;
@@ -375,6 +407,9 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
         cf[i].a = *reinterpret_cast<const u4v*>(rowp + 4 * hh);
       } else if constexpr (Q == 2) {
         cf[i].a = *reinterpret_cast<const u4v*>(rowp);
+      } else if constexpr (Q == 5) {
+        cf[i].a = *reinterpret_cast<const u4a*>(rowp + hh);
+        cf[i].b = *reinterpret_cast<const u4a*>(rowp + 5 + hh);
       } else {
         const u2v w01 = *reinterpret_cast<const u2v*>(rowp);
         const u2v w23 = *reinterpret_cast<const u2v*>(rowp + 2);
@@ -394,8 +429,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   // Codes: two register sets, step kt in set kt % 2, read from LDS together
   // with the scales one sub-step before the first dequantisation that needs
   // them.
-  CodeFrag cset0[FN], cset1[FN];
-  auto cset = [&](auto c) -> CodeFrag* {
+  CodeFrag<Q> cset0[FN], cset1[FN];
+  auto cset = [&](auto c) -> CodeFrag<Q>* {
     if constexpr (decltype(c)::value == 0) return cset0;
     else return cset1;
   };
@@ -421,8 +456,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     _Float16* xcur = xstage(ic<ST>{});
     _Float16* xnext = xstage(ic<N1>{});
     if (kt + 2 < ksteps) load_lds(kt + 2, xstage(ic<N2>{}), csstage(ic<N2>{}), szstage(ic<N2>{}));
-    const CodeFrag* ccur = cset(ic<CS>{});
-    CodeFrag* cnext = cset(ic<CS ^ 1>{});
+    const CodeFrag<Q>* ccur = cset(ic<CS>{});
+    CodeFrag<Q>* cnext = cset(ic<CS ^ 1>{});
     unroll<4>([&](auto sc_) {
       constexpr int S = decltype(sc_)::value;
       constexpr int P = S & 1, PN = P ^ 1;
@@ -555,6 +590,7 @@ hipError_t launch_q(int q, int g, int r, int64_t T, int d_in, int d_out, const v
   switch (q) {
     case 2: return launch_g<2, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     case 3: return launch_g<3, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 5: return launch_g<5, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     default: return launch_g<4, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
   }
 }

@@ -71,11 +71,15 @@ def test_query_sizes_cfg5(lib):
     # pre-scaled input rounded up to 256 bytes, then Z
     assert sz.linear_workspace_bytes == 100 * 5120 * 2 + 100 * 16 * 4
     assert sz.codes_bytes == 8192 * 160 * 2 * 4
+    # q = 5: five words per 32 codes
+    assert lib.ttq_query_sizes(ctypes.byref(_cfg(q=5)), 16, ctypes.byref(sz)) == 0
+    assert sz.codes_bytes == 8192 * 160 * 5 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=5), _capi.TTQ_ERR_UNSUPPORTED),
+    (dict(q=5), _capi.TTQ_OK),
     (dict(q=1), _capi.TTQ_ERR_INVALID_ARG),
+    (dict(q=6), _capi.TTQ_ERR_INVALID_ARG),
     (dict(q=8), _capi.TTQ_ERR_INVALID_ARG),
     (dict(g=16), _capi.TTQ_ERR_UNSUPPORTED),
     (dict(g=48), _capi.TTQ_ERR_INVALID_ARG),

@@ -122,7 +122,8 @@ def _check_quant(W16, D32, q, g, tag):
 
 
 @pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (2, 3, 32), (3, 4, 32), (3, 4, 64), (3, 4, 128),
-                                     (4, 4, 32), (5, 4, 32), (5, 2, 32)])
+                                     (4, 4, 32), (5, 4, 32), (5, 2, 32), (2, 5, 32), (3, 5, 64),
+                                     (4, 5, 128), (5, 5, 32)])
 def test_quantize_pack_bitexact(cfg, q, g):
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg)
@@ -133,7 +134,7 @@ def test_quantize_pack_bitexact(cfg, q, g):
     _check_quant(W, D, q, g, f"cfg{cfg}")
 
 
-@pytest.mark.parametrize("q", [2, 3, 4])
+@pytest.mark.parametrize("q", [2, 3, 4, 5])
 @pytest.mark.parametrize("g", [32, 64, 128])
 def test_quantize_pack_edge_cases(q, g):
     rng = np.random.default_rng(100 * q + g)
@@ -155,8 +156,9 @@ def test_quantize_pack_edge_cases(q, g):
         vals[1::g] = 6.0
         W[r] = vals
     # zero-point ties: with D = 1, -min/s is a half-integer (q4: s = 0.5,
-    # -mn/s = 2.5; q2: s = 2.5, -mn/s = 0.5; q3: s = 0.5, -mn/s = 3.5)
-    lo, hi = (-1.75, 1.75) if q == 3 else (-1.25, 6.25)
+    # -mn/s = 2.5; q2: s = 2.5, -mn/s = 0.5; q3: s = 0.5, -mn/s = 3.5;
+    # q5: s = 0.25, -mn/s = 2.5)
+    lo, hi = {3: (-1.75, 1.75), 5: (-0.625, 7.125)}.get(q, (-1.25, 6.25))
     for r in range(24, 40):
         vals = rng.integers(int(lo * 4), int(hi * 4) + 1, size=d) * 0.25
         vals[::g] = lo
@@ -283,6 +285,7 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0):
     (2, 2048, 3, 32, 16), (2, 1, 3, 32, 16), (2, 300, 3, 32, 0),
     (3, 1000, 4, 32, 0), (3, 1000, 4, 64, 0), (3, 1000, 4, 128, 0), (3, 257, 2, 64, 0), (3, 100, 3, 128, 16),
     (4, 777, 4, 32, 0), (4, 513, 4, 32, 16),
+    (1, 333, 5, 32, 0), (2, 2048, 5, 32, 16), (3, 1000, 5, 64, 0), (3, 257, 5, 128, 0), (4, 513, 5, 32, 16),
 ])
 def test_gemm_parity(cfg, T, q, g, r):
     _gemm_case(cfg, T, q, g, r)
@@ -292,9 +295,10 @@ def test_gemm_parity(cfg, T, q, g, r):
     (1, 1, 4, 32, 0), (1, 5, 4, 32, 0), (2, 2, 3, 32, 16), (2, 33, 3, 32, 16),
     (3, 7, 4, 64, 0), (3, 64, 4, 128, 0), (3, 31, 2, 32, 0), (4, 16, 4, 32, 16), (4, 63, 2, 64, 0),
     (5, 1, 4, 32, 0), (5, 64, 4, 32, 16),
+    (1, 3, 5, 32, 0), (2, 40, 5, 32, 16), (3, 17, 5, 64, 0), (4, 64, 5, 128, 0), (5, 1, 5, 32, 0),
 ])
 def test_decode_parity(cfg, T, q, g, r):
-    """T <= 64 takes the split-K decode kernel."""
+    """T <= 64 on the pre-scaled input takes the decode kernel."""
     _gemm_case(cfg, T, q, g, r)
 
 
@@ -303,7 +307,7 @@ def test_gemm_parity_strided_input():
     _gemm_case(3, 40, 4, 32, 0, pad_ld=64)
 
 
-@pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16)])
+@pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16), (5, 0)])
 def test_gemm_parity_full_cfg5_sampled(q, r):
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 16383],
                                      np.random.default_rng(3).integers(0, 16384, 59)]))
@@ -376,7 +380,13 @@ def test_e2e_cfg5_prefill_and_decode(q):
     _e2e(5, q, 32, 0, sample_rows=rows, decode_T=(1, 16, 64))
 
 
-@pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (3, 4, 64), (3, 3, 128), (5, 2, 32), (5, 4, 32)])
+@pytest.mark.parametrize("cfg,g,r", [(3, 32, 0), (2, 64, 16)])
+def test_e2e_q5(cfg, g, r):
+    _e2e(cfg, 5, g, r, T=2048, decode_T=(1, 16, 64))
+
+
+@pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (3, 4, 64), (3, 3, 128), (5, 2, 32), (5, 4, 32),
+                                     (1, 5, 64), (5, 5, 32)])
 def test_linear_few_tokens_single_launch(cfg, q, g):
     # ttq_linear with T <= 64 and r = 0 pre-scales inside its own kernels (one
     # kernel for T <= 4, split-K + reduction above): the output must equal

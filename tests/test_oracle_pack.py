@@ -57,7 +57,7 @@ def test_tiled_index_worked(golden_dir):
         assert int(np.argmax(oracle.tile_groups(v))) == c["index"]
 
 
-@pytest.mark.parametrize("q", [2, 3, 4])
+@pytest.mark.parametrize("q", [2, 3, 4, 5])
 def test_tiled_layout_is_a_bijection(q):
     d_out, d = 96, 320
     n, b, w = np.meshgrid(np.arange(d_out), np.arange(d // 32), np.arange(q), indexing="ij")
