@@ -168,29 +168,28 @@ def main():
     value = T * args.steps / elapsed / 1e3
 
     # ---- the GEMM's own duration inside the step ----
-    # The step again, composed of the two entry points ttq_linear is made of
-    # (ttq_prescale, then ttq_wlowbit_gemm on the same buffers and launch
-    # configuration), with HIP events on the launching stream around the
-    # GEMM: its average duration in the step's own power and cache state.
+    # The step again, composed of the entry points ttq_prepare and ttq_linear
+    # run (for fp16 input and T > 64 the projection is ttq_wlowbit_gemm_raw on
+    # the raw input, same buffers and launch configuration), with HIP events
+    # on the launching stream around the GEMM: its average duration in the
+    # step's own power and cache state.
     gemm_flops = 2.0 * T * d * d_out
     t_gm_step = None
     if "kernels" in only:
         s = torch.cuda.current_stream()
-        Xs_step = torch.empty((T, d), dtype=torch.float16, device="cuda")
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for e0, e1 in evs:
             layer.prepare(X)
-            ttq.ttq_prescale(X, layer.dinvsqrt, out=Xs_step)
             e0.record(s)
-            ttq.ttq_wlowbit_gemm(Xs_step, layer.codes, layer.scales, layer.zeros, q, g, d_out, out=Y)
+            ttq.ttq_wlowbit_gemm_raw(X, layer.dinvsqrt16, layer.codes, layer.scales, layer.zeros, q, g, d_out,
+                                     out=Y)
             e1.record(s)
         torch.cuda.synchronize()
         gm_launches = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
         t_gm_step = sum(gm_launches) / len(gm_launches)
         gm_pct = {f"us_p{k}": gm_launches[min(len(gm_launches) - 1, (len(gm_launches) * k) // 100)] * 1e6
                   for k in (10, 50, 90)}
-        del Xs_step
 
     # ---- per-kernel times, back to back (same inputs, same launch configuration) ----
     kernels = {}
@@ -202,8 +201,10 @@ def main():
         t_qp = time_graph(lambda: ttq.ttq_quantize_pack(W, D, q, g, layer.codes, layer.scales, layer.zeros), n_k, torch)
         Xs = ttq.ttq_prescale(X, R)
         t_ps = time_graph(lambda: ttq.ttq_prescale(X, R, out=Xs), n_k, torch)
-        t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out,
-                                                      out=Y), n_k, torch)
+        t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm_raw(X, layer.dinvsqrt16, layer.codes, layer.scales,
+                                                          layer.zeros, q, g, d_out, out=Y), n_k, torch)
+        t_gm_pre = time_loop(lambda: ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out,
+                                                          out=Y), n_k, torch)
         cs_bytes = T * d * 2 + 8 * d
         qp_bytes = 2 * d_out * d + 4 * d + q * d_out * d // 8 + 4 * d_out * d // g
         ps_bytes = 4 * T * d + 4 * d
@@ -213,10 +214,15 @@ def main():
                          "frac_hbm": cs_bytes / t_cs / 1e9 / HBM_PEAK_GBS},
             "quantize_pack": {"us": t_qp * 1e6, "GBs": qp_bytes / t_qp / 1e9,
                               "frac_hbm": qp_bytes / t_qp / 1e9 / HBM_PEAK_GBS},
+            # the raw-input GEMM of the step (back to back), and the pre-scaled
+            # pair it replaces for fp16 input (ttq_prescale + ttq_wlowbit_gemm,
+            # still the path for fp32 input)
+            "wlowbit_gemm_raw": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
+                                 "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
             "prescale": {"us": t_ps * 1e6, "GBs": ps_bytes / t_ps / 1e9,
                          "frac_hbm": ps_bytes / t_ps / 1e9 / HBM_PEAK_GBS},
-            "wlowbit_gemm": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
-                             "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
+            "wlowbit_gemm_prescaled": {"us": t_gm_pre * 1e6, "TFLOPs": gm_flops / t_gm_pre / 1e12,
+                                       "frac_mfma": gm_flops / t_gm_pre / 1e12 / MFMA_F16_PEAK_TFLOPS},
             "wlowbit_gemm_in_step": {"us": t_gm_step * 1e6, **gm_pct, "TFLOPs": gm_flops / t_gm_step / 1e12,
                                      "frac_mfma": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS},
         }
@@ -232,7 +238,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm_step / 1e12,
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm",
+                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm_raw",
                               "launch_us": t_gm_step * 1e6}
         log(f"bench: kernels {json.dumps(kernels)}")
 
@@ -356,7 +362,7 @@ def main():
         t0 = time.perf_counter()
         D0 = oracle.colstats(X_np, w.p, w.lam, w.alpha)
         c0, s0, z0 = oracle.quantize(W_np, D0, q, g)
-        oracle.pack(c0, q)
+        oracle.device_codes(c0, q)
         t_prep = time.perf_counter() - t0
         n_tok = T
         t0 = time.perf_counter()

@@ -38,7 +38,9 @@
  *
  * Packed code format (the pages fix none).  Codes: per output row, blocks
  * of 32 consecutive input channels; each block is q little-endian uint32
- * words forming one bitstream, code k of the block at bits [q*k, q*k+q).
+ * words forming one bitstream, slot k of the block at bits [q*k, q*k+q).
+ * Inside every 8 channels, slots 0..7 hold the codes of channels
+ * 0 2 4 6 1 3 5 7 (so slots j and j+4 hold the neighbours 2j and 2j+1).
  * The words are stored in a tiled order, so that one 64-channel step of 32
  * output rows is one contiguous chunk of 32 * 2q words:
  *   word w of block b of row n  ->  index ((nt * (d_in/64) + ks) * 32 + r) * 2q + pos
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTQ_ABI_VERSION 2
+#define TTQ_ABI_VERSION 3
 
 typedef enum ttq_status {
   TTQ_OK = 0,
@@ -104,7 +106,8 @@ typedef struct ttq_sizes {
   size_t scales_bytes;    /* fp16, d_out * (d_in/g), tiled order         */
   size_t zeros_bytes;     /* fp16, d_out * (d_in/g), tiled order         */
   size_t d_bytes;         /* fp32   [d_in]   D                           */
-  size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2)                    */
+  size_t dinvsqrt_bytes;  /* fp32   [d_in]   D^(-1/2), then its fp16     *
+                          * copy [d_in] (read by ttq_linear)            */
   size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */
   size_t workspace_bytes; /* prepare: column-statistic partial sums      */
   size_t linear_workspace_bytes; /* ttq_linear on any T <= T_max          */
@@ -218,10 +221,9 @@ ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_
                          int64_t ldx, const float* A, float* Z, void* stream);
 
 /* Xs = fp16(dinvsqrt * X): X device [T][ldx] (dtype xdt), dinvsqrt device
- * fp32 [d_in], Xs device fp16 [T][d_in] (dense rows).  Each product is taken
- * in fp32 and rounded to fp16.  Within every 8 consecutive channels Xs holds
- * them in the order 0 4 1 5 2 6 3 7 (the order in which ttq_wlowbit_gemm's
- * dequantisation pairs weights); d_in must be a multiple of 64. */
+ * fp32 [d_in], Xs device fp16 [T][d_in] (dense rows, the channel order of
+ * X).  Each product is taken in fp32 and rounded to fp16; d_in must be a
+ * multiple of 64. */
 ttq_status ttq_prescale(const void* X, ttq_dtype xdt, int64_t T, int32_t d_in, int64_t ldx,
                         const float* dinvsqrt, void* Xs, void* stream);
 
@@ -234,6 +236,20 @@ ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, i
                             int32_t r, const void* Xs, int64_t ldxs, const uint32_t* codes,
                             const void* scales, const void* zeros, const float* B,
                             const float* Z, void* Y, ttq_dtype ydt, int64_t ldy, void* stream);
+
+/* The same projection straight from the raw fp16 input, the form ttq_linear
+ * runs for fp16 X and T > 64: Y = (V_hat D^(-1/2)) X + B Z, D^(-1/2) applied
+ * to each dequantised weight pair (paper-daily.com section 2: the closed form
+ * Q[W D^(1/2)] D^(-1/2) X, here grouped as (Q[.] D^(-1/2)) X).
+ * X device fp16 [T][ldx] (ldx >= d_in, a multiple of 8); dinv16 device fp16
+ * [d_in], fp16(D^(-1/2)) (ttq_prepare writes it after the fp32 values in the
+ * handle's dinvsqrt buffer); Y device fp16 [T][ldy].  T must exceed 64
+ * (TTQ_ERR_SHAPE otherwise; fewer tokens go through ttq_linear).  Other
+ * arguments as for ttq_wlowbit_gemm. */
+ttq_status ttq_wlowbit_gemm_raw(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g,
+                                int32_t r, const void* X, int64_t ldx, const void* dinv16,
+                                const uint32_t* codes, const void* scales, const void* zeros,
+                                const float* B, const float* Z, void* Y, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

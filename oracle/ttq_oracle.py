@@ -34,6 +34,7 @@ __all__ = [
     "colstats", "colstats_f64", "svd_factors", "residual", "quantize", "pack",
     "unpack", "dequant", "linear", "linear_dense", "rtn_reference_levels",
     "tiled_code_index", "tile_codes", "untile_codes", "tile_groups", "untile_groups",
+    "SLOT_CODE8", "interleave8", "deinterleave8", "device_codes", "codes_from_device",
 ]
 
 
@@ -273,6 +274,47 @@ def untile_codes(flat, q: int, d_out: int, d: int) -> np.ndarray:
     flat = np.asarray(flat, dtype=np.uint32).reshape(-1)
     n, b, w = np.meshgrid(np.arange(d_out), np.arange(d // 32), np.arange(q), indexing="ij")
     return flat[tiled_code_index(n, b, w, q, d)]
+
+
+# ---------------------------------------------------------------------------
+# O4c  Order of the codes inside every 8 (the library's stored format)
+# ---------------------------------------------------------------------------
+# Before packing, the library reorders the codes of every 8 consecutive input
+# channels of a row so that stored slot m holds code SLOT_CODE8[m]: the even
+# channels first, then the odd ones.  A decoder that pairs slot j with slot
+# j + 4 (two codes per 32-bit register) then gets the channel pairs
+# (2j, 2j + 1), i.e. the natural channel order of the input.  The stored
+# words are tile_codes(pack(interleave8(codes))).
+
+SLOT_CODE8 = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def interleave8(codes) -> np.ndarray:
+    """[d'][d] codes -> the same codes in stored slot order (d % 8 == 0)."""
+    c = np.asarray(codes)
+    d_out, d = c.shape
+    if d % 8:
+        raise ValueError("d must be a multiple of 8")
+    return c.reshape(d_out, d // 8, 8)[:, :, list(SLOT_CODE8)].reshape(d_out, d)
+
+
+def deinterleave8(stored) -> np.ndarray:
+    """Inverse of interleave8."""
+    st = np.asarray(stored)
+    d_out, d = st.shape
+    out = np.empty_like(st).reshape(d_out, d // 8, 8)
+    out[:, :, list(SLOT_CODE8)] = st.reshape(d_out, d // 8, 8)
+    return out.reshape(d_out, d)
+
+
+def device_codes(codes, q: int) -> np.ndarray:
+    """The library's stored code words for [d'][d] codes (flat uint32)."""
+    return tile_codes(pack(interleave8(codes), q), q)
+
+
+def codes_from_device(flat, q: int, d_out: int, d: int) -> np.ndarray:
+    """Inverse of device_codes: flat stored words -> codes uint8 [d'][d]."""
+    return deinterleave8(unpack(untile_codes(flat, q, d_out, d), q, d))
 
 
 def tile_groups(vals) -> np.ndarray:

@@ -33,7 +33,8 @@ from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 
 __all__ = [
     "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
-    "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_query_sizes",
+    "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_wlowbit_gemm_raw",
+    "ttq_query_sizes",
     "ttq_colstats_workspace_bytes", "ttq_linear_workspace_bytes", "ttq_abi_version", "code_shape",
     "group_shape",
 ]
@@ -168,8 +169,7 @@ def ttq_lowrank_z(X, A, out=None):
 
 
 def ttq_prescale(X, dinvsqrt, out=None):
-    """Xs = fp16(D^(-1/2) X), [T][d] with the channels of every group of 8
-    stored in the order 0 4 1 5 2 6 3 7 (the low-bit GEMM's input)."""
+    """Xs = fp16(D^(-1/2) X), [T][d] (the pre-scaled input of ttq_wlowbit_gemm)."""
     torch = _torch()
     x, dt, T, ldx = _x_args(X)
     d = X.shape[1]
@@ -201,6 +201,30 @@ def ttq_wlowbit_gemm(Xs, codes, scales, zeros, q: int, g: int, d_out: int, B=Non
                                   _dev(codes, "codes", torch.int32), _dev(scales, "scales", torch.float16),
                                   _dev(zeros, "zeros", torch.float16), bp, zp,
                                   ctypes.c_void_p(out.data_ptr()), ydt, ldy, _stream()), "ttq_wlowbit_gemm")
+    return out
+
+
+def ttq_wlowbit_gemm_raw(X, dinv16, codes, scales, zeros, q: int, g: int, d_out: int, B=None, Z=None,
+                         out=None):
+    """Y = (V_hat D^(-1/2)) X + B Z from the raw fp16 input (T > 64), with
+    dinv16 the fp16 D^(-1/2) (TTQLinear.dinvsqrt16); Y is fp16."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    if dt != TTQ_F16:
+        raise TypeError("X must be float16 for the raw-input GEMM")
+    d_in = X.shape[1]
+    r = 0 if B is None else B.shape[1]
+    if out is None:
+        out = torch.empty((T, d_out), dtype=torch.float16, device=X.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.dtype != torch.float16:
+        raise ValueError("out must be 2-D fp16 with unit column stride")
+    ldy = out.stride(0) if T > 1 else d_out
+    bp = _dev(B, "B", torch.float32) if r else None
+    zp = _dev(Z, "Z", torch.float32) if r else None
+    check(load().ttq_wlowbit_gemm_raw(T, d_in, d_out, q, g, r, x, ldx, _dev(dinv16, "dinv16", torch.float16),
+                                      _dev(codes, "codes", torch.int32), _dev(scales, "scales", torch.float16),
+                                      _dev(zeros, "zeros", torch.float16), bp, zp,
+                                      ctypes.c_void_p(out.data_ptr()), ldy, _stream()), "ttq_wlowbit_gemm_raw")
     return out
 
 
@@ -256,7 +280,10 @@ class TTQLinear:
         self.scales = torch.empty(group_shape(self.d_out, self.d_in, g), dtype=torch.float16, device=dev)
         self.zeros = torch.empty(group_shape(self.d_out, self.d_in, g), dtype=torch.float16, device=dev)
         self.D = torch.empty(self.d_in, dtype=torch.float32, device=dev)
-        self.dinvsqrt = torch.empty(self.d_in, dtype=torch.float32, device=dev)
+        # D^(-1/2): fp32 [d_in], followed by its fp16 copy (sz.dinvsqrt_bytes = 6 d_in)
+        self._dinv_buf = torch.empty(sz.dinvsqrt_bytes, dtype=torch.uint8, device=dev)
+        self.dinvsqrt = self._dinv_buf[:4 * self.d_in].view(torch.float32)
+        self.dinvsqrt16 = self._dinv_buf[4 * self.d_in:6 * self.d_in].view(torch.float16)
         self.workspace = torch.empty(max(1, sz.workspace_bytes // 4), dtype=torch.float32, device=dev)
         if r > 0:
             if B is None or A is None:

@@ -68,12 +68,14 @@ SIGNATURES = {
     "ttq_prescale": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
     "ttq_wlowbit_gemm": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
                                         _P, _P, _P, ctypes.c_int, _I64, _P]),
+    "ttq_wlowbit_gemm_raw": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
+                                            _P, _P, _P, _P, _I64, _P]),
 }
 
 _lib = None
 
 
-ABI_VERSION = 2  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
+ABI_VERSION = 3  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
 
 
 def load() -> ctypes.CDLL:

@@ -27,6 +27,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// The fp16 copy of D^(-1/2) that follows the fp32 values in the dinvsqrt
+// buffer (4 d_in bytes in: 256-byte aligned, d_in being a multiple of 64).
+void* dinv16(const ttq_handle* h) { return reinterpret_cast<char*>(h->buf.dinvsqrt) + (size_t)h->cfg.d_in * 4; }
+
 ttq_status fail(ttq_status s, const char* fmt, ...) {
   char msg[512];
   va_list ap;
@@ -159,7 +163,7 @@ ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out)
   out->scales_bytes = dout * (din / (size_t)cfg->g) * 2;
   out->zeros_bytes = out->scales_bytes;
   out->d_bytes = din * 4;
-  out->dinvsqrt_bytes = din * 4;
+  out->dinvsqrt_bytes = din * 4 + din * 2;  // fp32, then the fp16 copy
   out->wres_bytes = cfg->r > 0 ? dout * din * 2 : 0;
   out->workspace_bytes = colstats_ws_bytes(T_max, cfg->d_in);
   // the largest need over 1 <= T <= T_max: the prefill form grows with T, the
@@ -232,7 +236,7 @@ ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int6
   TTQ_NEED(workspace);
   if (workspace_bytes < colstats_ws_bytes(T, d))
     return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, colstats_ws_bytes(T, d));
-  hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, d, ldx, p, lambda, alpha, D, dinvsqrt,
+  hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, d, ldx, p, lambda, alpha, D, dinvsqrt, nullptr,
                                       workspace, static_cast<hipStream_t>(stream));
   return hip_status(e, "colstats launch");
 }
@@ -320,6 +324,35 @@ ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, i
   return hip_status(e, "wlowbit_gemm launch");
 }
 
+ttq_status ttq_wlowbit_gemm_raw(int64_t T, int32_t d_in, int32_t d_out, int32_t q, int32_t g, int32_t r,
+                                const void* X, int64_t ldx, const void* dinv16, const uint32_t* codes,
+                                const void* scales, const void* zeros, const float* B, const float* Z, void* Y,
+                                int64_t ldy, void* stream) {
+  ttq_status s = check_qgr(q, g, r);
+  if (s != TTQ_OK) return s;
+  s = check_dims(d_in, d_out, g);
+  if (s != TTQ_OK) return s;
+  s = check_x(X, TTQ_F16, T, d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (ldx > (int64_t(1) << 22)) return fail(TTQ_ERR_SHAPE, "ldx=%lld too large", (long long)ldx);
+  if (T <= ttq::kDecodeMaxT)
+    return fail(TTQ_ERR_SHAPE, "T=%lld: the raw-input form is for T > %d (use ttq_linear)", (long long)T,
+                ttq::kDecodeMaxT);
+  s = check_y(Y, TTQ_F16, T, d_out, ldy);
+  if (s != TTQ_OK) return s;
+  TTQ_NEED(dinv16);
+  TTQ_NEED(codes);
+  TTQ_NEED(scales);
+  TTQ_NEED(zeros);
+  if (r > 0) {
+    TTQ_NEED(B);
+    TTQ_NEED(Z);
+  }
+  hipError_t e = ttq::launch_wlowbit_gemm_rawx(T, d_in, d_out, q, g, r, X, ldx, dinv16, codes, scales, zeros, B,
+                                               Z, Y, ldy, static_cast<hipStream_t>(stream));
+  return hip_status(e, "wlowbit_gemm launch");
+}
+
 ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
                        void* stream) {
   if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
@@ -331,7 +364,7 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   if (T > h->buf.T_max) return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld", (long long)T, (long long)h->buf.T_max);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.D,
-                                      h->buf.dinvsqrt, h->buf.workspace, st);
+                                      h->buf.dinvsqrt, dinv16(h), h->buf.workspace, st);
   if (e != hipSuccess) return hip_status(e, "colstats launch");
   e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes,
                                 h->buf.scales, h->buf.zeros, st);
@@ -375,6 +408,15 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   }
   void* xs = workspace;
   float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
+  if (xdt == TTQ_F16 && T > ttq::kDecodeMaxT) {
+    // fp16 input: the GEMM reads X itself, D^(-1/2) applied on the weight side
+    hipError_t e = hipSuccess;
+    if (c.r > 0) e = ttq::launch_prescale_z(T, c.d_in, X, false, ldx, h->buf.dinvsqrt, nullptr, h->buf.A, z, st);
+    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
+    e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
+                                      h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
+    return hip_status(e, "wlowbit_gemm launch");
+  }
   hipError_t e = ttq::launch_prescale_z(T, c.d_in, X, xdt == TTQ_F32, ldx, h->buf.dinvsqrt, xs,
                                         c.r > 0 ? h->buf.A : nullptr, z, st);
   if (e != hipSuccess) return hip_status(e, "prescale launch");

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void colstats_partial(const TX* __restric
 __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict__ partial, int chunks,
                                                          int64_t d, int64_t T, double lambda,
                                                          double alpha, float* __restrict__ D,
-                                                         float* __restrict__ dinvsqrt) {
+                                                         float* __restrict__ dinvsqrt,
+                                                         _Float16* __restrict__ dinv16) {
   const int cx = threadIdx.x & 31, sl = threadIdx.x >> 5;
   const int64_t j = (int64_t)blockIdx.x * 32 + cx;
   // all of this slice's chunk partials are requested at once (clamped,
@@ -119,12 +120,14 @@ __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict
   const double m = t / (double)T;
   const float dj = (float)pow(m + lambda, alpha);
   D[j] = dj;
-  dinvsqrt[j] = (float)(1.0 / sqrt((double)dj));
+  const float r = (float)(1.0 / sqrt((double)dj));
+  dinvsqrt[j] = r;
+  if (dinv16 != nullptr) dinv16[j] = (_Float16)r;  // fp16 copy, rounded to nearest even
 }
 
 template <typename TX>
 hipError_t launch_typed(const void* X, int64_t T, int64_t d, int64_t ldx, float p, float lambda,
-                        float alpha, float* D, float* dinvsqrt, float* partial, hipStream_t s) {
+                        float alpha, float* D, float* dinvsqrt, void* dinv16, float* partial, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(TX);
   const int chunks = colstats_chunks(T);
   const int64_t rows = (T + chunks - 1) / chunks;
@@ -139,7 +142,7 @@ hipError_t launch_typed(const void* X, int64_t T, int64_t d, int64_t ldx, float 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(colstats_finalize, dim3((unsigned)((d + 31) / 32)), dim3(256), 0, s, partial,
-                     chunks, d, T, (double)lambda, (double)alpha, D, dinvsqrt);
+                     chunks, d, T, (double)lambda, (double)alpha, D, dinvsqrt, static_cast<_Float16*>(dinv16));
   return hipGetLastError();
 }
 
@@ -154,10 +157,10 @@ int colstats_chunks(int64_t T) {
 }
 
 hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx, float p,
-                           float lambda, float alpha, float* D, float* dinvsqrt, float* partial,
+                           float lambda, float alpha, float* D, float* dinvsqrt, void* dinv16, float* partial,
                            hipStream_t s) {
-  if (x_f32) return launch_typed<float>(X, T, d, ldx, p, lambda, alpha, D, dinvsqrt, partial, s);
-  return launch_typed<_Float16>(X, T, d, ldx, p, lambda, alpha, D, dinvsqrt, partial, s);
+  if (x_f32) return launch_typed<float>(X, T, d, ldx, p, lambda, alpha, D, dinvsqrt, dinv16, partial, s);
+  return launch_typed<_Float16>(X, T, d, ldx, p, lambda, alpha, D, dinvsqrt, dinv16, partial, s);
 }
 
 }  // namespace ttq

@@ -6,10 +6,8 @@
 //   Xs = fp16(D^(-1/2) X)   the pre-scaled input the low-bit GEMM streams;
 //   Z  = X A^T              fp32 [T][16], the rank-16 input of the epilogue.
 //
-// One kernel does either or both: X is read from HBM once.  Xs is stored in
-// the channel order 0 4 1 5 2 6 3 7 within every 8 consecutive channels (the
-// order in which the GEMM's dequantisation produces weight pairs), rows of
-// d fp16 values.
+// One kernel does either or both: X is read from HBM once.  Xs keeps the
+// channel order of X, rows of d fp16 values.
 //
 // Xs is written with nontemporal stores: the GEMM reads it back from HBM
 // anyway (it is far larger than the caches), and streaming it past L2 keeps
@@ -84,8 +82,8 @@ __global__ __launch_bounds__(256) void prescale_z_kernel(int64_t T, int d, const
         h8 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[2 * e] = (_Float16)(x[g][e] * dv[e]);
-          o[2 * e + 1] = (_Float16)(x[g][e + 4] * dv[e + 4]);
+          o[2 * e] = (_Float16)(x[g][2 * e] * dv[2 * e]);
+          o[2 * e + 1] = (_Float16)(x[g][2 * e + 1] * dv[2 * e + 1]);
         }
         const int64_t t = t0 + kTok * g + row;
         if (t < T) __builtin_nontemporal_store(o, reinterpret_cast<h8*>(Xs + t * d + k0 + 8 * kb));
@@ -184,8 +182,8 @@ __global__ __launch_bounds__(256) void prescale_kernel(int64_t T, int d, const T
     h8 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (_Float16)(x[e] * dv[e]);
-      o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
+      o[2 * e] = (_Float16)(x[2 * e] * dv[2 * e]);
+      o[2 * e + 1] = (_Float16)(x[2 * e + 1] * dv[2 * e + 1]);
     }
     __builtin_nontemporal_store(o, reinterpret_cast<h8*>(yp + (int64_t)i * d));
   }

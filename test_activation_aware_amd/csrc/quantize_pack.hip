@@ -13,8 +13,9 @@
 //   z    = clamp(rint(-mn / s), 0, N)   round half to even
 //   c    = clamp(rint(v / s) + z, 0, N)
 //
-// Output is in the tiled storage order (32-row tiles, one contiguous chunk
-// per 64-channel step; see include/ttq.h).
+// Output is in the stored format of include/ttq.h: inside every 8 channels
+// the codes of channels 0 2 4 6 1 3 5 7, packed as a bitstream, words in the
+// tiled order (32-row tiles, one contiguous chunk per 64-channel step).
 //
 // Work split: a workgroup of 128 threads owns one 32-row tile of W over 128
 // input channels (4 blocks of 32), 10240 workgroups at the Qwen3-32B q_proj
@@ -81,6 +82,14 @@ __device__ __forceinline__ float mul_hi(uint32_t pair, float s) {
 // nearest even and saturates to [0, 255]: exact for integers in range)
 __device__ __forceinline__ uint32_t put_byte(float c, int i, uint32_t acc) {
   return __builtin_amdgcn_cvt_pk_u8_f32(c, (uint32_t)i, acc);
+}
+
+// Channel (within the 32-channel block) whose code goes to stored slot k:
+// inside every 8, slots 0-3 take the even channels and slots 4-7 the odd
+// ones, so that a decoder pairing slot j with slot j + 4 gets the two
+// neighbouring channels 2j and 2j + 1.
+__device__ __forceinline__ constexpr int slot_channel(int k) {
+  return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1);
 }
 
 // position of canonical word w of block-in-step h inside a row's 2q step words
@@ -189,8 +198,8 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     }
     const float rcp = __builtin_amdgcn_rcpf(s);
 
-    // code(k) gives an integer-valued float; packing into the canonical
-    // bitstream (code k at bit Q*k of the block's Q words)
+    // code(k) gives the integer-valued float stored in slot k; packing into
+    // the bitstream (slot k at bit Q*k of the block's Q words)
     uint32_t word[Q];
     auto pack = [&](auto&& code) {
       if constexpr (Q == 4) {
@@ -230,13 +239,13 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     };
     float far = 0.0f;  // largest distance of u from its rounded value
     pack([&](int k) {
-      const float u = __builtin_fmaf(v[k], rcp, zf);
+      const float u = __builtin_fmaf(v[slot_channel(k)], rcp, zf);
       const float c = rintf(u);
       far = fmaxf(far, fabsf(u - c));
       return c;
     });
     if (far > 0.5f - 0x1p-16f)  // rare: redo the block with the IEEE division
-      pack([&](int k) { return fminf(fmaxf(rintf(v[k] / s) + zf, 0.0f), N); });
+      pack([&](int k) { return fminf(fmaxf(rintf(v[slot_channel(k)] / s) + zf, 0.0f), N); });
     uint32_t* dst = &outc[(ksl * 32 + r) * SW];
 #pragma unroll
     for (int w = 0; w < Q; ++w) dst[step_pos<Q>(h, w)] = word[w];

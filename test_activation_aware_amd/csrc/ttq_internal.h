@@ -7,12 +7,13 @@
 
 namespace ttq {
 
-// Column statistic: partial sums then a fixed-order finalize.
+// Column statistic: partial sums then a fixed-order finalize.  dinv16 (may
+// be NULL): an fp16 copy of D^(-1/2).
 constexpr int kColstatsMaxChunks = 128;      // row chunks of the partial pass
 int colstats_chunks(int64_t T);              // chunks used for T tokens
 hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx,
                            float p, float lambda, float alpha, float* D, float* dinvsqrt,
-                           float* partial, hipStream_t s);
+                           void* dinv16, float* partial, hipStream_t s);
 
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W,
                                 const float* D, uint32_t* codes, void* scales, void* zeros,
@@ -59,5 +60,13 @@ hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int
                                int64_t ldxs, const uint32_t* codes, const void* scales,
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,
                                int64_t ldy, hipStream_t s);
+
+// The projection for T > kDecodeMaxT straight from the raw fp16 input X (row
+// stride ldx) with D^(-1/2) applied on the weight side: dinv16 is
+// fp16(D^(-1/2)) [d_in].  Y is fp16.
+hipError_t launch_wlowbit_gemm_rawx(int64_t T, int d_in, int d_out, int q, int g, int r, const void* X,
+                                    int64_t ldx, const void* dinv16, const uint32_t* codes, const void* scales,
+                                    const void* zeros, const float* B, const float* Z, void* Y, int64_t ldy,
+                                    hipStream_t s);
 
 }  // namespace ttq

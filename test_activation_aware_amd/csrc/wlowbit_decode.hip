@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FUSED) {
       // pre-scale into the wave's LDS slice with the prescale pass's
-      // arithmetic: fp16(fp32(x) * D^(-1/2)), channel order 0 4 1 5 2 6 3 7
+      // arithmetic: fp16(fp32(x) * D^(-1/2)), channel order kept
       // (every slot of the slice is written, the unused ones with copies: a
       // store under a branch would let the compiler sink the loads)
 #pragma unroll
@@ -327,10 +327,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
           xraw[j][t].get(x);
           h8 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[2 * e] = (_Float16)(x[e] * dv[e]);
-            o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
-          }
+          for (int e = 0; e < 8; ++e) o[e] = (_Float16)(x[e] * dv[e]);
           xsl[t * kRound * 8 + 64 * j + lane] = o;
         }
       }
@@ -505,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   // 4. pre-scale the input slice into LDS (the prescale pass's arithmetic,
-  //    channel order 0 4 1 5 2 6 3 7); the wait is for the input loads only
+  //    channel order kept); the wait is for the input loads only
   {
     const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
@@ -515,10 +512,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
       xraw[j].get(x);
       h8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = (_Float16)(x[e] * dv[e]);
-        o[2 * e + 1] = (_Float16)(x[e + 4] * dv[e + 4]);
-      }
+      for (int e = 0; e < 8; ++e) o[e] = (_Float16)(x[e] * dv[e]);
       // every thread stores (rows past T and threads past the groups repeat
       // a row that another thread also writes, with the same values): a
       // store under a branch would pull the loads down behind the codes

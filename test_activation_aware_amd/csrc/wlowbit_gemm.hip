@@ -38,9 +38,10 @@
 //     the exponent bits 0x6400 (v_and_or_b32, two codes per register);
 //     (1024 + c) - (1024 + z) = c - z exactly, times s gives the fp16 weight
 //     with one rounding (packed fp16 add and multiply).  The OR trick pairs
-//     code j with code j+4 of each 8-code group; the prescale pass stores Xs in
-//     the channel order 0 4 1 5 2 6 3 7 within every 8 channels to match (the
-//     MFMA only needs A and B to agree on the order of the reduction).
+//     stored slot j with slot j+4 of each 8-code group; the quantiser stores
+//     the codes of channels 0 2 4 6 1 3 5 7 in slots 0..7, so every pair is
+//     two neighbouring channels and the fragment comes out in the input's own
+//     channel order.
 //   * Rank-r term: before the K loop each fragment gets two extra MFMAs,
 //     B16 x Z_hi and B16 x Z_lo with Z = Z_hi + Z_lo split into two fp16
 //     parts, so the fp32 Z keeps about 22 bits.
@@ -213,10 +214,19 @@ __device__ __forceinline__ void block_barrier() {
 // FM 32-token fragments per wave: FM = 8 (256 tokens per workgroup, one
 // workgroup per CU, 256 accumulator registers per lane) for long prompts,
 // FM = 4 (128 tokens, two workgroups per CU) for short ones.
-template <int Q, int G, typename TY, bool LOWRANK, int FM>
+//
+// RAWX = false: Xs is the pre-scaled input D^(-1/2) X.  RAWX = true: Xs is
+// the raw fp16 input X, and D^(-1/2) is applied to the weight side of the
+// same product instead, V_hat D^(-1/2) (the pages' closed form
+// Q[W D^(1/2)] D^(-1/2) X can be grouped either way): dvh holds
+// fp16(D^(-1/2)) and each dequantised pair is multiplied by its two entries
+// (one packed multiply).  The weight side is the cheap side: a weight
+// fragment feeds FM MFMAs, an input fragment FN.
+template <int Q, int G, typename TY, bool LOWRANK, int FM, bool RAWX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(FM == 8 ? 1 : 2, FM == 8 ? 1 : 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
+                         const _Float16* __restrict__ dvh,
                          const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
                          const _Float16* __restrict__ zeros, const float* __restrict__ Bf,
                          const float* __restrict__ Z, TY* __restrict__ Y, int64_t ldy, int tiles_n,
@@ -237,6 +247,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * BK], xs1[BM * BK], xs2[BM * BK];
   __shared__ __attribute__((aligned(16))) uint32_t cs0[CW], cs1[CW], cs2[CW];
   __shared__ __attribute__((aligned(16))) _Float16 sz0[2 * SZ], sz1[2 * SZ], sz2[2 * SZ];
+  constexpr int DVN = RAWX ? BK : 8;  // fp16 D^(-1/2) of the step (RAWX)
+  __shared__ __attribute__((aligned(16))) _Float16 dv0[DVN], dv1[DVN], dv2[DVN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -327,6 +339,12 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     else if constexpr (S == 1) return sz1;
     else return sz2;
   };
+  auto dvstage = [&](auto st) -> _Float16* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return dv0;
+    else if constexpr (S == 1) return dv1;
+    else return dv2;
+  };
 
   // ---- requests for one step: X, codes, scales and zeros -> LDS ----
   // Only direct-to-LDS loads run inside the K loop, and one wait per step
@@ -355,8 +373,10 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   }
   // scales (wave 0) and zeros (wave 1): lane l < SLOTS moves 8 halfs
   const int soff = ((lane / (4 * GPK)) * ng * 32 + 8 * (lane % (4 * GPK))) * 2;
+  // RAWX: the step's 64 fp16 D^(-1/2) values, lanes 0-7 of wave 2
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(dvh, RAWX ? (int64_t)d_in * 2 : 0);
 
-  auto load_lds = [&](int kt, _Float16* xs, uint32_t* cs, _Float16* sz) {
+  auto load_lds = [&](int kt, _Float16* xs, uint32_t* cs, _Float16* sz, _Float16* dv) {
 #pragma unroll
     for (int j = 0; j < XSL / kThreads; ++j)
       lds_dma16(rs_x, xoff, kt * BK * 2 + j * xjstride, reinterpret_cast<char*>(xs) + 16 * (wave + 4 * j) * 64);
@@ -365,6 +385,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
       if ((wave + 4 * j) * 64 < CSL) lds_dma16(rs_c, coff[j], kt * 32 * SW * 4, cs + 4 * (wave + 4 * j) * 64);
     if (wave < 2 && lane < SLOTS)
       lds_dma16(wave == 0 ? rs_s : rs_z, soff, (kt * BK / G) * 32 * 2, sz + wave * SZ);
+    if constexpr (RAWX)
+      if (wave == 2 && lane < BK / 8) lds_dma16(rs_d, 16 * lane, kt * BK * 2, dv);
   };
 
   // ---- operands from LDS ----
@@ -383,7 +405,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
         out[4 + i * GPK + gi] = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
       }
   };
-  auto dequant = [&](auto sc_, const CodeFrag<Q>& cf, const Scales& sv, int i) -> h8 {
+  // dvp (RAWX): this lane's 8 fp16 D^(-1/2) values of the sub-step
+  auto dequant = [&](auto sc_, const CodeFrag<Q>& cf, const Scales& sv, int i, const h8& dvp) -> h8 {
     constexpr int S = decltype(sc_)::value;
     constexpr int gi = (G == 32) ? (S >> 1) : 0;
     uint32_t pr[4];
@@ -393,11 +416,16 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     h8 a;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const h2 wv = (as_h2(pr[j]) + nz) * sc;
+      h2 wv = (as_h2(pr[j]) + nz) * sc;  // channels 2j and 2j + 1
+      if constexpr (RAWX) wv = wv * h2{dvp[2 * j], dvp[2 * j + 1]};
       a[2 * j] = wv[0];
       a[2 * j + 1] = wv[1];
     }
     return a;
+  };
+  auto read_dv = [&](const _Float16* dv, int S) -> h8 {
+    if constexpr (RAWX) return *reinterpret_cast<const h8*>(&dv[16 * S + 8 * hh]);
+    else return h8{};
   };
   auto read_codes = [&](const uint32_t* cs, CodeFrag<Q>* cf) {
 #pragma unroll
@@ -438,14 +466,17 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   Scales szcur, sznext;
 
   // ---- prologue: steps 0 and 1 requested, step 0's first operands ready ----
-  load_lds(0, xs0, cs0, sz0);
-  if (ksteps > 1) load_lds(1, xs1, cs1, sz1);
+  load_lds(0, xs0, cs0, sz0, dv0);
+  if (ksteps > 1) load_lds(1, xs1, cs1, sz1, dv1);
   wait_vmem<0>();
   block_barrier();
   read_codes(cs0, cset0);
   read_scales(sz0, szcur);
+  {
+    const h8 dvp = read_dv(dv0, 0);
 #pragma unroll
-  for (int i = 0; i < FN; ++i) aop[0][i] = dequant(ic<0>{}, cset0[i], szcur, i);
+    for (int i = 0; i < FN; ++i) aop[0][i] = dequant(ic<0>{}, cset0[i], szcur, i, dvp);
+  }
 #pragma unroll
   for (int j = 0; j < FM; ++j) bop[0][j] = read_b(ic<0>{}, xs0, j);
 
@@ -455,7 +486,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     constexpr int N1 = (ST + 1) % 3, N2 = (ST + 2) % 3;
     _Float16* xcur = xstage(ic<ST>{});
     _Float16* xnext = xstage(ic<N1>{});
-    if (kt + 2 < ksteps) load_lds(kt + 2, xstage(ic<N2>{}), csstage(ic<N2>{}), szstage(ic<N2>{}));
+    if (kt + 2 < ksteps)
+      load_lds(kt + 2, xstage(ic<N2>{}), csstage(ic<N2>{}), szstage(ic<N2>{}), dvstage(ic<N2>{}));
     const CodeFrag<Q>* ccur = cset(ic<CS>{});
     CodeFrag<Q>* cnext = cset(ic<CS ^ 1>{});
     unroll<4>([&](auto sc_) {
@@ -472,13 +504,15 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
           read_codes(csstage(ic<N1>{}), cnext);
           read_scales(szstage(ic<N1>{}), sznext);
         }
+        const h8 dvp = read_dv(dvstage(ic<ST>{}), S + 1);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<S + 1>{}, ccur[i], szcur, i);
+        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<S + 1>{}, ccur[i], szcur, i, dvp);
       } else {
 #pragma unroll
         for (int j = 0; j < FM; ++j) bop[PN][j] = read_b(ic<0>{}, xnext, j);
+        const h8 dvp = read_dv(dvstage(ic<N1>{}), 0);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<0>{}, cnext[i], sznext, i);
+        for (int i = 0; i < FN; ++i) aop[PN][i] = dequant(ic<0>{}, cnext[i], sznext, i, dvp);
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -538,60 +572,66 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   }
 }
 
-template <int Q, int G, typename TY, bool LR, int FM>
-hipError_t launch_fm(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                     const uint32_t* codes, const void* scales, const void* zeros,
-                     const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+// The launch arguments shared by every instance
+struct GemmArgs {
+  int64_t T;
+  int d_in, d_out;
+  const void* X;  // Xs (pre-scaled) or the raw fp16 input
+  int64_t ldx;
+  const void* dvh;  // fp16 D^(-1/2) (raw input only)
+  const uint32_t* codes;
+  const void* scales;
+  const void* zeros;
+  const float* B;
+  const float* Z;
+  void* Y;
+  int64_t ldy;
+};
+
+template <int Q, int G, typename TY, bool LR, int FM, bool RAWX>
+hipError_t launch_fm(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = 32 * FM;
-  const int tiles_n = (d_out + BN - 1) / BN;
-  const int64_t tiles_m = (T + BM - 1) / BM;
+  const int tiles_n = (a.d_out + BN - 1) / BN;
+  const int64_t tiles_m = (a.T + BM - 1) / BM;
   const int64_t tiles = tiles_n * tiles_m;
-  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR, FM>), dim3((unsigned)tiles), dim3(kThreads), 0, s, T,
-                     d_in, d_out, static_cast<const _Float16*>(Xs), ldxs, codes,
-                     static_cast<const _Float16*>(scales), static_cast<const _Float16*>(zeros), B, Z,
-                     static_cast<TY*>(Y), ldy, tiles_n, (int)tiles);
+  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR, FM, RAWX>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
+                     a.T, a.d_in, a.d_out, static_cast<const _Float16*>(a.X), a.ldx,
+                     static_cast<const _Float16*>(a.dvh), a.codes, static_cast<const _Float16*>(a.scales),
+                     static_cast<const _Float16*>(a.zeros), a.B, a.Z, static_cast<TY*>(a.Y), a.ldy, tiles_n,
+                     (int)tiles);
   return hipGetLastError();
 }
 
 // 256-token tiles once there are enough of them to give every CU a few
-template <int Q, int G, typename TY, bool LR>
-hipError_t launch_cfg(int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                      const uint32_t* codes, const void* scales, const void* zeros,
-                      const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
-  const int64_t tiles8 = ((d_out + BN - 1) / BN) * ((T + 255) / 256);
-  if (tiles8 >= 1024)
-    return launch_fm<Q, G, TY, LR, 8>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-  return launch_fm<Q, G, TY, LR, 4>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+template <int Q, int G, typename TY, bool LR, bool RAWX>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles8 = ((a.d_out + BN - 1) / BN) * ((a.T + 255) / 256);
+  if (tiles8 >= 1024) return launch_fm<Q, G, TY, LR, 8, RAWX>(a, s);
+  return launch_fm<Q, G, TY, LR, 4, RAWX>(a, s);
 }
 
-template <int Q, int G, typename TY>
-hipError_t launch_lr(int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                     const uint32_t* codes, const void* scales, const void* zeros, const float* B,
-                     const float* Z, void* Y, int64_t ldy, hipStream_t s) {
-  if (r > 0) return launch_cfg<Q, G, TY, true>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-  return launch_cfg<Q, G, TY, false>(T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+template <int Q, int G, typename TY, bool RAWX>
+hipError_t launch_lr(int r, const GemmArgs& a, hipStream_t s) {
+  if (r > 0) return launch_cfg<Q, G, TY, true, RAWX>(a, s);
+  return launch_cfg<Q, G, TY, false, RAWX>(a, s);
 }
 
-template <int Q, typename TY>
-hipError_t launch_g(int g, int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                    const uint32_t* codes, const void* scales, const void* zeros, const float* B,
-                    const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+template <int Q, typename TY, bool RAWX>
+hipError_t launch_g(int g, int r, const GemmArgs& a, hipStream_t s) {
   switch (g) {
-    case 32: return launch_lr<Q, 32, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-    case 64: return launch_lr<Q, 64, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-    default: return launch_lr<Q, 128, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 32: return launch_lr<Q, 32, TY, RAWX>(r, a, s);
+    case 64: return launch_lr<Q, 64, TY, RAWX>(r, a, s);
+    default: return launch_lr<Q, 128, TY, RAWX>(r, a, s);
   }
 }
 
-template <typename TY>
-hipError_t launch_q(int q, int g, int r, int64_t T, int d_in, int d_out, const void* Xs, int64_t ldxs,
-                    const uint32_t* codes, const void* scales, const void* zeros, const float* B,
-                    const float* Z, void* Y, int64_t ldy, hipStream_t s) {
+template <typename TY, bool RAWX>
+hipError_t launch_q(int q, int g, int r, const GemmArgs& a, hipStream_t s) {
   switch (q) {
-    case 2: return launch_g<2, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-    case 3: return launch_g<3, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-    case 5: return launch_g<5, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-    default: return launch_g<4, TY>(g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+    case 2: return launch_g<2, TY, RAWX>(g, r, a, s);
+    case 3: return launch_g<3, TY, RAWX>(g, r, a, s);
+    case 5: return launch_g<5, TY, RAWX>(g, r, a, s);
+    default: return launch_g<4, TY, RAWX>(g, r, a, s);
   }
 }
 
@@ -603,9 +643,18 @@ hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int
                                int64_t ldy, hipStream_t s) {
   if (T <= kDecodeMaxT)
     return launch_wlowbit_decode(T, d_in, d_out, q, g, r, Xs, ldxs, codes, scales, zeros, B, Z, Y, y_f32, ldy, s);
-  if (y_f32)
-    return launch_q<float>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
-  return launch_q<_Float16>(q, g, r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
+  const GemmArgs a{T, d_in, d_out, Xs, ldxs, nullptr, codes, scales, zeros, B, Z, Y, ldy};
+  if (y_f32) return launch_q<float, false>(q, g, r, a, s);
+  return launch_q<_Float16, false>(q, g, r, a, s);
+}
+
+hipError_t launch_wlowbit_gemm_rawx(int64_t T, int d_in, int d_out, int q, int g, int r, const void* X,
+                                    int64_t ldx, const void* dinv16, const uint32_t* codes, const void* scales,
+                                    const void* zeros, const float* B, const float* Z, void* Y, int64_t ldy,
+                                    hipStream_t s) {
+  if (T <= kDecodeMaxT) return hipErrorInvalidValue;
+  const GemmArgs a{T, d_in, d_out, X, ldx, dinv16, codes, scales, zeros, B, Z, Y, ldy};
+  return launch_q<_Float16, true>(q, g, r, a, s);
 }
 
 }  // namespace ttq

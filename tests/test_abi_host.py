@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 2
+    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 3
     for s in range(7):
         assert lib.ttq_status_string(s).decode().startswith("TTQ_")
     assert lib.ttq_status_string(99) == b"unknown ttq_status"
@@ -53,7 +53,8 @@ def test_query_sizes_cfg5(lib):
     assert lib.ttq_query_sizes(ctypes.byref(_cfg()), 16384, ctypes.byref(sz)) == 0
     assert sz.codes_bytes == 8192 * 160 * 4 * 4          # 20.97 MB of 4-bit codes
     assert sz.scales_bytes == sz.zeros_bytes == 8192 * 160 * 2
-    assert sz.d_bytes == sz.dinvsqrt_bytes == 5120 * 4
+    assert sz.d_bytes == 5120 * 4
+    assert sz.dinvsqrt_bytes == 5120 * 4 + 5120 * 2  # fp32, then the fp16 copy
     assert sz.wres_bytes == 0
     assert sz.workspace_bytes == lib.ttq_colstats_workspace_bytes(16384, 5120) > 0
     assert sz.linear_workspace_bytes == lib.ttq_linear_workspace_bytes(16384, 5120, 8192, 0) == 16384 * 5120 * 2
@@ -126,6 +127,17 @@ def test_null_and_alignment(lib):
         == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_wlowbit_gemm(0, 128, 64, 4, 32, 0, None, 128, None, None, None, None, None,
                                 None, 1, 64, None) == _capi.TTQ_OK
+    # raw-input gemm: prefill sizes only (T > 64), NULL D^(-1/2), misaligned X, odd ldx
+    assert lib.ttq_wlowbit_gemm_raw(64, 128, 64, 4, 32, 0, P, 128, P, P, P, P, None, None, P, 64, None) \
+        == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_wlowbit_gemm_raw(65, 128, 64, 4, 32, 0, P, 128, None, P, P, P, None, None, P, 64, None) \
+        == _capi.TTQ_ERR_NULL
+    assert lib.ttq_wlowbit_gemm_raw(65, 128, 64, 4, 32, 0, MIS, 128, P, P, P, P, None, None, P, 64, None) \
+        == _capi.TTQ_ERR_ALIGN
+    assert lib.ttq_wlowbit_gemm_raw(65, 128, 64, 4, 32, 0, P, 130, P, P, P, P, None, None, P, 64, None) \
+        == _capi.TTQ_ERR_ALIGN
+    assert lib.ttq_wlowbit_gemm_raw(65, 128, 64, 4, 32, 16, P, 128, P, P, P, P, P, None, P, 64, None) \
+        == _capi.TTQ_ERR_NULL
     # prescale: d not a multiple of 64, NULL dinvsqrt, misaligned Xs, T = 0 no-op
     assert lib.ttq_prescale(P, 1, 4, 96, 96, P, P, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_prescale(P, 1, 4, 128, 128, None, P, None) == _capi.TTQ_ERR_NULL

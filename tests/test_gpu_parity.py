@@ -112,7 +112,7 @@ def _check_quant(W16, D32, q, g, tag):
     say(f"quantize {tag} q={q} g={g} shape={W16.shape}")
     cg, sg, zg = ttq.ttq_quantize_pack(dev(W16), dev(D32), q, g)
     c0, s0, z0 = oracle.quantize(W16, D32, q, g)
-    words0 = oracle.tile_codes(oracle.pack(c0, q), q)
+    words0 = oracle.device_codes(c0, q)
     cg = host(cg).view(np.uint32).reshape(-1)
     assert cg.shape == words0.shape
     bad = np.flatnonzero(cg != words0)
@@ -220,17 +220,6 @@ def test_lowrank_z(cfg, T):
 # ---------------------------------------------------------------------------
 # wlowbit_gemm given the oracle's codes
 # ---------------------------------------------------------------------------
-def unpermute8(xs):
-    """Undo the prescale layout: within every 8 channels the stored order is
-    0 4 1 5 2 6 3 7 (include/ttq.h, ttq_prescale)."""
-    T, d = xs.shape
-    blk = xs.reshape(T, d // 8, 8)
-    out = np.empty_like(blk)
-    out[:, :, 0:4] = blk[:, :, 0::2]
-    out[:, :, 4:8] = blk[:, :, 1::2]
-    return out.reshape(T, d)
-
-
 @pytest.mark.parametrize("cfg,T", [(1, 333), (2, 2048), (5, 4097), (3, 1)])
 def test_prescale(cfg, T):
     w = wl.CONFIGS[cfg]
@@ -241,13 +230,13 @@ def test_prescale(cfg, T):
     Xs = host(ttq.ttq_prescale(dev(X), dev(R)))
     assert Xs.dtype == np.float16 and Xs.shape == X.shape
     ref = X.astype(np.float64) * R.astype(np.float64)[None, :]
-    got = unpermute8(Xs).astype(np.float64)
+    got = Xs.astype(np.float64)
     # one fp32 rounding, then one fp16 rounding (normal range)
     bound = np.abs(ref) * (2.0 ** -11 + 2.0 ** -23) + 2.0 ** -25
     assert np.all(np.abs(got - ref) <= bound)
 
 
-def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0):
+def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0, raw=False):
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg, T=T)
     D = oracle.colstats(X, w.p, w.lam, w.alpha)
@@ -258,17 +247,21 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0):
         A = (rng.standard_normal((r, W.shape[1])) * 0.018).astype(np.float32)
     Wq = oracle.residual(W, B, A) if r else W
     c, s, z = oracle.quantize(Wq, D, q, g)
-    say(f"gemm cfg={cfg} T={T} q={q} g={g} r={r}")
+    say(f"gemm cfg={cfg} T={T} q={q} g={g} r={r} raw={raw}")
     Xd = dev(X)
     Zd = ttq.ttq_lowrank_z(Xd, dev(A)) if r else None
-    Xs = ttq.ttq_prescale(Xd, dev(oracle_dinvsqrt(D)))
-    if pad_ld:  # the GEMM on a row-strided view of the pre-scaled input
+    Xs = Xd if raw else ttq.ttq_prescale(Xd, dev(oracle_dinvsqrt(D)))
+    if pad_ld:  # the GEMM on a row-strided view of its input
         wide = torch.zeros((T, X.shape[1] + pad_ld), dtype=torch.float16, device="cuda")
         wide[:, :X.shape[1]] = Xs
         Xs = wide[:, :X.shape[1]]
-    Yd = ttq.ttq_wlowbit_gemm(Xs, dev(oracle.tile_codes(oracle.pack(c, q), q)),
-                              dev(oracle.tile_groups(s)), dev(oracle.tile_groups(z)), q, g,
-                              W.shape[0], B=dev(B) if r else None, Z=Zd, out_dtype=Xd.dtype)
+    parts = (dev(oracle.device_codes(c, q)), dev(oracle.tile_groups(s)), dev(oracle.tile_groups(z)), q, g,
+             W.shape[0])
+    if raw:  # the raw input, fp16(D^(-1/2)) on the weight side
+        Yd = ttq.ttq_wlowbit_gemm_raw(Xs, dev(oracle_dinvsqrt(D).astype(np.float16)), *parts,
+                                      B=dev(B) if r else None, Z=Zd)
+    else:
+        Yd = ttq.ttq_wlowbit_gemm(Xs, *parts, B=dev(B) if r else None, Z=Zd, out_dtype=Xd.dtype)
     Yg = host(Yd)
     assert Yg.dtype == X.dtype and Yg.shape == (T, W.shape[0])
     rows = np.arange(T) if sample_rows is None else sample_rows
@@ -305,13 +298,24 @@ def test_decode_parity(cfg, T, q, g, r):
 def test_gemm_parity_strided_input():
     _gemm_case(3, 300, 4, 32, 0, pad_ld=64)
     _gemm_case(3, 40, 4, 32, 0, pad_ld=64)
+    _gemm_case(3, 300, 4, 32, 0, pad_ld=64, raw=True)
 
 
-@pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16), (5, 0)])
-def test_gemm_parity_full_cfg5_sampled(q, r):
+@pytest.mark.parametrize("cfg,T,q,g,r", [
+    (2, 2048, 3, 32, 16), (2, 65, 5, 64, 0), (3, 1000, 4, 64, 0), (3, 257, 2, 128, 0), (3, 100, 3, 128, 16),
+    (4, 777, 4, 32, 0), (4, 513, 5, 32, 16), (5, 4097, 4, 32, 0),
+])
+def test_gemm_raw_parity(cfg, T, q, g, r):
+    """The raw-input form (what ttq_linear runs for fp16 input, T > 64)."""
+    _gemm_case(cfg, T, q, g, r, raw=True)
+
+
+@pytest.mark.parametrize("q,r,raw", [(4, 0, False), (2, 0, False), (4, 16, False), (5, 0, False),
+                                     (4, 0, True), (4, 16, True), (2, 0, True)])
+def test_gemm_parity_full_cfg5_sampled(q, r, raw):
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 16383],
                                      np.random.default_rng(3).integers(0, 16384, 59)]))
-    _gemm_case(5, 16384, q, 32, r, sample_rows=rows)
+    _gemm_case(5, 16384, q, 32, r, sample_rows=rows, raw=raw)
 
 
 # ---------------------------------------------------------------------------
@@ -333,10 +337,11 @@ def _e2e(cfg, q, g, r, T=None, prompt=0, sample_rows=None, alpha=None, decode_T=
     D0 = oracle.colstats(X, w.p, w.lam, alpha)
     Dg = host(layer.D)
     assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+    # the fp16 copy of D^(-1/2) is the fp32 one rounded to nearest even
+    assert host(layer.dinvsqrt16).tobytes() == host(layer.dinvsqrt).astype(np.float16).tobytes()
     Wq = oracle.residual(W, B, A) if r else W
     c0, s0, z0 = oracle.quantize(Wq, D0, q, g)
-    cg = oracle.unpack(oracle.untile_codes(host(layer.codes).view(np.uint32), q, W.shape[0], W.shape[1]),
-                       q, W.shape[1])
+    cg = oracle.codes_from_device(host(layer.codes).view(np.uint32), q, W.shape[0], W.shape[1])
     agree = np.mean(cg == c0)
     say(f"  code agreement with the oracle's own D: {agree:.6f}")
     assert agree >= 0.999
@@ -435,7 +440,7 @@ def test_long_prompt_past_2gb():
     Dg = host(layer.D)
     assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
     c0, s0, z0 = oracle.quantize(W, Dg, 4, 32)          # codes given the GPU's own D: bit-exact
-    assert host(layer.codes).view(np.uint32).tobytes() == oracle.tile_codes(oracle.pack(c0, 4), 4).tobytes()
+    assert host(layer.codes).view(np.uint32).tobytes() == oracle.device_codes(c0, 4).tobytes()
     Y = layer.linear(Xd)
     rows = np.array([0, 1, 4095, 4096, T // 2 + 7, T - 4097, T - 2, T - 1])
     Yg = host(Y[torch.from_numpy(rows).to(Y.device)])
@@ -483,7 +488,7 @@ def test_alpha_zero_gives_rtn_on_gpu():
     layer.prepare(dev(X))
     assert np.all(host(layer.D) == 1.0)
     c0, s0, z0 = oracle.quantize(W, np.ones(W.shape[1], np.float32), 3, 32)
-    assert host(layer.codes).view(np.uint32).tobytes() == oracle.tile_codes(oracle.pack(c0, 3), 3).tobytes()
+    assert host(layer.codes).view(np.uint32).tobytes() == oracle.device_codes(c0, 3).tobytes()
     assert host(layer.scales).view(np.uint16).tobytes() == oracle.tile_groups(s0).view(np.uint16).tobytes()
     layer.close()
 

@@ -1,5 +1,6 @@
-"""Pins for the packing format and its tiled storage order: hand-worked
-words and indices, round trips, bijection."""
+"""Pins for the packing format, the order of the codes inside every 8 and
+the tiled storage order: hand-worked words and indices, round trips,
+bijection."""
 import json
 import os
 
@@ -78,3 +79,32 @@ def test_tiled_step_chunks_are_contiguous():
     # and a row's step words put the words of MFMA lane half 0 (w = 0, 2) first
     row = oracle.tiled_code_index(5, np.array([0, 0, 1, 1, 0, 0, 1, 1]), np.array([0, 2, 0, 2, 1, 3, 1, 3]), 4, d)
     assert np.array_equal(row - row[0], np.arange(8))
+
+
+def test_slot_order_worked_words(golden_dir):
+    with open(os.path.join(golden_dir, "slot_order.json")) as f:
+        g = json.load(f)
+    for q, words in g["words"].items():
+        q = int(q)
+        codes = (np.arange(32) % (1 << q)).astype(np.uint8)[None, :]
+        packed = oracle.pack(oracle.interleave8(codes), q)
+        assert [hex(int(w)) for w in packed[0, 0]] == words
+
+
+def test_slot_order_pairs_natural_channels():
+    # slots j and j + 4 of every group of 8 hold channels 2j and 2j + 1
+    ch = np.arange(64)[None, :]
+    st8 = oracle.interleave8(ch).reshape(8, 8)
+    for grp in range(8):
+        for j in range(4):
+            assert st8[grp, j] == 8 * grp + 2 * j and st8[grp, j + 4] == 8 * grp + 2 * j + 1
+
+
+@pytest.mark.parametrize("q", [2, 3, 4, 5])
+def test_device_codes_roundtrip(q):
+    d_out, d = 64, 192
+    codes = np.random.default_rng(10 + q).integers(0, 1 << q, size=(d_out, d)).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.deinterleave8(oracle.interleave8(codes)), codes)
+    flat = oracle.device_codes(codes, q)
+    assert flat.dtype == np.uint32 and flat.size == d_out * d // 32 * q
+    np.testing.assert_array_equal(oracle.codes_from_device(flat, q, d_out, d), codes)
