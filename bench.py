@@ -42,7 +42,7 @@ def parse():
                     help="untimed steps run for this long before the warmup steps, so that the GPU's "
                          "clock and power state is the steady one of continuous work")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels,qkv; "
+    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels,qkv,variants; "
                     "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
                     "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
@@ -128,7 +128,7 @@ def main():
         print("bench.py: this implementation runs on one GPU only; the multi-GPU sharding of the path "
               "is described, not implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels", "qkv"}
+    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels", "qkv", "variants"}
 
     import numpy as np
     import torch
@@ -274,6 +274,33 @@ def main():
         layer16.close()
         del rng
 
+    # ---- other code widths and group sizes on the same prompt and weight ----
+    # (the same step, r = 0: prepare + projection, settled and timed like the
+    # headline; the quantize_pack and GEMM kernels alone by their own events)
+    variants = None
+    if "variants" in only:
+        variants = {}
+        for qv, gv in ((2, 32), (3, 32), (5, 32), (4, 16), (4, 64), (4, 128)):
+            lv = ttq.TTQLinear(W, q=qv, g=gv, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+
+            def step_v():
+                lv.prepare(X)
+                lv.linear(X, out=Y)
+            settle(step_v, args.settle_ms / 4, torch)
+            t_v = time_loop(step_v, args.steps, torch)
+            t_q = time_graph(lambda: ttq.ttq_quantize_pack(W, lv.D, qv, gv, lv.codes, lv.scales, lv.zeros),
+                             10, torch)
+            t_g = time_loop(lambda: ttq.ttq_wlowbit_gemm_raw(X, lv.dinvsqrt16, lv.codes, lv.scales, lv.zeros, qv,
+                                                             gv, d_out, out=Y), 10, torch)
+            qp_b = 2 * d_out * d + 4 * d + qv * d_out * d // 8 + 4 * d_out * d // gv
+            variants[f"q{qv}_g{gv}"] = {
+                "k_tok_s": T / t_v / 1e3, "ms_per_step": t_v * 1e3,
+                "quantize_pack_us": t_q * 1e6, "quantize_pack_frac_hbm": qp_b / t_q / 1e9 / HBM_PEAK_GBS,
+                "gemm_us_back_to_back": t_g * 1e6,
+                "gemm_frac_mfma_back_to_back": gemm_flops / t_g / 1e12 / MFMA_F16_PEAK_TFLOPS}
+            lv.close()
+        log(f"bench: variants {json.dumps(variants)}")
+
     # ---- q, k, v of one layer sharing one prepare (GQA: k, v have 1024 rows) ----
     qkv = None
     if "qkv" in only:
@@ -406,6 +433,8 @@ def main():
         out["decode"] = decode
     if qkv is not None:
         out["qkv_shared_prepare"] = qkv
+    if variants is not None:
+        out["variants"] = variants
     print(json.dumps(out), flush=True)
     layer.close()
 

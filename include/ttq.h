@@ -84,7 +84,7 @@ typedef enum ttq_dtype {
  *   d_in  (d)  input channels,  multiple of 64 and of g
  *   d_out (d') output channels, multiple of 32
  *   q  bits per code: 2, 3, 4 or 5
- *   g  group size along d_in: 32, 64 or 128
+ *   g  group size along d_in: 16, 32, 64 or 128 (8: TTQ_ERR_UNSUPPORTED)
  *   r  low-rank rank: 0 or 16
  *   alpha >= 0, p > 0, lambda > 0 unless alpha == 0 (a dead channel would
  *   otherwise get d_j = 0 and an infinite D^(-1/2)). */

@@ -61,8 +61,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 ttq_status check_qgr(int32_t q, int32_t g, int32_t r) {
   if (q < 2 || q > 5) return fail(TTQ_ERR_INVALID_ARG, "q=%d, expected 2, 3, 4 or 5", q);
-  if (g == 16 || g == 8) return fail(TTQ_ERR_UNSUPPORTED, "group size %d (micro-scaling) is not built", g);
-  if (g != 32 && g != 64 && g != 128) return fail(TTQ_ERR_INVALID_ARG, "g=%d, expected 32, 64 or 128", g);
+  if (g == 8) return fail(TTQ_ERR_UNSUPPORTED, "group size 8 is not built (16, 32, 64 or 128)");
+  if (g != 16 && g != 32 && g != 64 && g != 128) return fail(TTQ_ERR_INVALID_ARG, "g=%d, expected 16, 32, 64 or 128", g);
   if (r < 0) return fail(TTQ_ERR_INVALID_ARG, "r=%d is negative", r);
   if (r != 0 && r != 16) return fail(TTQ_ERR_UNSUPPORTED, "rank r=%d is not built (0 or 16)", r);
   return TTQ_OK;

@@ -24,8 +24,8 @@
 //     row per 16 lanes, and is parked in LDS (rows padded by 16 bytes, so
 //     the block reads below hit 16 distinct bank groups);
 //   * thread (r, b) = (row in tile, 32-channel block) quantises its block
-//     from LDS; groups of 64 / 128 channels meet through an LDS min/max
-//     exchange;
+//     from LDS (as two groups when g = 16); groups of 64 / 128 channels meet
+//     through an LDS min/max exchange;
 //   * codes are placed in LDS in the tiled order and leave as one contiguous
 //     store of 2 steps x 32 rows x 2q words; scales and zeros likewise (all
 //     with nontemporal stores, which measured about 5 % faster here).
@@ -103,7 +103,9 @@ template <int Q, int G>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const _Float16* __restrict__ W, const float* __restrict__ D, int d_in,
     uint32_t* __restrict__ codes, _Float16* __restrict__ scales, _Float16* __restrict__ zeros) {
-  constexpr int LPG = G / 32;               // blocks per group
+  constexpr int LPG = G >= 32 ? G / 32 : 1;  // blocks per group
+  constexpr int SG = G < 32 ? 32 / G : 1;     // groups inside one block (g = 16: 2)
+  constexpr int CPG = 32 / SG;                // channels of the block per such group
   constexpr float N = (float)((1 << Q) - 1);
   constexpr int SW = 2 * Q;                 // words per row per 64-channel step
   constexpr int GPW = kCols / G;            // groups per workgroup column range
@@ -147,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   const int h = bl & 1, ksl = bl >> 1;
 
   float v[32];
-  float mn = 0.f, mx = 0.f;
+  float mn[SG], mx[SG];
+#pragma unroll
+  for (int sg = 0; sg < SG; ++sg) mn[sg] = mx[sg] = 0.f;
   if (active) {
     const _Float16* src = &wt[r * kRowPitch + bl * 32];
 #pragma unroll
@@ -162,41 +166,45 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       o[6] = mul_lo(raw.w, sb.z); o[7] = mul_hi(raw.w, sb.w);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        mn = fminf(mn, o[k]);
-        mx = fmaxf(mx, o[k]);
+        mn[(8 * i + k) / CPG] = fminf(mn[(8 * i + k) / CPG], o[k]);
+        mx[(8 * i + k) / CPG] = fmaxf(mx[(8 * i + k) / CPG], o[k]);
       }
     }
   }
   if constexpr (LPG > 1) {
-    red_mn[bl][r] = mn;
-    red_mx[bl][r] = mx;
+    red_mn[bl][r] = mn[0];
+    red_mx[bl][r] = mx[0];
     __syncthreads();
     const int first = bl & ~(LPG - 1);
 #pragma unroll
     for (int j = 0; j < LPG; ++j) {
-      mn = fminf(mn, red_mn[first + j][r]);
-      mx = fmaxf(mx, red_mx[first + j][r]);
+      mn[0] = fminf(mn[0], red_mn[first + j][r]);
+      mx[0] = fmaxf(mx[0], red_mx[first + j][r]);
     }
   }
 
   if (active) {
-    float s, zf;
-    _Float16 s16;
-    if (mx == mn) {  // all-zero group
-      s16 = (_Float16)1.0f;
-      s = 1.0f;
-      zf = 0.0f;
-    } else {
-      const float s32 = (mx - mn) / N;
-      s16 = fp16_round_up(s32);
-      s = (float)s16;
-      // z by the same reciprocal fast path
-      const float x = -mn * __builtin_amdgcn_rcpf(s);
-      float zr = rintf(x);
-      if (fabsf(x - zr) > 0.5f - 0x1p-16f) zr = rintf(-mn / s);
-      zf = fminf(fmaxf(zr, 0.0f), N) + 0.0f;
+    // per group of the block: scale s, zero point zf, 1/s
+    float s[SG], zf[SG], rcp[SG];
+    _Float16 s16[SG];
+#pragma unroll
+    for (int sg = 0; sg < SG; ++sg) {
+      if (mx[sg] == mn[sg]) {  // all-zero group
+        s16[sg] = (_Float16)1.0f;
+        s[sg] = 1.0f;
+        zf[sg] = 0.0f;
+      } else {
+        const float s32 = (mx[sg] - mn[sg]) / N;
+        s16[sg] = fp16_round_up(s32);
+        s[sg] = (float)s16[sg];
+        // z by the same reciprocal fast path
+        const float x = -mn[sg] * __builtin_amdgcn_rcpf(s[sg]);
+        float zr = rintf(x);
+        if (fabsf(x - zr) > 0.5f - 0x1p-16f) zr = rintf(-mn[sg] / s[sg]);
+        zf[sg] = fminf(fmaxf(zr, 0.0f), N) + 0.0f;
+      }
+      rcp[sg] = __builtin_amdgcn_rcpf(s[sg]);
     }
-    const float rcp = __builtin_amdgcn_rcpf(s);
 
     // code(k) gives the integer-valued float stored in slot k; packing into
     // the bitstream (slot k at bit Q*k of the block's Q words)
@@ -239,19 +247,29 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     };
     float far = 0.0f;  // largest distance of u from its rounded value
     pack([&](int k) {
-      const float u = __builtin_fmaf(v[slot_channel(k)], rcp, zf);
+      const int ch = slot_channel(k), sg = ch / CPG;
+      const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
       const float c = rintf(u);
       far = fmaxf(far, fabsf(u - c));
       return c;
     });
     if (far > 0.5f - 0x1p-16f)  // rare: redo the block with the IEEE division
-      pack([&](int k) { return fminf(fmaxf(rintf(v[slot_channel(k)] / s) + zf, 0.0f), N); });
+      pack([&](int k) {
+        const int ch = slot_channel(k), sg = ch / CPG;
+        return fminf(fmaxf(rintf(v[ch] / s[sg]) + zf[sg], 0.0f), N);
+      });
     uint32_t* dst = &outc[(ksl * 32 + r) * SW];
 #pragma unroll
     for (int w = 0; w < Q; ++w) dst[step_pos<Q>(h, w)] = word[w];
-    if ((bl % LPG) == 0) {
-      outs[(bl / LPG) * 32 + r] = s16;
-      outz[(bl / LPG) * 32 + r] = (_Float16)zf;
+    if constexpr (SG > 1) {
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        outs[(bl * SG + sg) * 32 + r] = s16[sg];
+        outz[(bl * SG + sg) * 32 + r] = (_Float16)zf[sg];
+      }
+    } else if ((bl % LPG) == 0) {
+      outs[(bl / LPG) * 32 + r] = s16[0];
+      outz[(bl / LPG) * 32 + r] = (_Float16)zf[0];
     }
   }
   __syncthreads();
@@ -280,6 +298,10 @@ hipError_t launch_q(int d_out, int d_in, int g, const _Float16* W, const float* 
                     _Float16* scales, _Float16* zeros, hipStream_t s) {
   dim3 grid((unsigned)((d_in + kCols - 1) / kCols), (unsigned)(d_out / 32));
   switch (g) {
+    case 16:
+      hipLaunchKernelGGL((quantize_pack_kernel<Q, 16>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
+                         scales, zeros);
+      break;
     case 32:
       hipLaunchKernelGGL((quantize_pack_kernel<Q, 32>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
                          scales, zeros);

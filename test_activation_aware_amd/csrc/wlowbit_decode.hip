@@ -442,7 +442,8 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
     const uint32_t* codes,  // (input pointers not __restrict__: see wlowbit_decode_kernel)
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros, float* __restrict__ P) {
   constexpr int SW = 2 * Q;
-  constexpr int kPieces = 128;  // scale / zero pieces of 16 bytes a split can touch, per wave
+  // scale / zero pieces of 16 bytes a split can touch, per wave (a multiple of 64)
+  constexpr int kPieces = ((kSplitPerMax * 64 / G + 1) * 4 + 63) / 64 * 64;
   constexpr int kTokPerThread = (kDecodeMaxT + 5) / 6;  // >= 6 thread groups stage the input
   __shared__ __attribute__((aligned(16))) _Float16 xsl[kDecodeMaxT * kSplitPitch];
   __shared__ __attribute__((aligned(16))) _Float16 sgrp[kWaves][2][kPieces * 8];
@@ -635,6 +636,10 @@ hipError_t launch_fused(int g, int T, int d_in, int d_out, const void* X, int64_
   TX* y = static_cast<TX*>(Y);
   const float* nf = nullptr;
   switch (g) {
+    case 16:
+      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 16, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
+                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
+      break;
     case 32:
       hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 32, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
                          d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
@@ -676,6 +681,7 @@ hipError_t launch_g(int g, int r, int T, int d_in, int d_out, const void* Xs, in
                     const uint32_t* codes, const void* scales, const void* zeros, const float* B,
                     const float* Z, void* Y, int64_t ldy, hipStream_t s) {
   switch (g) {
+    case 16: return launch_lr<Q, 16, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     case 32: return launch_lr<Q, 32, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     case 64: return launch_lr<Q, 64, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
     default: return launch_lr<Q, 128, TY>(r, T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
@@ -724,6 +730,7 @@ hipError_t launch_splitk(int q, int g, int T, int d_in, int d_out, const void* X
                          float* P, hipStream_t s) {
 #define TTQ_SPLITK_G(QQ)                                                                                      \
   switch (g) {                                                                                                \
+    case 16: return launch_splitk_g<QQ, 16, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
     case 32: return launch_splitk_g<QQ, 32, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
     case 64: return launch_splitk_g<QQ, 64, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \
     default: return launch_splitk_g<QQ, 128, TX>(T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, P, s); \

@@ -240,7 +240,9 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   constexpr int CW = 8 * 32 * SW;               // code words per step (8 row tiles)
   constexpr int CSL = CW / 4;                   // 16-byte slots of codes per step
   constexpr int CJ = (CSL + kThreads - 1) / kThreads;
-  static_assert(XSL % kThreads == 0 && CSL % 64 == 0 && SLOTS <= 64, "slot split");
+  constexpr int SJ = (SLOTS + 63) / 64;         // 16-byte loads per lane of scales / zeros
+  constexpr bool WIDE_S = FN * GPK > 4;         // more than 4 groups per fragment pair (g = 16)
+  static_assert(XSL % kThreads == 0 && CSL % 64 == 0 && (SLOTS <= 64 || SLOTS % 64 == 0), "slot split");
 
   // One array per stage: an LDS read of one array does not have to wait for
   // direct-to-LDS loads still landing in another.
@@ -371,8 +373,14 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     const int p = (wave + 4 * j) * 64 + lane;
     coff[j] = (int)(((p / (16 * Q)) * ctile + 4 * (p % (16 * Q))) * 4);
   }
-  // scales (wave 0) and zeros (wave 1): lane l < SLOTS moves 8 halfs
-  const int soff = ((lane / (4 * GPK)) * ng * 32 + 8 * (lane % (4 * GPK))) * 2;
+  // scales (wave 0) and zeros (wave 1): slot p = 64 j + lane < SLOTS moves
+  // 8 halfs (row tile p / (4 GPK), piece p % (4 GPK) of its step)
+  int soff[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) {
+    const int p = 64 * j + lane;
+    soff[j] = ((p / (4 * GPK)) * ng * 32 + 8 * (p % (4 * GPK))) * 2;
+  }
   // RAWX: the step's 64 fp16 D^(-1/2) values, lanes 0-7 of wave 2
   const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(dvh, RAWX ? (int64_t)d_in * 2 : 0);
 
@@ -383,16 +391,22 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
 #pragma unroll
     for (int j = 0; j < CJ; ++j)
       if ((wave + 4 * j) * 64 < CSL) lds_dma16(rs_c, coff[j], kt * 32 * SW * 4, cs + 4 * (wave + 4 * j) * 64);
-    if (wave < 2 && lane < SLOTS)
-      lds_dma16(wave == 0 ? rs_s : rs_z, soff, (kt * BK / G) * 32 * 2, sz + wave * SZ);
+#pragma unroll
+    for (int j = 0; j < SJ; ++j)
+      if (wave < 2 && 64 * j + lane < SLOTS)
+        lds_dma16(wave == 0 ? rs_s : rs_z, soff[j], (kt * BK / G) * 32 * 2, sz + wave * SZ + 64 * 8 * j);
     if constexpr (RAWX)
       if (wave == 2 && lane < BK / 8) lds_dma16(rs_d, 16 * lane, kt * BK * 2, dv);
   };
 
   // ---- operands from LDS ----
-  // per fragment i and group gi (k = i * GPK + gi): the scale s at element k
-  // and -(1024 + z) at element 4 + k
-  typedef h8 Scales;
+  // per fragment i and group gi (k = i * GPK + gi): the scale s and
+  // -(1024 + z); up to 4 groups per fragment pair share one vector (s at
+  // element k, -(1024 + z) at 4 + k), 8 (g = 16) take two
+  struct ScalePair {
+    h8 s, nz;
+  };
+  using Scales = std::conditional_t<WIDE_S, ScalePair, h8>;
   auto read_scales = [&](const _Float16* sz, Scales& out) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -401,18 +415,30 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
         const int tl = wave * 2 + i;
         const _Float16 sv = sz[(tl * GPK + gi) * 32 + l32];
         const _Float16 z = sz[SZ + (tl * GPK + gi) * 32 + l32];
-        out[i * GPK + gi] = sv;
-        out[4 + i * GPK + gi] = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
+        const _Float16 nzv = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
+        if constexpr (WIDE_S) {
+          out.s[i * GPK + gi] = sv;
+          out.nz[i * GPK + gi] = nzv;
+        } else {
+          out[i * GPK + gi] = sv;
+          out[4 + i * GPK + gi] = nzv;
+        }
       }
   };
   // dvp (RAWX): this lane's 8 fp16 D^(-1/2) values of the sub-step
   auto dequant = [&](auto sc_, const CodeFrag<Q>& cf, const Scales& sv, int i, const h8& dvp) -> h8 {
     constexpr int S = decltype(sc_)::value;
-    constexpr int gi = (G == 32) ? (S >> 1) : 0;
+    constexpr int gi = (G == 16) ? S : (G == 32) ? (S >> 1) : 0;
     uint32_t pr[4];
     code_pairs<Q, S>(cf, hh, mask, magic, pr);
-    const h2 sc = {sv[i * GPK + gi], sv[i * GPK + gi]};
-    const h2 nz = {sv[4 + i * GPK + gi], sv[4 + i * GPK + gi]};
+    h2 sc, nz;
+    if constexpr (WIDE_S) {
+      sc = h2{sv.s[i * GPK + gi], sv.s[i * GPK + gi]};
+      nz = h2{sv.nz[i * GPK + gi], sv.nz[i * GPK + gi]};
+    } else {
+      sc = h2{sv[i * GPK + gi], sv[i * GPK + gi]};
+      nz = h2{sv[4 + i * GPK + gi], sv[4 + i * GPK + gi]};
+    }
     h8 a;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -619,6 +645,7 @@ hipError_t launch_lr(int r, const GemmArgs& a, hipStream_t s) {
 template <int Q, typename TY, bool RAWX>
 hipError_t launch_g(int g, int r, const GemmArgs& a, hipStream_t s) {
   switch (g) {
+    case 16: return launch_lr<Q, 16, TY, RAWX>(r, a, s);
     case 32: return launch_lr<Q, 32, TY, RAWX>(r, a, s);
     case 64: return launch_lr<Q, 64, TY, RAWX>(r, a, s);
     default: return launch_lr<Q, 128, TY, RAWX>(r, a, s);

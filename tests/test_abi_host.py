@@ -82,7 +82,8 @@ def test_query_sizes_cfg5(lib):
     (dict(q=1), _capi.TTQ_ERR_INVALID_ARG),
     (dict(q=6), _capi.TTQ_ERR_INVALID_ARG),
     (dict(q=8), _capi.TTQ_ERR_INVALID_ARG),
-    (dict(g=16), _capi.TTQ_ERR_UNSUPPORTED),
+    (dict(g=16), _capi.TTQ_OK),
+    (dict(g=8), _capi.TTQ_ERR_UNSUPPORTED),
     (dict(g=48), _capi.TTQ_ERR_INVALID_ARG),
     (dict(r=8), _capi.TTQ_ERR_UNSUPPORTED),
     (dict(r=-1), _capi.TTQ_ERR_INVALID_ARG),

@@ -123,7 +123,7 @@ def _check_quant(W16, D32, q, g, tag):
 
 @pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (2, 3, 32), (3, 4, 32), (3, 4, 64), (3, 4, 128),
                                      (4, 4, 32), (5, 4, 32), (5, 2, 32), (2, 5, 32), (3, 5, 64),
-                                     (4, 5, 128), (5, 5, 32)])
+                                     (4, 5, 128), (5, 5, 32), (2, 3, 16), (3, 4, 16), (5, 4, 16)])
 def test_quantize_pack_bitexact(cfg, q, g):
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg)
@@ -135,7 +135,7 @@ def test_quantize_pack_bitexact(cfg, q, g):
 
 
 @pytest.mark.parametrize("q", [2, 3, 4, 5])
-@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
 def test_quantize_pack_edge_cases(q, g):
     rng = np.random.default_rng(100 * q + g)
     d_out, d = 96, 512
@@ -279,6 +279,7 @@ def _gemm_case(cfg, T, q, g, r, sample_rows=None, pad_ld=0, raw=False):
     (3, 1000, 4, 32, 0), (3, 1000, 4, 64, 0), (3, 1000, 4, 128, 0), (3, 257, 2, 64, 0), (3, 100, 3, 128, 16),
     (4, 777, 4, 32, 0), (4, 513, 4, 32, 16),
     (1, 333, 5, 32, 0), (2, 2048, 5, 32, 16), (3, 1000, 5, 64, 0), (3, 257, 5, 128, 0), (4, 513, 5, 32, 16),
+    (1, 2048, 4, 16, 0), (2, 300, 3, 16, 16), (3, 1000, 4, 16, 0), (4, 777, 2, 16, 16),
 ])
 def test_gemm_parity(cfg, T, q, g, r):
     _gemm_case(cfg, T, q, g, r)
@@ -289,6 +290,7 @@ def test_gemm_parity(cfg, T, q, g, r):
     (3, 7, 4, 64, 0), (3, 64, 4, 128, 0), (3, 31, 2, 32, 0), (4, 16, 4, 32, 16), (4, 63, 2, 64, 0),
     (5, 1, 4, 32, 0), (5, 64, 4, 32, 16),
     (1, 3, 5, 32, 0), (2, 40, 5, 32, 16), (3, 17, 5, 64, 0), (4, 64, 5, 128, 0), (5, 1, 5, 32, 0),
+    (1, 7, 4, 16, 0), (2, 33, 3, 16, 16), (5, 16, 4, 16, 0),
 ])
 def test_decode_parity(cfg, T, q, g, r):
     """T <= 64 on the pre-scaled input takes the decode kernel."""
@@ -303,7 +305,7 @@ def test_gemm_parity_strided_input():
 
 @pytest.mark.parametrize("cfg,T,q,g,r", [
     (2, 2048, 3, 32, 16), (2, 65, 5, 64, 0), (3, 1000, 4, 64, 0), (3, 257, 2, 128, 0), (3, 100, 3, 128, 16),
-    (4, 777, 4, 32, 0), (4, 513, 5, 32, 16), (5, 4097, 4, 32, 0),
+    (4, 777, 4, 32, 0), (4, 513, 5, 32, 16), (5, 4097, 4, 32, 0), (3, 300, 4, 16, 0), (4, 513, 5, 16, 16),
 ])
 def test_gemm_raw_parity(cfg, T, q, g, r):
     """The raw-input form (what ttq_linear runs for fp16 input, T > 64)."""
@@ -368,7 +370,7 @@ def test_e2e_cfg2_lowrank(alpha):
     _e2e(2, 3, 32, 16, alpha=alpha)
 
 
-@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
 def test_e2e_cfg3_groupsize(g):
     _e2e(3, 4, g, 0, T=2048)
 
@@ -391,7 +393,7 @@ def test_e2e_q5(cfg, g, r):
 
 
 @pytest.mark.parametrize("cfg,q,g", [(1, 4, 32), (3, 4, 64), (3, 3, 128), (5, 2, 32), (5, 4, 32),
-                                     (1, 5, 64), (5, 5, 32)])
+                                     (1, 5, 64), (5, 5, 32), (3, 4, 16), (5, 5, 16)])
 def test_linear_few_tokens_single_launch(cfg, q, g):
     # ttq_linear with T <= 64 and r = 0 pre-scales inside its own kernels (one
     # kernel for T <= 4, split-K + reduction above): the output must equal
