@@ -31,6 +31,7 @@ MUTANTS = {
     "residual_sign": ("W16.astype(np.float64) - B.astype(np.float64) @ A.astype(np.float64)).astype(np.float16)",
                       "W16.astype(np.float64) + B.astype(np.float64) @ A.astype(np.float64)).astype(np.float16)"),
     "lowrank_term_dropped": ("Y = Y + (X64 @ A64.T) @ B64.T", "Y = Y"),
+    "slot_order_inverted": ("SLOT_CODE8 = (0, 2, 4, 6, 1, 3, 5, 7)", "SLOT_CODE8 = (0, 4, 1, 5, 2, 6, 3, 7)"),
 }
 
 
