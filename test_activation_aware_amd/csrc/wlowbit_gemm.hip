@@ -224,7 +224,9 @@ __device__ __forceinline__ void block_barrier() {
 // fragment feeds FM MFMAs, an input fragment FN.
 template <int Q, int G, typename TY, bool LOWRANK, int FM, bool RAWX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(FM == 8 ? 1 : 2, FM == 8 ? 1 : 2)))
+                          // FM = 4 aims at two workgroups per CU; the q = 5 and g = 16
+                          // forms need more than the 128 registers that allows
+                          amdgpu_waves_per_eu((FM == 8 || Q == 5 || G == 16) ? 1 : 2, FM == 8 ? 1 : 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
                          const _Float16* __restrict__ dvh,
                          const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
