@@ -20,6 +20,11 @@ MIS = ctypes.c_void_p((1 << 20) + 4)
 
 @pytest.fixture(scope="module")
 def lib():
+    # the host checks need the library itself (hipcc cross-compiles it without
+    # a GPU); build it once if nothing is built yet
+    if not os.path.exists(_capi.LIB_PATH):
+        from test_activation_aware_amd.build import build
+        build()
     return _capi.load()
 
 
