@@ -8,10 +8,12 @@ before the timed region.
 
 One step = the whole per-prompt hot path: ttq_prepare (column statistic +
 quantise/pack) then ttq_linear (the low-bit projection of the prompt).
-Reported: prefill k tokens/s at r = 0 (the value), the same at r = 16, the
-decode projection for T in {1, 16, 64} reusing the prefill quantisation,
-per-kernel times with their roofline fractions, and the CPU oracle on a
-bounded sample as a baseline.
+Reported: prefill k tokens/s at r = 0 (the value), the GEMM's own duration
+inside the timed steps against the fp16 matrix-core peak (roofline), the same
+step at r = 16, the decode projection for T in {1, 16, 64} reusing the
+prefill quantisation, per-kernel times with their roofline fractions, q/k/v
+sharing one prepare, the other code widths and group sizes, and the CPU
+oracle on one step of the workload as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
 """
@@ -159,37 +161,37 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
+    # HIP events on the launching stream around ttq_linear inside the timed
+    # steps: for fp16 input, T > 64 and r = 0 it launches exactly one kernel,
+    # the raw-input GEMM, so each pair brackets that kernel's run within the
+    # step (the host enqueues far ahead of the GPU, so no idle time falls
+    # between the events)
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for e0, e1 in evs:
+        layer.prepare(X)
+        e0.record(s)
+        layer.linear(X, out=Y)
+        e1.record(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed / args.steps * 1e3
     value = T * args.steps / elapsed / 1e3
+    gm_launches = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+    t_gm_step = sum(gm_launches) / len(gm_launches)
+    gm_pct = {f"us_p{k}": gm_launches[min(len(gm_launches) - 1, (len(gm_launches) * k) // 100)] * 1e6
+              for k in (10, 50, 90)}
 
-    # ---- the GEMM's own duration inside the step ----
-    # The step again, composed of the entry points ttq_prepare and ttq_linear
-    # run (for fp16 input and T > 64 the projection is ttq_wlowbit_gemm_raw on
-    # the raw input, same buffers and launch configuration), with HIP events
-    # on the launching stream around the GEMM: its average duration in the
-    # step's own power and cache state.
     gemm_flops = 2.0 * T * d * d_out
-    t_gm_step = None
-    if "kernels" in only:
-        s = torch.cuda.current_stream()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for e0, e1 in evs:
-            layer.prepare(X)
-            e0.record(s)
-            ttq.ttq_wlowbit_gemm_raw(X, layer.dinvsqrt16, layer.codes, layer.scales, layer.zeros, q, g, d_out,
-                                     out=Y)
-            e1.record(s)
-        torch.cuda.synchronize()
-        gm_launches = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
-        t_gm_step = sum(gm_launches) / len(gm_launches)
-        gm_pct = {f"us_p{k}": gm_launches[min(len(gm_launches) - 1, (len(gm_launches) * k) // 100)] * 1e6
-                  for k in (10, 50, 90)}
+    result["projection_k_tok_s"] = T / t_gm_step / 1e3
+    result["roofline"] = {"bound": "mfma", "achieved": gemm_flops / t_gm_step / 1e12,
+                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": gemm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                          "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm_raw",
+                          "launch_us": t_gm_step * 1e6}
 
     # ---- per-kernel times, back to back (same inputs, same launch configuration) ----
     kernels = {}
@@ -234,12 +236,6 @@ def main():
         t_dense = time_loop(lambda: torch.nn.functional.linear(X, Wd), n_k, torch)
         kernels["dense_fp16_gemm_context"] = {"us": t_dense * 1e6, "TFLOPs": gm_flops / t_dense / 1e12}
         del Wd
-        result["projection_k_tok_s"] = T / t_gm_step / 1e3
-        result["roofline"] = {"bound": "mfma", "achieved": gm_flops / t_gm_step / 1e12,
-                              "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                              "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm_raw",
-                              "launch_us": t_gm_step * 1e6}
         log(f"bench: kernels {json.dumps(kernels)}")
 
     # ---- a plain copy of known size: calibrates the byte counters ----
