@@ -162,6 +162,7 @@ ttq_status ttq_set_weight(ttq_handle* h, const void* W, void* stream);
 /* Per-prompt prefill step, prepare(X, W, q, g, alpha, lambda, p) with W and
  * the hyper-parameters bound in the handle:
  *   D, D^(-1/2) = colstats(X)  then  codes, scales, zeros = quantize(W_res, D).
+ * D^(-1/2) is written as fp32 followed by an fp16 copy (ttq_sizes).
  * X: device [T][ldx] of dtype xdt, 1 <= T <= T_max. */
 ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
                        int64_t ldx, void* stream);
@@ -171,7 +172,10 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
  * X: device [T][ldx] of dtype xdt; Y: device [T][ldy] of the same dtype,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
- * quantisation.  Runs ttq_prescale (fused with ttq_lowrank_z when r > 0:
+ * quantisation.  fp16 input with T > 64: ttq_lowrank_z into `workspace`
+ * when r > 0, then ttq_wlowbit_gemm_raw on X itself (D^(-1/2) applied to the
+ * dequantised weights, with the fp16 copy ttq_prepare wrote).  fp32 input,
+ * or r > 0 with T <= 64: ttq_prescale (fused with ttq_lowrank_z when r > 0:
  * one read of X) into `workspace`, then ttq_wlowbit_gemm.  With r = 0 and
  * few tokens the input is pre-scaled inside the projection kernels (the same
  * arithmetic): T <= 4, one kernel, `workspace` untouched; 4 < T <= 64, a
