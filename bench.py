@@ -44,7 +44,7 @@ def parse():
                     help="untimed steps run for this long before the warmup steps, so that the GPU's "
                          "clock and power state is the steady one of continuous work")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels,qkv,variants; "
+    ap.add_argument("--only", default="", help="comma list of parts to run: step,r16,decode,kernels,qkv,variants,configs; "
                     "'copy' (never by default) adds a plain device copy of 512 MiB, the reference "
                     "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
@@ -130,7 +130,8 @@ def main():
         print("bench.py: this implementation runs on one GPU only; the multi-GPU sharding of the path "
               "is described, not implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels", "qkv", "variants"}
+    only = set(filter(None, args.only.split(","))) or {"step", "r16", "decode", "kernels", "qkv", "variants",
+                                                        "configs"}
 
     import numpy as np
     import torch
@@ -297,6 +298,62 @@ def main():
             lv.close()
         log(f"bench: variants {json.dumps(variants)}")
 
+    # ---- the other layer shapes of the pages' models (OPT-125M, OPT-350M,
+    # Qwen3-1.7B, Qwen3-8B q_proj) with their own q, g, alpha and r: the same
+    # step, its kernels alone, and the projection's duration inside the
+    # steps (events around ttq_linear; for r = 16 and fp16 input it also
+    # launches the Z pass, reported on its own) ----
+    configs = None
+    if "configs" in only:
+        configs = {}
+        for cfg, r_c in ((1, 0), (2, 16), (3, 0), (4, 0), (4, 16)):
+            wc = wl.CONFIGS[cfg]
+            qc, gc = wc.q[0], wc.g[0]
+            Xc_np, Wc_np = wl.config_inputs(cfg)
+            Xc = torch.from_numpy(Xc_np).cuda()
+            Wc = torch.from_numpy(Wc_np).cuda()
+            Bc = Ac = None
+            if r_c:
+                Bc, Ac = ttq.svd_factors(Wc_np, r_c)
+            lc = ttq.TTQLinear(Wc, q=qc, g=gc, alpha=wc.alpha, lam=wc.lam, p=wc.p, r=r_c, T_max=wc.T, B=Bc, A=Ac)
+            Yc = torch.empty((wc.T, wc.d_out), dtype=Xc.dtype, device="cuda")
+
+            def step_c():
+                lc.prepare(Xc)
+                lc.linear(Xc, out=Yc)
+            settle(step_c, args.settle_ms / 4, torch)
+            evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            t0c = time.perf_counter()
+            for e0, e1 in evc:
+                lc.prepare(Xc)
+                e0.record(s)
+                lc.linear(Xc, out=Yc)
+                e1.record(s)
+            torch.cuda.synchronize()
+            t_c = (time.perf_counter() - t0c) / args.steps
+            t_lin = sum(e0.elapsed_time(e1) for e0, e1 in evc) / len(evc) * 1e-3
+            t_cs_c = time_graph(lambda: ttq.ttq_colstats(Xc, wc.p, wc.lam, wc.alpha, D=lc.D, dinvsqrt=lc.dinvsqrt,
+                                                         workspace=lc.workspace), 10, torch)
+            Wq = lc.wres if r_c else Wc
+            t_qp_c = time_graph(lambda: ttq.ttq_quantize_pack(Wq, lc.D, qc, gc, lc.codes, lc.scales, lc.zeros),
+                                10, torch)
+            fl = 2.0 * wc.T * wc.d * wc.d_out
+            xb = Xc.element_size()
+            cs_b = wc.T * wc.d * xb + 8 * wc.d
+            qp_b = 2 * wc.d_out * wc.d + 4 * wc.d + qc * wc.d_out * wc.d // 8 + 4 * wc.d_out * wc.d // gc
+            configs[f"{wc.name}_q{qc}g{gc}r{r_c}"] = {
+                "d": wc.d, "d_out": wc.d_out, "T": wc.T, "x_dtype": wc.x_dtype,
+                "k_tok_s": wc.T / t_c / 1e3, "ms_per_step": t_c * 1e3,
+                "colstats_us": t_cs_c * 1e6, "colstats_frac_hbm": cs_b / t_cs_c / 1e9 / HBM_PEAK_GBS,
+                "quantize_pack_us": t_qp_c * 1e6, "quantize_pack_frac_hbm": qp_b / t_qp_c / 1e9 / HBM_PEAK_GBS,
+                "linear_us_in_step": t_lin * 1e6,
+                "linear_frac_mfma_in_step": fl / t_lin / 1e12 / MFMA_F16_PEAK_TFLOPS}
+            lc.close()
+            del Xc, Wc, Yc
+        log(f"bench: configs {json.dumps(configs)}")
+
     # ---- q, k, v of one layer sharing one prepare (GQA: k, v have 1024 rows) ----
     qkv = None
     if "qkv" in only:
@@ -431,6 +488,8 @@ def main():
         out["qkv_shared_prepare"] = qkv
     if variants is not None:
         out["variants"] = variants
+    if configs is not None:
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
     layer.close()
 
