@@ -8,12 +8,15 @@
 // that consumes the pre-scaled input).
 //
 // CDNA4 design (gfx950, wave64, MFMA v_mfma_f32_32x32x16_f16):
-//   * A workgroup of 4 waves computes a 256 (output channels) x 32*FM
-//     (tokens) tile of Y^T; wave w owns channels [64w, 64w + 64) x all the
-//     tokens as 2 x FM fragments of 32x32.  The fp32 accumulators live in the
-//     accumulator registers (AGPRs).  Long prompts use FM = 8 (256 AGPRs, one
-//     workgroup per CU: each weight fragment dequantised once feeds 8 MFMAs);
-//     short ones FM = 4 (128 AGPRs, two workgroups per CU).
+//   * A workgroup computes a 256 (output channels) x 32*FM (tokens) tile of
+//     Y^T; each wave owns FN 32-row fragments x all the tokens, i.e. FN x FM
+//     fragments of 32x32 (FN = 2: 4 waves, FN = 1: 8 waves).  The fp32
+//     accumulators live in the accumulator registers (AGPRs).  Long prompts
+//     use FM = 8 (each weight fragment dequantised once feeds 8 MFMAs): with
+//     FN = 2 one workgroup per CU (256 AGPRs), with FN = 1 two waves per SIMD
+//     (128 AGPRs each, one wave's dequantisation and barrier wait overlapping
+//     the other's MFMAs); short ones FM = 4 (128 AGPRs, two workgroups per
+//     CU).
 //   * MFMA "A" = dequantised weight (rows = output channels), "B" = pre-scaled
 //     input (columns = tokens): accumulator lanes hold 4 consecutive output
 //     channels of one token, stored as 8 or 16 bytes.
@@ -66,10 +69,10 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));  // 4 words at a word boundary
 
-constexpr int kThreads = 256;
 constexpr int BN = 256;  // output channels per workgroup
 constexpr int BK = 64;   // input channels per step
-constexpr int FN = 2;    // 32-row fragments per wave
+// threads of a workgroup whose waves own FN 32-row fragments each
+constexpr int threads_for(int fn) { return 64 * (BN / (32 * fn)); }
 constexpr int kXcds = 8;
 
 template <int I>
@@ -222,11 +225,13 @@ __device__ __forceinline__ void block_barrier() {
 // fp16(D^(-1/2)) and each dequantised pair is multiplied by its two entries
 // (one packed multiply).  The weight side is the cheap side: a weight
 // fragment feeds FM MFMAs, an input fragment FN.
-template <int Q, int G, typename TY, bool LOWRANK, int FM, bool RAWX>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          // FM = 4 aims at two workgroups per CU; the q = 5 and g = 16
-                          // forms need more than the 128 registers that allows
-                          amdgpu_waves_per_eu((FM == 8 || Q == 5 || G == 16) ? 1 : 2, FM == 8 ? 1 : 2)))
+template <int Q, int G, typename TY, bool LOWRANK, int FM, bool RAWX, int FN>
+__global__ __attribute__((amdgpu_flat_work_group_size(threads_for(FN), threads_for(FN)),
+                          // FN = 2: FM = 4 aims at two workgroups per CU (the q = 5
+                          // and g = 16 forms need more than the 128 registers that
+                          // allows), FM = 8 takes one.  FN = 1: two waves per SIMD.
+                          amdgpu_waves_per_eu((FN == 2 && (FM == 8 || Q == 5 || G == 16)) ? 1 : 2,
+                                              (FN == 2 && FM == 8) ? 1 : 2)))
 void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
                          const _Float16* __restrict__ dvh,
                          const uint32_t* __restrict__ codes, const _Float16* __restrict__ scales,
@@ -234,6 +239,8 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
                          const float* __restrict__ Z, TY* __restrict__ Y, int64_t ldy, int tiles_n,
                          int tiles) {
   constexpr int BM = 32 * FM;                   // tokens per workgroup
+  constexpr int NW = BN / (32 * FN);            // waves
+  constexpr int kThreads = 64 * NW;
   constexpr int GPK = (G <= BK) ? BK / G : 1;  // groups per step
   constexpr int SW = 2 * Q;                     // code words per row per step
   constexpr int SZ = 8 * GPK * 32;              // scales (and zeros) per step
@@ -287,7 +294,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     h8 bfr[FN];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const int n = min(n0 + wave * 64 + i * 32 + l32, d_out - 1);
+      const int n = min(n0 + wave * 32 * FN + i * 32 + l32, d_out - 1);
       const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
       const float4 b0 = bp[0], b1 = bp[1];
       bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
@@ -362,17 +369,17 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(scales + (int64_t)ntile0 * ng * 32, (int64_t)(ntiles - ntile0) * ng * 64);
   const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(zeros + (int64_t)ntile0 * ng * 32, (int64_t)(ntiles - ntile0) * ng * 64);
   // X slot p -> row p / 8, physical chunk p % 8 holding logical chunk
-  // (p % 8) ^ swz(row); slot p + 256 j is row + 32 j with the same swizzle,
-  // so the per-lane offset is shared and j enters the scalar offset
+  // (p % 8) ^ swz(row); slot p + 64 NW j is row + 8 NW j with the same
+  // swizzle, so the per-lane offset is shared and j enters the scalar offset
   const int xrow = wave * 8 + (lane >> 3);
   const int xoff = (int)(xrow * ldxs * 2) + 16 * ((lane & 7) ^ swz(xrow));
-  const int xjstride = (int)(32 * ldxs * 2);
+  const int xjstride = (int)(8 * NW * ldxs * 2);
   // codes slot p -> row tile p / (16q), 16-byte piece p % (16q) of that
   // tile's contiguous step chunk
   int coff[CJ];
 #pragma unroll
   for (int j = 0; j < CJ; ++j) {
-    const int p = (wave + 4 * j) * 64 + lane;
+    const int p = (wave + NW * j) * 64 + lane;
     coff[j] = (int)(((p / (16 * Q)) * ctile + 4 * (p % (16 * Q))) * 4);
   }
   // scales (wave 0) and zeros (wave 1): slot p = 64 j + lane < SLOTS moves
@@ -389,10 +396,10 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   auto load_lds = [&](int kt, _Float16* xs, uint32_t* cs, _Float16* sz, _Float16* dv) {
 #pragma unroll
     for (int j = 0; j < XSL / kThreads; ++j)
-      lds_dma16(rs_x, xoff, kt * BK * 2 + j * xjstride, reinterpret_cast<char*>(xs) + 16 * (wave + 4 * j) * 64);
+      lds_dma16(rs_x, xoff, kt * BK * 2 + j * xjstride, reinterpret_cast<char*>(xs) + 16 * (wave + NW * j) * 64);
 #pragma unroll
     for (int j = 0; j < CJ; ++j)
-      if ((wave + 4 * j) * 64 < CSL) lds_dma16(rs_c, coff[j], kt * 32 * SW * 4, cs + 4 * (wave + 4 * j) * 64);
+      if ((wave + NW * j) * 64 < CSL) lds_dma16(rs_c, coff[j], kt * 32 * SW * 4, cs + 4 * (wave + NW * j) * 64);
 #pragma unroll
     for (int j = 0; j < SJ; ++j)
       if (wave < 2 && 64 * j + lane < SLOTS)
@@ -414,7 +421,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int gi = 0; gi < GPK; ++gi) {
-        const int tl = wave * 2 + i;
+        const int tl = wave * FN + i;
         const _Float16 sv = sz[(tl * GPK + gi) * 32 + l32];
         const _Float16 z = sz[SZ + (tl * GPK + gi) * 32 + l32];
         const _Float16 nzv = (_Float16)(-1024.0f) - z;  // -(1024 + z), exact
@@ -458,7 +465,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   auto read_codes = [&](const uint32_t* cs, CodeFrag<Q>* cf) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const uint32_t* rowp = cs + ((wave * 2 + i) * 32 + l32) * SW;
+      const uint32_t* rowp = cs + ((wave * FN + i) * 32 + l32) * SW;
       if constexpr (Q == 4) {
         cf[i].a = *reinterpret_cast<const u4v*>(rowp + 4 * hh);
       } else if constexpr (Q == 2) {
@@ -589,7 +596,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int n = n0 + wave * 64 + i * 32 + 8 * e4 + 4 * hh;
+        const int n = n0 + wave * 32 * FN + i * 32 + 8 * e4 + 4 * hh;
         if (n < d_out) {
           float v[4] = {acc[i][j][4 * e4 + 0], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
                         acc[i][j][4 * e4 + 3]};
@@ -616,13 +623,13 @@ struct GemmArgs {
   int64_t ldy;
 };
 
-template <int Q, int G, typename TY, bool LR, int FM, bool RAWX>
+template <int Q, int G, typename TY, bool LR, int FM, bool RAWX, int FN>
 hipError_t launch_fm(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = 32 * FM;
   const int tiles_n = (a.d_out + BN - 1) / BN;
   const int64_t tiles_m = (a.T + BM - 1) / BM;
   const int64_t tiles = tiles_n * tiles_m;
-  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR, FM, RAWX>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((wlowbit_gemm_kernel<Q, G, TY, LR, FM, RAWX, FN>), dim3((unsigned)tiles), dim3(threads_for(FN)), 0, s,
                      a.T, a.d_in, a.d_out, static_cast<const _Float16*>(a.X), a.ldx,
                      static_cast<const _Float16*>(a.dvh), a.codes, static_cast<const _Float16*>(a.scales),
                      static_cast<const _Float16*>(a.zeros), a.B, a.Z, static_cast<TY*>(a.Y), a.ldy, tiles_n,
@@ -630,12 +637,18 @@ hipError_t launch_fm(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256-token tiles once there are enough of them to give every CU a few
+// 256-token tiles once there are enough of them to give every CU a few.
+// With 256-token tiles, q = 2 or 4, g >= 32 and no rank-16 term, eight waves
+// of one fragment each (two per SIMD: one wave's dequantisation and barrier
+// wait overlap the other's MFMAs) measured 1-1.4 % faster than four waves
+// of two and compile without spills at 128 registers; the other forms keep
+// four waves.
 template <int Q, int G, typename TY, bool LR, bool RAWX>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles8 = ((a.d_out + BN - 1) / BN) * ((a.T + 255) / 256);
-  if (tiles8 >= 1024) return launch_fm<Q, G, TY, LR, 8, RAWX>(a, s);
-  return launch_fm<Q, G, TY, LR, 4, RAWX>(a, s);
+  constexpr int FN8 = (!LR && (Q == 2 || Q == 4) && G >= 32) ? 1 : 2;
+  if (tiles8 >= 1024) return launch_fm<Q, G, TY, LR, 8, RAWX, FN8>(a, s);
+  return launch_fm<Q, G, TY, LR, 4, RAWX, 2>(a, s);
 }
 
 template <int Q, int G, typename TY, bool RAWX>
