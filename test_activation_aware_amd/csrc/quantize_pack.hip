@@ -238,7 +238,9 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
         for (int i = 0; i < Q; ++i) word[i] = 0u;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
-          const uint32_t ci = (uint32_t)fminf(fmaxf(code(k), 0.0f), N);
+          // code(k) is in [0, N] on both paths below (the fast one by its
+          // error bound, the exact one by its clamp)
+          const uint32_t ci = (uint32_t)code(k);
           const int bit = Q * k;
           word[bit >> 5] |= ci << (bit & 31);
           if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
