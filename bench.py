@@ -289,12 +289,18 @@ def main():
                              10, torch)
             t_g = time_loop(lambda: ttq.ttq_wlowbit_gemm_raw(X, lv.dinvsqrt16, lv.codes, lv.scales, lv.zeros, qv,
                                                              gv, d_out, out=Y), 10, torch)
+            # one decode token reusing this quantisation (graph replay)
+            X1 = torch.from_numpy(wl.decode_inputs(w.cfg, 1, step=1)).cuda()
+            Y1 = torch.empty((1, d_out), dtype=torch.float16, device="cuda")
+            t_d1 = time_graph(lambda: lv.linear(X1, out=Y1), 20, torch)
+            d1_b = qv * d_out * d // 8 + 4 * d_out * d // gv + 2 * (d + d_out) + 4 * d
             qp_b = 2 * d_out * d + 4 * d + qv * d_out * d // 8 + 4 * d_out * d // gv
             variants[f"q{qv}_g{gv}"] = {
                 "k_tok_s": T / t_v / 1e3, "ms_per_step": t_v * 1e3,
                 "quantize_pack_us": t_q * 1e6, "quantize_pack_frac_hbm": qp_b / t_q / 1e9 / HBM_PEAK_GBS,
                 "gemm_us_back_to_back": t_g * 1e6,
-                "gemm_frac_mfma_back_to_back": gemm_flops / t_g / 1e12 / MFMA_F16_PEAK_TFLOPS}
+                "gemm_frac_mfma_back_to_back": gemm_flops / t_g / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                "decode_1_us": t_d1 * 1e6, "decode_1_frac_hbm": d1_b / t_d1 / 1e9 / HBM_PEAK_GBS}
             lv.close()
         log(f"bench: variants {json.dumps(variants)}")
 
