@@ -2,9 +2,11 @@
 
 The library is built in-tree, next to this file, so it travels with the
 source tree.  `python -m test_activation_aware_amd.build` or build() runs
-it; it always recompiles."""
+it; it always recompiles.  Each source is compiled to an object of its own
+(in parallel, under _build/), then the objects are linked."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import shutil
@@ -15,13 +17,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttq.so")
+OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -39,17 +41,34 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "api.cpp")]
 
 
-def build(verbose: bool = False) -> str:
+def _compile(src: str) -> tuple:
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in proc.stderr.splitlines() if "packed-fp32-ops" not in l)
+    return obj, proc.returncode, " ".join(cmd), errs
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(16, len(srcs), os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, srcs))
+    for obj, rc, cmd, errs in results:
+        if verbose:
+            print(cmd, flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) on {obj}:\n{errs}")
+        if verbose and errs.strip():
+            print(errs, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[r[0] for r in results]]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in proc.stderr.splitlines() if "packed-fp32-ops" not in l)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+        raise RuntimeError(f"link failed ({proc.returncode}):\n{proc.stderr}")
     os.replace(tmp, LIB)
     return LIB
 
