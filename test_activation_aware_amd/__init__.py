@@ -228,33 +228,47 @@ def ttq_wlowbit_gemm_raw(X, dinv16, codes, scales, zeros, q: int, g: int, d_out:
     return out
 
 
-def svd_factors(W, r: int, oversample: int = 16, power_iters: int = 6, seed: int = 0):
+def svd_factors(W, r: int):
     """Static rank-r factors B [d'][r], A [r][d] (fp32, balanced split
-    B = U_r S_r^(1/2), A = S_r^(1/2) V_r^T) of the weight, computed once on the
-    host as the pages prescribe (SVD-initialised static factors).
+    B = U_r S_r^(1/2), A = S_r^(1/2) V_r^T) of the top-r SVD of the weight,
+    computed once on the host (paper-daily.com deep reading of arXiv
+    2603.19296, section 2: factors initialised from the SVD of W and kept
+    static; gist.science French summary, section 2B).
 
-    Small weights use LAPACK's full SVD.  Large ones use a randomised range
-    finder with power iterations (Halko, Martinsson & Tropp, "Finding
-    structure with randomness", 2011, Algorithms 4.4 and 5.1) followed by an
-    exact SVD of the small projected matrix."""
+    Exact in fp64, not randomised: the r largest eigenpairs of the Gram
+    matrix of the weight's narrower side (LAPACK's relatively robust
+    representation solver through scipy, asked for those r only), then the
+    other side's singular vectors by one product, u_i = W v_i / s_i.  The
+    Gram matrix squares the singular values, so the leading ones, the only
+    ones used, keep fp64 accuracy.  At the Qwen3-32B q_proj shape
+    (8192 x 5120) this takes a few seconds; a randomised range finder with a
+    handful of power iterations does not converge there, because the
+    spectrum of a Gaussian weight is nearly flat at its top."""
+    import scipy.linalg
+
     W64 = np.asarray(W, dtype=np.float64)
     d_out, d_in = W64.shape
     if r == 0:
         return np.zeros((d_out, 0), np.float32), np.zeros((0, d_in), np.float32)
-    if min(d_out, d_in) <= 2048:
-        U, S, Vt = np.linalg.svd(W64, full_matrices=False)
+    if r < 0 or r > min(d_out, d_in):
+        raise ValueError(f"rank r={r} must be in [0, min(d_out, d_in) = {min(d_out, d_in)}]")
+    tall = d_out >= d_in
+    gram = W64.T @ W64 if tall else W64 @ W64.T
+    n = gram.shape[0]
+    ev, vecs = scipy.linalg.eigh(gram, subset_by_index=[n - r, n - 1], driver="evr")
+    ev, vecs = ev[::-1], vecs[:, ::-1]                     # descending
+    S = np.sqrt(np.maximum(ev, 0.0))
+    live = S > S[0] * 1e-12 if S[0] > 0 else np.zeros_like(S, dtype=bool)
+    inv = np.where(live, 1.0 / np.where(live, S, 1.0), 0.0)
+    if tall:
+        V = vecs
+        U = (W64 @ V) * inv[None, :]
     else:
-        rng = np.random.default_rng(seed)
-        k = r + oversample
-        Q, _ = np.linalg.qr(W64 @ rng.standard_normal((d_in, k)))
-        for _ in range(power_iters):
-            Qt, _ = np.linalg.qr(W64.T @ Q)
-            Q, _ = np.linalg.qr(W64 @ Qt)
-        Ub, S, Vt = np.linalg.svd(Q.T @ W64, full_matrices=False)
-        U = Q @ Ub
-    root = np.sqrt(S[:r])
-    return ((U[:, :r] * root[None, :]).astype(np.float32),
-            (root[:, None] * Vt[:r, :]).astype(np.float32))
+        U = vecs
+        V = (W64.T @ U) * inv[None, :]
+    root = np.where(live, np.sqrt(S), 0.0)
+    return ((U * root[None, :]).astype(np.float32),
+            (root[:, None] * V.T).astype(np.float32))
 
 
 class TTQLinear:
