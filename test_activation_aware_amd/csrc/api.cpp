@@ -51,6 +51,12 @@ ttq_status hip_status(hipError_t e, const char* what) {
   return fail(TTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Longest row stride (elements) of a projection input: the prefill kernel
+// addresses a 256-row input tile through a buffer resource whose byte
+// offsets are 32-bit (at most 0x7FFFFFF0), so 256 * ld * 2 bytes must stay
+// below 2^31.
+constexpr int64_t kMaxGemmLd = (int64_t(1) << 22) - 8;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 #define TTQ_NEED(ptr)                                                          \
@@ -71,7 +77,7 @@ ttq_status check_qgr(int32_t q, int32_t g, int32_t r) {
 ttq_status check_dims(int64_t d_in, int64_t d_out, int32_t g) {
   if (d_in <= 0 || d_in % 64 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld must be a positive multiple of 64", (long long)d_in);
   if (d_in % g != 0) return fail(TTQ_ERR_SHAPE, "d_in=%lld is not a multiple of g=%d", (long long)d_in, g);
-  if (d_in > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_in=%lld too large", (long long)d_in);
+  if (d_in > kMaxGemmLd) return fail(TTQ_ERR_SHAPE, "d_in=%lld too large (at most %lld)", (long long)d_in, (long long)kMaxGemmLd);
   if (d_out <= 0 || d_out % 32 != 0) return fail(TTQ_ERR_SHAPE, "d_out=%lld must be a positive multiple of 32", (long long)d_out);
   if (d_out > (1 << 24)) return fail(TTQ_ERR_SHAPE, "d_out=%lld too large", (long long)d_out);
   return TTQ_OK;
@@ -117,6 +123,13 @@ size_t linear_ws_bytes(int64_t T, int64_t d, int64_t d_out, int32_t r) {
   size_t b = xs_bytes(T, d) + (r > 0 ? (size_t)T * (size_t)r * 4 : 0);
   if (r == 0 && d >= 64 && d_out > 0) b = std::max(b, ttq::decode_splitk_ws_bytes(T, (int)d, (int)d_out));
   return b;
+}
+
+// the row stride of a projection input (X, or the pre-scaled Xs)
+ttq_status check_gemm_ld(int64_t ld, const char* name) {
+  if (ld > kMaxGemmLd)
+    return fail(TTQ_ERR_SHAPE, "%s=%lld too large (at most %lld elements)", name, (long long)ld, (long long)kMaxGemmLd);
+  return TTQ_OK;
 }
 
 ttq_status check_y(const void* Y, ttq_dtype ydt, int64_t T, int64_t d_out, int64_t ldy) {
@@ -308,7 +321,8 @@ ttq_status ttq_wlowbit_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t q, i
   if (s != TTQ_OK) return s;
   s = check_x(Xs, TTQ_F16, T, d_in, ldxs);
   if (s != TTQ_OK) return s;
-  if (ldxs > (int64_t(1) << 22)) return fail(TTQ_ERR_SHAPE, "ldxs=%lld too large", (long long)ldxs);
+  s = check_gemm_ld(ldxs, "ldxs");
+  if (s != TTQ_OK) return s;
   s = check_y(Y, ydt, T, d_out, ldy);
   if (s != TTQ_OK) return s;
   if (T == 0) return ok();
@@ -334,7 +348,8 @@ ttq_status ttq_wlowbit_gemm_raw(int64_t T, int32_t d_in, int32_t d_out, int32_t 
   if (s != TTQ_OK) return s;
   s = check_x(X, TTQ_F16, T, d_in, ldx);
   if (s != TTQ_OK) return s;
-  if (ldx > (int64_t(1) << 22)) return fail(TTQ_ERR_SHAPE, "ldx=%lld too large", (long long)ldx);
+  s = check_gemm_ld(ldx, "ldx");
+  if (s != TTQ_OK) return s;
   if (T <= ttq::kDecodeMaxT)
     return fail(TTQ_ERR_SHAPE, "T=%lld: the raw-input form is for T > %d (use ttq_linear)", (long long)T,
                 ttq::kDecodeMaxT);
@@ -381,12 +396,14 @@ size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx,
                       void* Y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
   if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
-  if (!h->prepared) return fail(TTQ_ERR_INVALID_ARG, "ttq_prepare has not been called on this handle");
   const ttq_config& c = h->cfg;
   ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
   if (s != TTQ_OK) return s;
+  s = check_gemm_ld(ldx, "ldx");
+  if (s != TTQ_OK) return s;
   s = check_y(Y, xdt, T, c.d_out, ldy);
   if (s != TTQ_OK) return s;
+  if (!h->prepared) return fail(TTQ_ERR_INVALID_ARG, "ttq_prepare has not been called on this handle");
   if (T == 0) return ok();
   TTQ_NEED(workspace);
   const size_t need = linear_ws_bytes(T, c.d_in, c.d_out, c.r);

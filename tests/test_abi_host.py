@@ -97,6 +97,8 @@ def test_query_sizes_cfg5(lib):
     (dict(d_out=6), _capi.TTQ_ERR_SHAPE),
     (dict(d_out=48), _capi.TTQ_ERR_SHAPE),
     (dict(d_out=0), _capi.TTQ_ERR_SHAPE),
+    (dict(d_in=1 << 22), _capi.TTQ_ERR_SHAPE),
+    (dict(d_in=(1 << 22) - 64), _capi.TTQ_OK),
     (dict(alpha=-0.1), _capi.TTQ_ERR_INVALID_ARG),
     (dict(alpha=float("nan")), _capi.TTQ_ERR_INVALID_ARG),
     (dict(p=0.0), _capi.TTQ_ERR_INVALID_ARG),
@@ -133,6 +135,9 @@ def test_null_and_alignment(lib):
         == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_wlowbit_gemm(0, 128, 64, 4, 32, 0, None, 128, None, None, None, None, None,
                                 None, 1, 64, None) == _capi.TTQ_OK
+    # input strides that a 256-row tile's 32-bit buffer offsets cannot reach
+    assert lib.ttq_wlowbit_gemm(300, 128, 64, 4, 32, 0, P, 1 << 22, P, P, P, None, None, P, 1, 64, None) \
+        == _capi.TTQ_ERR_SHAPE
     # raw-input gemm: prefill sizes only (T > 64), NULL D^(-1/2), misaligned X, odd ldx
     assert lib.ttq_wlowbit_gemm_raw(64, 128, 64, 4, 32, 0, P, 128, P, P, P, P, None, None, P, 64, None) \
         == _capi.TTQ_ERR_SHAPE
@@ -144,6 +149,8 @@ def test_null_and_alignment(lib):
         == _capi.TTQ_ERR_ALIGN
     assert lib.ttq_wlowbit_gemm_raw(65, 128, 64, 4, 32, 16, P, 128, P, P, P, P, P, None, P, 64, None) \
         == _capi.TTQ_ERR_NULL
+    assert lib.ttq_wlowbit_gemm_raw(300, 128, 64, 4, 32, 0, P, 1 << 22, P, P, P, P, None, None, P, 64, None) \
+        == _capi.TTQ_ERR_SHAPE
     # prescale: d not a multiple of 64, NULL dinvsqrt, misaligned Xs, T = 0 no-op
     assert lib.ttq_prescale(P, 1, 4, 96, 96, P, P, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_prescale(P, 1, 4, 128, 128, None, P, None) == _capi.TTQ_ERR_NULL
@@ -180,6 +187,10 @@ def test_handle_lifecycle_errors(lib):
         assert lib.ttq_prepare(h, P, 1, 17, 128, None) == _capi.TTQ_ERR_SHAPE   # > T_max
         assert lib.ttq_prepare(h, P, 1, 4, 64, None) == _capi.TTQ_ERR_SHAPE     # ldx < d
         assert lib.ttq_prepare(h, None, 1, 4, 128, None) == _capi.TTQ_ERR_NULL
+        # argument checks come before the handle's state: an input stride past
+        # what the projection's 32-bit tile offsets reach is a shape error
+        assert lib.ttq_linear(h, P, 1, 300, 1 << 22, P, 64, P, 1 << 30, None) == _capi.TTQ_ERR_SHAPE
+        assert lib.ttq_linear(h, P, 1, 4, (1 << 22) - 8, P, 64, P, 1 << 30, None) == _capi.TTQ_ERR_INVALID_ARG
     finally:
         lib.ttq_destroy(h)
     lib.ttq_destroy(None)
