@@ -51,7 +51,7 @@ def parse():
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qwen3_32b_qproj_q4g32r0.md")
-GEMM_SOURCE = os.path.join(ROOT, "test_activation_aware_amd", "csrc", "wlowbit_gemm.hip")
+GEMM_SOURCE = os.path.join(ROOT, "test_activation_aware_amd", "csrc", "wlowbit_gemm_impl.h")
 
 
 def gemm_traffic():
@@ -62,7 +62,7 @@ def gemm_traffic():
         src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
-    sha = re.search(r"source sha256 of wlowbit_gemm\.hip: ([0-9a-f]{64})", text)
+    sha = re.search(r"source sha256 of wlowbit_gemm_impl\.h: ([0-9a-f]{64})", text)
     val = re.search(r"traffic bytes per launch: (\d+)", text)
     if not sha or not val or sha.group(1) != src:
         return None
@@ -170,9 +170,11 @@ def main():
     s = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    evp = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
+    for ep, (e0, e1) in zip(evp, evs):
+        ep.record(s)
         layer.prepare(X)
         e0.record(s)
         layer.linear(X, out=Y)
@@ -181,6 +183,10 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed / args.steps * 1e3
     value = T * args.steps / elapsed / 1e3
+    # the prepare step (colstats + quantize_pack) inside the timed steps
+    t_prep_step = sum(ep.elapsed_time(e0) for ep, (e0, _) in zip(evp, evs)) / args.steps * 1e-3
+    result["prepare_k_tok_s"] = T / t_prep_step / 1e3
+    result["prepare_us_in_step"] = t_prep_step * 1e6
     gm_launches = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
     t_gm_step = sum(gm_launches) / len(gm_launches)
     gm_pct = {f"us_p{k}": gm_launches[min(len(gm_launches) - 1, (len(gm_launches) * k) // 100)] * 1e6
@@ -210,13 +216,38 @@ def main():
                                                           out=Y), n_k, torch)
         cs_bytes = T * d * 2 + 8 * d
         qp_bytes = 2 * d_out * d + 4 * d + q * d_out * d // 8 + 4 * d_out * d // g
+        # cold: every call reads a different copy of X (3 x 168 MB) or of W with
+        # its own outputs (6 x 110 MB), more than the 256 MB Infinity Cache and
+        # the 8 x 4 MB L2 hold, so each call streams its inputs from HBM
+        n_xc, n_wc = 3, 6
+        Xc = [X.clone() for _ in range(n_xc)]
+        Dc = [torch.empty_like(D) for _ in range(n_xc)]
+        Rc = [torch.empty_like(R) for _ in range(n_xc)]
+        wsc = [torch.empty_like(ws) for _ in range(n_xc)]
+        Wc = [W.clone() for _ in range(n_wc)]
+        outc = [(torch.empty_like(layer.codes), torch.empty_like(layer.scales), torch.empty_like(layer.zeros))
+                for _ in range(n_wc)]
+
+        def cs_cold():
+            for i in range(n_xc):
+                ttq.ttq_colstats(Xc[i], w.p, w.lam, w.alpha, D=Dc[i], dinvsqrt=Rc[i], workspace=wsc[i])
+
+        def qp_cold():
+            for i in range(n_wc):
+                ttq.ttq_quantize_pack(Wc[i], D, q, g, *outc[i])
+        t_cs_cold = time_graph(cs_cold, 4, torch) / n_xc
+        t_qp_cold = time_graph(qp_cold, 4, torch) / n_wc
+        del Xc, Dc, Rc, wsc, Wc, outc
         ps_bytes = 4 * T * d + 4 * d
         gm_flops = gemm_flops
         kernels = {
             "colstats": {"us": t_cs * 1e6, "GBs": cs_bytes / t_cs / 1e9,
-                         "frac_hbm": cs_bytes / t_cs / 1e9 / HBM_PEAK_GBS},
+                         "frac_hbm": cs_bytes / t_cs / 1e9 / HBM_PEAK_GBS,
+                         "us_cold": t_cs_cold * 1e6, "frac_hbm_cold": cs_bytes / t_cs_cold / 1e9 / HBM_PEAK_GBS},
             "quantize_pack": {"us": t_qp * 1e6, "GBs": qp_bytes / t_qp / 1e9,
-                              "frac_hbm": qp_bytes / t_qp / 1e9 / HBM_PEAK_GBS},
+                              "frac_hbm": qp_bytes / t_qp / 1e9 / HBM_PEAK_GBS,
+                              "us_cold": t_qp_cold * 1e6,
+                              "frac_hbm_cold": qp_bytes / t_qp_cold / 1e9 / HBM_PEAK_GBS},
             # the raw-input GEMM of the step (back to back), and the pre-scaled
             # pair it replaces for fp16 input (ttq_prescale + ttq_wlowbit_gemm,
             # still the path for fp32 input)
@@ -482,6 +513,8 @@ def main():
     if "roofline" in result:
         out["roofline"] = result["roofline"]
         out["projection_k_tok_s"] = result["projection_k_tok_s"]
+        out["prepare_k_tok_s"] = result["prepare_k_tok_s"]
+        out["prepare_us_in_step"] = result["prepare_us_in_step"]
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if r16 is not None:

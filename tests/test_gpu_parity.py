@@ -410,14 +410,23 @@ def _e2e(cfg, q, g, r, T=None, prompt=0, alpha=None, decode_T=()):
     check_quant_given_d(layer, Wq, q, g)
     c0, s0, z0 = oracle.quantize(Wq, D0, q, g)
     cg = oracle.codes_from_device(host(layer.codes).view(np.uint32), q, W.shape[0], W.shape[1])
-    agree = np.mean(cg == c0)
-    say(f"  code agreement with the oracle's own D: {agree:.6f}")
-    assert agree >= 0.999
+    flips = np.flatnonzero(cg != c0)
+    say(f"  codes differing from the oracle's own D: {flips.size} of {cg.size}")
+    # D agrees to 1e-5, so only codes whose scaled weight sits at a rounding
+    # tie of the oracle's quantiser may differ, and then by one level
+    assert flips.size <= 1e-4 * cg.size
+    assert np.all(np.abs(cg.reshape(-1)[flips].astype(int) - c0.reshape(-1)[flips].astype(int)) == 1)
     Y0 = oracle.linear(X, c0, s0, z0, D0, g, B, A)
-    if T >= 256 and W.shape[0] >= 256:
+    if T >= 256 and W.shape[0] >= 256 and flips.size == 0:
         check_y(Yg, Y0, "prefill")
     else:
-        assert rel_fro(Yg, Y0) <= Y_TOL
+        # a flipped code moves a whole output channel by one quantisation step
+        # times the input, so only the whole-output bound applies here; the
+        # per-row and per-tile bounds are checked with identical codes in the
+        # GEMM tests
+        e = rel_fro(Yg, Y0)
+        say(f"  prefill rel_fro={e:.3e}")
+        assert np.all(np.isfinite(Yg)) and e <= Y_TOL
     del Y0, Yg
     for Td in decode_T:
         Xn = wl.decode_inputs(cfg, Td, step=Td)
