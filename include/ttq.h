@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTQ_ABI_VERSION 3
+#define TTQ_ABI_VERSION 4
 
 typedef enum ttq_status {
   TTQ_OK = 0,
@@ -191,6 +191,25 @@ size_t ttq_linear_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_
 ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
                       int64_t ldx, void* Y, int64_t ldy, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* The whole per-prompt prefill step in one call: ttq_prepare(X) then
+ * ttq_linear(X) on the same prompt (paper-daily.com deep reading, section 6:
+ * the quantisation parameters are computed from the prompt at prefill; the
+ * projection of the prompt follows).  Writes D, D^(-1/2), codes, scales and
+ * zeros into the handle (as ttq_prepare) and Y = the projection of X (as
+ * ttq_linear).  With r = 16, fp16 input and T > 64 the column statistic and
+ * Z = X A^T come from one read of X (the form the two separate calls cannot
+ * use, since ttq_linear may see other inputs than the prompt); D is then
+ * summed in another fixed grouping than ttq_prepare's and may differ from it
+ * in the last bits (both within 1e-5 of the exact statistic).  Otherwise it
+ * is exactly ttq_prepare followed by ttq_linear.  workspace: device memory of
+ * at least ttq_prefill_workspace_bytes(T, d_in, d_out, r, xdt) bytes, owned
+ * by the caller; the handle's own workspace is used too (by the statistic of
+ * the unfused form).  1 <= T <= T_max; the input stride ldx must stay below
+ * 2^22 elements (as for ttq_linear). */
+size_t ttq_prefill_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_t r, ttq_dtype xdt);
+ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, void* Y,
+                       int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Sub-steps, exported so each kernel can be checked on its own ---- */
 

@@ -344,6 +344,26 @@ class TTQLinear:
                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()), "ttq_linear")
         return out
 
+    def prefill(self, X, out=None):
+        """The whole per-prompt step, prepare(X) then linear(X), in one call
+        (ttq_prefill: with r = 16 and fp16 input the statistic and A X come
+        from one read of X).  Returns Y [T][d_out]."""
+        torch = _torch()
+        x, dt, T, ldx = _x_args(X)
+        if X.shape[1] != self.d_in:
+            raise ValueError(f"X has {X.shape[1]} channels, the layer {self.d_in}")
+        out = torch.empty((T, self.d_out), dtype=X.dtype, device=X.device) if out is None else out
+        if out.dtype != X.dtype or out.dim() != 2 or out.stride(1) != 1 or out.shape != (T, self.d_out):
+            raise ValueError("out must be [T][d_out] with X's dtype and unit column stride")
+        ldy = out.stride(0) if T > 1 else self.d_out
+        need = load().ttq_prefill_workspace_bytes(T, self.d_in, self.d_out, self.r, dt)
+        if self.linear_workspace.numel() < need:
+            self.linear_workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        ws = self.linear_workspace
+        check(load().ttq_prefill(self._h, x, dt, T, ldx, ctypes.c_void_p(out.data_ptr()), ldy,
+                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()), "ttq_prefill")
+        return out
+
     def close(self) -> None:
         if getattr(self, "_h", None):
             load().ttq_destroy(self._h)

@@ -60,6 +60,8 @@ SIGNATURES = {
     "ttq_prepare": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P]),
     "ttq_linear_workspace_bytes": (_S, [_I64, _I32, _I32, _I32]),
     "ttq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, _S, _P]),
+    "ttq_prefill_workspace_bytes": (_S, [_I64, _I32, _I32, _I32, ctypes.c_int]),
+    "ttq_prefill": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, _S, _P]),
     "ttq_colstats_workspace_bytes": (_S, [_I64, _I64]),
     "ttq_colstats": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P, _S, _P]),
     "ttq_quantize_pack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
@@ -75,7 +77,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 3  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
+ABI_VERSION = 4  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
 
 
 def load() -> ctypes.CDLL:

@@ -132,6 +132,19 @@ ttq_status check_gemm_ld(int64_t ld, const char* name) {
   return TTQ_OK;
 }
 
+// ttq_prefill's workspace: with the rank-16 term and fp16 input of more than
+// kDecodeMaxT tokens, the fused statistic pass's partial sums, then Z (fp32
+// [T][r]); otherwise what ttq_linear needs (the handle's own workspace takes
+// the statistic)
+bool prefill_fused(int64_t T, int32_t r, ttq_dtype xdt) { return r > 0 && xdt == TTQ_F16 && T > ttq::kDecodeMaxT; }
+size_t fused_partial_bytes(int64_t T, int64_t d) {
+  return ((size_t)ttq::colstats_z_chunks(T) * (size_t)d * 4 + 255) & ~(size_t)255;
+}
+size_t prefill_ws_bytes(int64_t T, int64_t d, int64_t d_out, int32_t r, ttq_dtype xdt) {
+  if (prefill_fused(T, r, xdt)) return fused_partial_bytes(T, d) + (size_t)T * (size_t)r * 4;
+  return linear_ws_bytes(T, d, d_out, r);
+}
+
 ttq_status check_y(const void* Y, ttq_dtype ydt, int64_t T, int64_t d_out, int64_t ldy) {
   if (ydt != TTQ_F16 && ydt != TTQ_F32) return fail(TTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)ydt);
   if (ldy < d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%lld", (long long)ldy, (long long)d_out);
@@ -439,6 +452,48 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   if (e != hipSuccess) return hip_status(e, "prescale launch");
   e = ttq::launch_wlowbit_gemm(T, c.d_in, c.d_out, c.q, c.g, c.r, xs, c.d_in, h->buf.codes, h->buf.scales,
                                h->buf.zeros, h->buf.B, z, Y, xdt == TTQ_F32, ldy, st);
+  return hip_status(e, "wlowbit_gemm launch");
+}
+
+size_t ttq_prefill_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32_t r, ttq_dtype xdt) {
+  if (T < 0 || d_in <= 0 || d_out < 0 || r < 0 || (xdt != TTQ_F16 && xdt != TTQ_F32)) return 0;
+  return prefill_ws_bytes(T, d_in, d_out, r, xdt);
+}
+
+ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, void* Y, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
+  const ttq_config& c = h->cfg;
+  ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
+  if (s != TTQ_OK) return s;
+  s = check_gemm_ld(ldx, "ldx");
+  if (s != TTQ_OK) return s;
+  s = check_y(Y, xdt, T, c.d_out, ldy);
+  if (s != TTQ_OK) return s;
+  if (!h->weight_bound) return fail(TTQ_ERR_INVALID_ARG, "ttq_set_weight has not been called");
+  if (T < 1) return fail(TTQ_ERR_SHAPE, "T=%lld: prefill needs at least one token", (long long)T);
+  if (T > h->buf.T_max) return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld", (long long)T, (long long)h->buf.T_max);
+  TTQ_NEED(workspace);
+  const size_t need = prefill_ws_bytes(T, c.d_in, c.d_out, c.r, xdt);
+  if (workspace_bytes < need) return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (!prefill_fused(T, c.r, xdt)) {
+    // no rank-16 term to fuse: exactly ttq_prepare then ttq_linear
+    s = ttq_prepare(h, X, xdt, T, ldx, stream);
+    if (s != TTQ_OK) return s;
+    return ttq_linear(h, X, xdt, T, ldx, Y, ldy, workspace, workspace_bytes, stream);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* partial = static_cast<float*>(workspace);
+  float* z = reinterpret_cast<float*>(static_cast<char*>(workspace) + fused_partial_bytes(T, c.d_in));
+  hipError_t e = ttq::launch_colstats_z(X, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.A, h->buf.D,
+                                        h->buf.dinvsqrt, dinv16(h), partial, z, st);
+  if (e != hipSuccess) return hip_status(e, "colstats_z launch");
+  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes, h->buf.scales,
+                                h->buf.zeros, st);
+  if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
+  h->prepared = true;
+  e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
+                                    h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
   return hip_status(e, "wlowbit_gemm launch");
 }
 

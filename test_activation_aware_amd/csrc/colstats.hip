@@ -13,6 +13,21 @@
 //     of the chunk partials in fp64 and the slices are combined in a fixed
 //     order; then divide by T, add lambda, raise to alpha, round once to
 //     fp32.  No atomics: bitwise deterministic.
+//
+// With the rank-16 term (fp16 input), colstats_z_partial replaces pass 1 and
+// also forms Z = X A^T, the low-rank input of the projection
+// Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X) (paper-daily.com deep
+// reading, section 2: static low-rank factors applied to the raw input), from
+// the same read of X.  A workgroup owns 16 TG tokens and all d channels; its
+// 4 waves take 32-channel chunks round-robin.  Lane l holds token l % 16 and
+// channels 8 (l / 16) .. + 8 of a chunk, the operand layout of a 16x16x32
+// fp16 MFMA whose other operand is the matching slice of A^T (A split into
+// two fp16 parts, so Z keeps about 22 bits; the same operands, chunk order
+// and wave order as ttq_lowrank_z, so Z is the same bit for bit).  For the
+// statistic each lane squares its 8 channels over its TG tokens, and the 16
+// lanes that hold the same channels are added by a fixed tree of DPP row
+// rotations; one partial row per workgroup (16 TG tokens) goes to the same
+// finalize pass.
 #include "ttq_internal.h"
 
 namespace ttq {
@@ -91,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void colstats_partial(const TX* __restric
 }
 
 // 256 threads = 32 columns x 8 slices of the chunk list; slice w sums chunks
-// w, w+8, w+16, ... and the 8 slice sums are added in slice order.
+// w, w+8, w+16, ... in that order and the 8 slice sums are added in slice
+// order.
 __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict__ partial, int chunks,
                                                          int64_t d, int64_t T, double lambda,
                                                          double alpha, float* __restrict__ D,
@@ -99,17 +115,19 @@ __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict
                                                          _Float16* __restrict__ dinv16) {
   const int cx = threadIdx.x & 31, sl = threadIdx.x >> 5;
   const int64_t j = (int64_t)blockIdx.x * 32 + cx;
-  // all of this slice's chunk partials are requested at once (clamped,
-  // unconditional loads), then added in chunk order
+  // a slice requests kPerSlice of its chunk partials at once (clamped,
+  // unconditional loads), then adds them in chunk order
   constexpr int kPerSlice = kColstatsMaxChunks / 8;
   const int64_t jc = j < d ? j : d - 1;
-  float v[kPerSlice];
-#pragma unroll
-  for (int i = 0; i < kPerSlice; ++i) v[i] = partial[(int64_t)min(sl + 8 * i, chunks - 1) * d + jc];
   double s = 0.0;
+  for (int base = 0; base < chunks; base += 8 * kPerSlice) {
+    float v[kPerSlice];
 #pragma unroll
-  for (int i = 0; i < kPerSlice; ++i)
-    if (sl + 8 * i < chunks) s += (double)v[i];
+    for (int i = 0; i < kPerSlice; ++i) v[i] = partial[(int64_t)min(base + sl + 8 * i, chunks - 1) * d + jc];
+#pragma unroll
+    for (int i = 0; i < kPerSlice; ++i)
+      if (base + sl + 8 * i < chunks) s += (double)v[i];
+  }
   __shared__ double red[8][32];
   red[sl][cx] = s;
   __syncthreads();
@@ -123,6 +141,121 @@ __global__ __launch_bounds__(256) void colstats_finalize(const float* __restrict
   const float r = (float)(1.0 / sqrt((double)dj));
   dinvsqrt[j] = r;
   if (dinv16 != nullptr) dinv16[j] = (_Float16)r;  // fp16 copy, rounded to nearest even
+}
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRank = 16;   // rows of A
+constexpr int kTok = 16;    // tokens per MFMA group
+constexpr int kChunk = 32;  // channels per wave step
+
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), by rotations
+// of 8, 4, 2 and 1 lanes: every lane of the row ends with the row's total,
+// always added in the same order.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+  return v;
+}
+
+template <int PMODE, int TG>
+__global__ __launch_bounds__(256) void colstats_z_partial(int64_t T, int d, const _Float16* __restrict__ X,
+                                                          int64_t ldx, float p, const float* __restrict__ A,
+                                                          float* __restrict__ partial, float* __restrict__ Z) {
+  __shared__ f4 zred[kWaves][TG][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kb = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok * TG;
+  const _Float16* xr[TG];
+  float live[TG];  // 1 for tokens < T, 0 for the clamped rows past the end
+#pragma unroll
+  for (int g = 0; g < TG; ++g) {
+    const int64_t t = t0 + kTok * g + row;
+    xr[g] = X + (t < T ? t : T - 1) * ldx + 8 * kb;
+    live[g] = t < T ? 1.f : 0.f;
+  }
+  const float* ar = A + (int64_t)row * d + 8 * kb;  // A^T column j = row of A
+  float* prow = partial + (int64_t)blockIdx.x * d + 8 * kb;
+  f4 acc[TG];
+#pragma unroll
+  for (int g = 0; g < TG; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = d / kChunk;
+
+  auto chunk = [&](int k0, const h8 (&x)[TG], const float (&a)[8]) {
+    h8 ahi, alo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ahi[e] = (_Float16)a[e];
+      alo[e] = (_Float16)(a[e] - (float)ahi[e]);
+    }
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[g], ahi, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[g], alo, acc[g], 0, 0, 0);
+    }
+    float st[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = live[0] * powabs<PMODE>((float)x[0][e], p);
+#pragma unroll
+      for (int g = 1; g < TG; ++g) v += live[g] * powabs<PMODE>((float)x[g][e], p);
+      st[e] = row16_sum(v);
+    }
+    if (row == 0) {
+      float4* o = reinterpret_cast<float4*>(prow + k0);
+      o[0] = make_float4(st[0], st[1], st[2], st[3]);
+      o[1] = make_float4(st[4], st[5], st[6], st[7]);
+    }
+  };
+  auto load_chunk = [&](int k0, h8 (&x)[TG], float (&a)[8]) {
+#pragma unroll
+    for (int g = 0; g < TG; ++g) x[g] = *reinterpret_cast<const h8*>(xr[g] + k0);
+    const float4 a0 = reinterpret_cast<const float4*>(ar + k0)[0];
+    const float4 a1 = reinterpret_cast<const float4*>(ar + k0)[1];
+    a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+    a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+  };
+  // kU chunks per pass, all their loads requested before any is used; chunks
+  // are accumulated in the order c = wave, wave + 4, ... (as ttq_lowrank_z)
+  constexpr int kU = TG >= 4 ? 2 : 4;
+  int c = wave;
+  for (; c + 4 * (kU - 1) < nchunks; c += 4 * kU) {
+    h8 x[kU][TG];
+    float a[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load_chunk((c + 4 * u) * kChunk, x[u], a[u]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) chunk((c + 4 * u) * kChunk, x[u], a[u]);
+  }
+  for (; c < nchunks; c += 4) {
+    h8 x[TG];
+    float a[8];
+    load_chunk(c * kChunk, x, a);
+    chunk(c * kChunk, x, a);
+  }
+
+  // lane l holds Z[t0 + 16 g + 4 (l / 16) + i][l % 16], i = 0..3, for this
+  // wave's chunks; the 4 waves' partials are added in wave order
+#pragma unroll
+  for (int g = 0; g < TG; ++g) zred[wave][g][lane] = acc[g];
+  __syncthreads();
+  if (wave < TG) {
+    const int g = wave;
+    f4 s = zred[0][g][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f4 v = zred[w][g][lane];
+      s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tz = t0 + kTok * g + 4 * kb + i;
+      if (tz < T) Z[tz * kRank + row] = s[i];
+    }
+  }
 }
 
 template <typename TX>
@@ -154,6 +287,40 @@ int colstats_chunks(int64_t T) {
   if (c > kColstatsMaxChunks) c = kColstatsMaxChunks;
   if (c < 1) c = 1;
   return (int)c;
+}
+
+// tokens per workgroup of the fused pass: 64 while that leaves a workgroup
+// per CU, else 16 (the grouping of ttq_lowrank_z, so Z is the same)
+int colstats_z_tg(int64_t T) { return T >= 64 * 256 ? 4 : 1; }
+
+int colstats_z_chunks(int64_t T) {
+  const int64_t tok = (int64_t)kTok * colstats_z_tg(T);
+  return (int)((T + tok - 1) / tok);
+}
+
+hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float p, float lambda, float alpha,
+                             const float* A, float* D, float* dinvsqrt, void* dinv16, float* partial, float* Z,
+                             hipStream_t s) {
+  const int tg = colstats_z_tg(T);
+  const int chunks = colstats_z_chunks(T);
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const dim3 grid((unsigned)chunks), block(kThreads);
+#define TTQ_CZ(PM, TGV) hipLaunchKernelGGL((colstats_z_partial<PM, TGV>), grid, block, 0, s, T, d, x, ldx, p, A, partial, Z)
+  if (tg == 4) {
+    if (p == 2.0f) TTQ_CZ(2, 4);
+    else if (p == 1.0f) TTQ_CZ(1, 4);
+    else TTQ_CZ(0, 4);
+  } else {
+    if (p == 2.0f) TTQ_CZ(2, 1);
+    else if (p == 1.0f) TTQ_CZ(1, 1);
+    else TTQ_CZ(0, 1);
+  }
+#undef TTQ_CZ
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(colstats_finalize, dim3((unsigned)((d + 31) / 32)), dim3(256), 0, s, partial, chunks, (int64_t)d,
+                     T, (double)lambda, (double)alpha, D, dinvsqrt, static_cast<_Float16*>(dinv16));
+  return hipGetLastError();
 }
 
 hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx, float p,

@@ -15,6 +15,14 @@ hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int6
                            float p, float lambda, float alpha, float* D, float* dinvsqrt,
                            void* dinv16, float* partial, hipStream_t s);
 
+// The same statistic from fp16 X together with Z = X A^T (fp32 [T][16], A
+// fp32 [16][d], d a multiple of 64): one read of X.  The partial sums take
+// colstats_z_chunks(T) rows of d floats.
+int colstats_z_chunks(int64_t T);
+hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float p, float lambda, float alpha,
+                             const float* A, float* D, float* dinvsqrt, void* dinv16, float* partial, float* Z,
+                             hipStream_t s);
+
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W,
                                 const float* D, uint32_t* codes, void* scales, void* zeros,
                                 hipStream_t s);

@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 3
+    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 4
     for s in range(7):
         assert lib.ttq_status_string(s).decode().startswith("TTQ_")
     assert lib.ttq_status_string(99) == b"unknown ttq_status"
@@ -80,6 +80,18 @@ def test_query_sizes_cfg5(lib):
     # q = 5: five words per 32 codes
     assert lib.ttq_query_sizes(ctypes.byref(_cfg(q=5)), 16, ctypes.byref(sz)) == 0
     assert sz.codes_bytes == 8192 * 160 * 5 * 4
+
+
+def test_prefill_workspace_sizes(lib):
+    # rank 16, fp16 input, T > 64: the fused statistic's partial rows (16
+    # tokens per row below 16384 tokens, 64 from there) then Z
+    assert lib.ttq_prefill_workspace_bytes(16384, 5120, 8192, 16, 1) == 256 * 5120 * 4 + 16384 * 16 * 4
+    assert lib.ttq_prefill_workspace_bytes(1000, 4096, 4096, 16, 1) == \
+        ((63 * 4096 * 4 + 255) // 256) * 256 + 1000 * 16 * 4
+    # otherwise what ttq_linear needs
+    for T, r, dt in ((16384, 0, 1), (64, 16, 1), (2048, 16, 0), (5, 0, 1)):
+        assert lib.ttq_prefill_workspace_bytes(T, 5120, 8192, r, dt) == lib.ttq_linear_workspace_bytes(T, 5120, 8192, r)
+    assert lib.ttq_prefill_workspace_bytes(16, 5120, 8192, 0, 7) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -187,6 +199,12 @@ def test_handle_lifecycle_errors(lib):
         assert lib.ttq_prepare(h, P, 1, 17, 128, None) == _capi.TTQ_ERR_SHAPE   # > T_max
         assert lib.ttq_prepare(h, P, 1, 4, 64, None) == _capi.TTQ_ERR_SHAPE     # ldx < d
         assert lib.ttq_prepare(h, None, 1, 4, 128, None) == _capi.TTQ_ERR_NULL
+        # prefill: validation before anything is enqueued
+        assert lib.ttq_prefill(h, P, 1, 0, 128, P, 64, P, 1 << 30, None) == _capi.TTQ_ERR_SHAPE
+        assert lib.ttq_prefill(h, P, 1, 17, 128, P, 64, P, 1 << 30, None) == _capi.TTQ_ERR_SHAPE
+        assert lib.ttq_prefill(h, P, 1, 4, 128, P, 64, None, 1 << 30, None) == _capi.TTQ_ERR_NULL
+        assert lib.ttq_prefill(h, P, 1, 4, 128, P, 64, P, 4, None) == _capi.TTQ_ERR_SHAPE
+        assert lib.ttq_prefill(h, P, 1, 4, 128, MIS, 64, P, 1 << 30, None) == _capi.TTQ_ERR_ALIGN
         # argument checks come before the handle's state: an input stride past
         # what the projection's 32-bit tile offsets reach is a shape error
         assert lib.ttq_linear(h, P, 1, 300, 1 << 22, P, 64, P, 1 << 30, None) == _capi.TTQ_ERR_SHAPE

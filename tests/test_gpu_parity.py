@@ -386,7 +386,7 @@ def test_gemm_full_256_token_tiles(T, q, g, r, raw, d_out):
 # ---------------------------------------------------------------------------
 # end to end through the handle API (prepare once, project prefill + decode)
 # ---------------------------------------------------------------------------
-def _e2e(cfg, q, g, r, T=None, prompt=0, alpha=None, decode_T=()):
+def _e2e(cfg, q, g, r, T=None, prompt=0, alpha=None, decode_T=(), prefill=False):
     w = wl.CONFIGS[cfg]
     alpha = w.alpha if alpha is None else alpha
     X, W = cfg_inputs(cfg, T=T, prompt=prompt)
@@ -397,8 +397,11 @@ def _e2e(cfg, q, g, r, T=None, prompt=0, alpha=None, decode_T=()):
     B = host(layer.B) if r else None
     A = host(layer.A) if r else None
     Xd = dev(X)
-    layer.prepare(Xd)
-    Yg = host(layer.linear(Xd))
+    if prefill:   # ttq_prefill: the statistic (and Z for r = 16) from one read of X
+        Yg = host(layer.prefill(Xd))
+    else:
+        layer.prepare(Xd)
+        Yg = host(layer.linear(Xd))
     D0 = oracle.colstats(X, w.p, w.lam, alpha)
     Dg = host(layer.D)
     assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
@@ -459,6 +462,16 @@ def test_e2e_cfg4_prompts(prompt, r):
 @pytest.mark.parametrize("q,r", [(4, 0), (2, 0), (4, 16), (2, 16)])
 def test_e2e_cfg5_prefill_and_decode(q, r):
     _e2e(5, q, 32, r, decode_T=(1, 16, 64))
+
+
+@pytest.mark.parametrize("cfg,q,g,r,T", [
+    (5, 4, 32, 16, None), (5, 2, 32, 16, 16384 + 37), (4, 4, 32, 16, None), (4, 4, 32, 16, 1000),
+    (2, 3, 32, 16, None), (2, 3, 32, 16, 65), (2, 3, 32, 16, 40), (5, 4, 32, 0, 8192), (1, 4, 32, 0, None),
+])
+def test_e2e_prefill(cfg, q, g, r, T):
+    """ttq_prefill: prepare and projection of one prompt in one call (the
+    statistic and Z fused for r = 16, fp16 input, T > 64)."""
+    _e2e(cfg, q, g, r, T=T, prefill=True, decode_T=(1, 16) if cfg >= 2 else ())
 
 
 @pytest.mark.parametrize("cfg,g,r", [(3, 32, 0), (2, 64, 16)])
