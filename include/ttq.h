@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTQ_ABI_VERSION 4
+#define TTQ_ABI_VERSION 5
 
 typedef enum ttq_status {
   TTQ_OK = 0,
@@ -111,11 +111,22 @@ typedef struct ttq_sizes {
   size_t wres_bytes;      /* fp16   [d_out][d_in] W - B A (0 when r = 0) */
   size_t workspace_bytes; /* prepare: column-statistic partial sums      */
   size_t linear_workspace_bytes; /* ttq_linear on any T <= T_max          */
+  size_t wexp_bytes;      /* fp16   [d_out][d_in] effective weight W_hat  *
+                          * (optional buffer, see ttq_buffers.wexp)      */
 } ttq_sizes;
 
 /* Device buffers a handle works in (all caller-owned, see ttq_sizes).
  * B (fp32 [d_out][r]) and A (fp32 [r][d_in]) are the static factors; they
- * and wres are ignored when r = 0.  The workspace serves ttq_prepare only. */
+ * and wres are ignored when r = 0.  The workspace serves ttq_prepare only.
+ * wexp (optional, may be NULL): room for the effective fp16 weight
+ * W_hat[n][j] = fp16(fp16((c - z) s) * fp16(d_j^(-1/2))), the pages' closed
+ * form Q[(W - B A) D^(1/2)] D^(-1/2) (paper-daily.com deep reading, section
+ * 2) in exactly the fp16 values the low-bit projection kernel dequantises.
+ * With it, a prepare on an fp16 prompt of at least
+ * ttq_dense_min_tokens(d_out) tokens also writes W_hat, and projections of
+ * that many fp16 tokens run a dense fp16 GEMM on it: the dequantisation is
+ * done once per prompt instead of once per 256-token tile, with the same
+ * outputs bit for bit. */
 typedef struct ttq_buffers {
   uint32_t* codes;
   void* scales;
@@ -128,6 +139,7 @@ typedef struct ttq_buffers {
   float* workspace;
   int64_t T_max;
   size_t workspace_bytes;
+  void* wexp;
 } ttq_buffers;
 
 typedef struct ttq_handle ttq_handle;
@@ -211,6 +223,10 @@ size_t ttq_prefill_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32
 ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, void* Y,
                        int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Smallest number of fp16 tokens for which a handle with a wexp buffer takes
+ * the dense path (pure host; -1 for d_out <= 0). */
+int64_t ttq_dense_min_tokens(int32_t d_out);
+
 /* ---- Sub-steps, exported so each kernel can be checked on its own ---- */
 
 /* Column statistic: D[j] = fp32((mean_{t<T} |X[t][j]|^p + lambda)^alpha) and
@@ -273,6 +289,20 @@ ttq_status ttq_wlowbit_gemm_raw(int64_t T, int32_t d_in, int32_t d_out, int32_t 
                                 int32_t r, const void* X, int64_t ldx, const void* dinv16,
                                 const uint32_t* codes, const void* scales, const void* zeros,
                                 const float* B, const float* Z, void* Y, int64_t ldy, void* stream);
+
+/* The dense projection on an effective fp16 weight, the form ttq_linear runs
+ * for long fp16 prompts when the handle holds W_hat:
+ *   Y = W_hat X + B Z   (paper-daily.com deep reading, section 2: the closed
+ *   form Q[W D^(1/2)] D^(-1/2) applied to the raw input; B Z the static
+ *   rank-16 term, gist.science French summary, section 2B)
+ * X device fp16 [T][ldx] (ldx >= d_in, a multiple of 8, below 2^22); Wexp
+ * device fp16 [d_out][d_in]; B device fp32 [d_out][r] and Z device fp32
+ * [T][r] (ignored when r = 0); Y device fp16 [T][ldy].  fp16 operands on the
+ * matrix cores, fp32 accumulation in the same K order as ttq_wlowbit_gemm_raw
+ * (so on W_hat formed from that kernel's codes the outputs are identical).
+ * Any T >= 0. */
+ttq_status ttq_wexp_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t r, const void* X, int64_t ldx,
+                         const void* Wexp, const float* B, const float* Z, void* Y, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

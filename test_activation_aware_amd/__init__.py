@@ -34,7 +34,7 @@ from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 __all__ = [
     "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
     "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_wlowbit_gemm_raw",
-    "ttq_query_sizes",
+    "ttq_query_sizes", "ttq_dense_min_tokens", "ttq_wexp_gemm",
     "ttq_colstats_workspace_bytes", "ttq_linear_workspace_bytes", "ttq_abi_version", "code_shape",
     "group_shape",
 ]
@@ -228,6 +228,33 @@ def ttq_wlowbit_gemm_raw(X, dinv16, codes, scales, zeros, q: int, g: int, d_out:
     return out
 
 
+def ttq_dense_min_tokens(d_out: int) -> int:
+    return load().ttq_dense_min_tokens(d_out)
+
+
+def ttq_wexp_gemm(X, Wexp, B=None, Z=None, out=None):
+    """Y = W_hat X + B Z from an effective fp16 weight W_hat [d_out][d_in]
+    (the dense projection of long prompts); Y is fp16."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    if dt != TTQ_F16:
+        raise TypeError("X must be float16 for the dense projection")
+    d_out, d_in = Wexp.shape
+    if X.shape[1] != d_in:
+        raise ValueError("X and W_hat disagree on d_in")
+    r = 0 if B is None else B.shape[1]
+    if out is None:
+        out = torch.empty((T, d_out), dtype=torch.float16, device=X.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.dtype != torch.float16:
+        raise ValueError("out must be 2-D fp16 with unit column stride")
+    ldy = out.stride(0) if T > 1 else d_out
+    bp = _dev(B, "B", torch.float32) if r else None
+    zp = _dev(Z, "Z", torch.float32) if r else None
+    check(load().ttq_wexp_gemm(T, d_in, d_out, r, x, ldx, _dev(Wexp, "Wexp", torch.float16), bp, zp,
+                               ctypes.c_void_p(out.data_ptr()), ldy, _stream()), "ttq_wexp_gemm")
+    return out
+
+
 def svd_factors(W, r: int):
     """Static rank-r factors B [d'][r], A [r][d] (fp32, balanced split
     B = U_r S_r^(1/2), A = S_r^(1/2) V_r^T) of the top-r SVD of the weight,
@@ -276,7 +303,10 @@ class TTQLinear:
     the C library only records pointers to them."""
 
     def __init__(self, W, q: int = 4, g: int = 32, alpha: float = 0.5, lam: float = 0.4,
-                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None):
+                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None, expand=None):
+        """expand: give the handle room for the effective fp16 weight, so that
+        prompts of at least ttq_dense_min_tokens(d_out) fp16 tokens run the
+        dense projection (default: when T_max reaches that length)."""
         torch = _torch()
         if W.dtype != torch.float16 or W.device.type != "cuda" or not W.is_contiguous():
             raise ValueError("W must be a contiguous fp16 GPU tensor [d_out][d_in]")
@@ -299,6 +329,9 @@ class TTQLinear:
         self.dinvsqrt = self._dinv_buf[:4 * self.d_in].view(torch.float32)
         self.dinvsqrt16 = self._dinv_buf[4 * self.d_in:6 * self.d_in].view(torch.float16)
         self.workspace = torch.empty(max(1, sz.workspace_bytes // 4), dtype=torch.float32, device=dev)
+        if expand is None:
+            expand = T_max >= lib.ttq_dense_min_tokens(self.d_out)
+        self.wexp = torch.empty_like(W) if expand else None
         if r > 0:
             if B is None or A is None:
                 B, A = svd_factors(W.float().cpu().numpy(), r)
@@ -313,7 +346,7 @@ class TTQLinear:
         ptr = lambda t: None if t is None else t.data_ptr()
         self._bufs = _capi.ttq_buffers(ptr(self.codes), ptr(self.scales), ptr(self.zeros), ptr(self.D),
                                        ptr(self.dinvsqrt), ptr(self.wres), ptr(self.B), ptr(self.A),
-                                       ptr(self.workspace), T_max, self.workspace.numel() * 4)
+                                       ptr(self.workspace), T_max, self.workspace.numel() * 4, ptr(self.wexp))
         h = ctypes.c_void_p()
         check(lib.ttq_create(ctypes.byref(self._cfg), ctypes.byref(self._bufs), ctypes.byref(h)), "ttq_create")
         self._h = h

@@ -31,14 +31,14 @@ class ttq_config(ctypes.Structure):
 class ttq_sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "codes_bytes", "scales_bytes", "zeros_bytes", "d_bytes", "dinvsqrt_bytes",
-        "wres_bytes", "workspace_bytes", "linear_workspace_bytes")]
+        "wres_bytes", "workspace_bytes", "linear_workspace_bytes", "wexp_bytes")]
 
 
 class ttq_buffers(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
                 ("D", ctypes.c_void_p), ("dinvsqrt", ctypes.c_void_p), ("wres", ctypes.c_void_p),
                 ("B", ctypes.c_void_p), ("A", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("T_max", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("wexp", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -70,6 +70,8 @@ SIGNATURES = {
     "ttq_prescale": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
     "ttq_wlowbit_gemm": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
                                         _P, _P, _P, ctypes.c_int, _I64, _P]),
+    "ttq_dense_min_tokens": (_I64, [_I32]),
+    "ttq_wexp_gemm": (ctypes.c_int, [_I64, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _I64, _P]),
     "ttq_wlowbit_gemm_raw": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P,
                                             _P, _P, _P, _P, _I64, _P]),
 }
@@ -77,7 +79,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 4  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
+ABI_VERSION = 5  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
 
 
 def load() -> ctypes.CDLL:

@@ -15,12 +15,17 @@
 #include "../../include/ttq.h"
 #include "ttq_internal.h"
 
+#ifndef TTQ_DENSE_FORM
+#define TTQ_DENSE_FORM 0  // wave layout of the dense GEMM (launch_dense_gemm)
+#endif
+
 struct ttq_handle {
   ttq_config cfg;
   ttq_buffers buf;
   const void* wsrc;  // W (r = 0) or buf.wres (r > 0)
   bool weight_bound;
   bool prepared;
+  bool wexp_valid;  // the last prepare wrote the effective fp16 weight
 };
 
 namespace {
@@ -111,6 +116,20 @@ ttq_status check_x(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t l
   return TTQ_OK;
 }
 
+// Long prompts with fp16 input run the dense GEMM on the effective fp16
+// weight W_hat when the handle has a buffer for it: once the 256 x 256 tile
+// grid has at least kDenseMinTiles tiles (two workgroups per CU), forming
+// W_hat once costs less than dequantising every weight fragment again for
+// each token tile.
+constexpr int64_t kDenseMinTiles = 512;
+int64_t dense_min_tokens(int64_t d_out) {
+  const int64_t tn = (d_out + 255) / 256;
+  return 256 * ((kDenseMinTiles + tn - 1) / tn - 1) + 1;
+}
+bool use_dense(const ttq_handle* h, ttq_dtype xdt, int64_t T) {
+  return h->buf.wexp != nullptr && xdt == TTQ_F16 && T > ttq::kDecodeMaxT && T >= dense_min_tokens(h->cfg.d_out);
+}
+
 size_t colstats_ws_bytes(int64_t T, int64_t d) {
   return (size_t)ttq::colstats_chunks(T < 1 ? 1 : T) * (size_t)d * sizeof(float);
 }
@@ -191,6 +210,7 @@ ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out)
   out->d_bytes = din * 4;
   out->dinvsqrt_bytes = din * 4 + din * 2;  // fp32, then the fp16 copy
   out->wres_bytes = cfg->r > 0 ? dout * din * 2 : 0;
+  out->wexp_bytes = dout * din * 2;
   out->workspace_bytes = colstats_ws_bytes(T_max, cfg->d_in);
   // the largest need over 1 <= T <= T_max: the prefill form grows with T, the
   // split-K form with T up to kDecodeMaxT
@@ -214,6 +234,7 @@ ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle
   TTQ_NEED(bufs->workspace);
   if (bufs->workspace_bytes < sz.workspace_bytes)
     return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", bufs->workspace_bytes, sz.workspace_bytes);
+  if (bufs->wexp != nullptr && !aligned16(bufs->wexp)) return fail(TTQ_ERR_ALIGN, "bufs->wexp is not 16-byte aligned");
   if (cfg->r > 0) {
     TTQ_NEED(bufs->wres);
     TTQ_NEED(bufs->B);
@@ -226,6 +247,7 @@ ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle
   h->wsrc = nullptr;
   h->weight_bound = false;
   h->prepared = false;
+  h->wexp_valid = false;
   *out = h;
   return ok();
 }
@@ -279,7 +301,7 @@ ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g, 
   TTQ_NEED(codes);
   TTQ_NEED(scales);
   TTQ_NEED(zeros);
-  hipError_t e = ttq::launch_quantize_pack(d_out, d_in, q, g, W_src, D, codes, scales, zeros,
+  hipError_t e = ttq::launch_quantize_pack(d_out, d_in, q, g, W_src, D, codes, scales, zeros, nullptr, nullptr,
                                            static_cast<hipStream_t>(stream));
   return hip_status(e, "quantize_pack launch");
 }
@@ -394,10 +416,12 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.D,
                                       h->buf.dinvsqrt, dinv16(h), h->buf.workspace, st);
   if (e != hipSuccess) return hip_status(e, "colstats launch");
-  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes,
-                                h->buf.scales, h->buf.zeros, st);
+  const bool expand = use_dense(h, xdt, T);
+  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes, h->buf.scales,
+                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
   if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
   h->prepared = true;
+  h->wexp_valid = expand;
   return ok();
 }
 
@@ -438,6 +462,15 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   }
   void* xs = workspace;
   float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
+  if (h->wexp_valid && use_dense(h, xdt, T)) {
+    // a long prompt: the dense GEMM on the effective weight the last prepare
+    // formed (same results as the raw-input GEMM on the codes)
+    hipError_t e = hipSuccess;
+    if (c.r > 0) e = ttq::launch_prescale_z(T, c.d_in, X, false, ldx, h->buf.dinvsqrt, nullptr, h->buf.A, z, st);
+    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
+    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, TTQ_DENSE_FORM, st);
+    return hip_status(e, "dense_gemm launch");
+  }
   if (xdt == TTQ_F16 && T > ttq::kDecodeMaxT) {
     // fp16 input: the GEMM reads X itself, D^(-1/2) applied on the weight side
     hipError_t e = hipSuccess;
@@ -488,13 +521,46 @@ ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   hipError_t e = ttq::launch_colstats_z(X, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.A, h->buf.D,
                                         h->buf.dinvsqrt, dinv16(h), partial, z, st);
   if (e != hipSuccess) return hip_status(e, "colstats_z launch");
+  const bool expand = use_dense(h, xdt, T);
   e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes, h->buf.scales,
-                                h->buf.zeros, st);
+                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
   if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
   h->prepared = true;
-  e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
-                                    h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
-  return hip_status(e, "wlowbit_gemm launch");
+  h->wexp_valid = expand;
+  if (expand)
+    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, TTQ_DENSE_FORM, st);
+  else
+    e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
+                                      h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
+  return hip_status(e, "projection launch");
+}
+
+int64_t ttq_dense_min_tokens(int32_t d_out) {
+  if (d_out <= 0) return -1;
+  return std::max<int64_t>(dense_min_tokens(d_out), ttq::kDecodeMaxT + 1);
+}
+
+ttq_status ttq_wexp_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t r, const void* X, int64_t ldx,
+                         const void* Wexp, const float* B, const float* Z, void* Y, int64_t ldy, void* stream) {
+  ttq_status s = check_qgr(4, 32, r);
+  if (s != TTQ_OK) return s;
+  s = check_dims(d_in, d_out, 32);
+  if (s != TTQ_OK) return s;
+  s = check_x(X, TTQ_F16, T, d_in, ldx);
+  if (s != TTQ_OK) return s;
+  s = check_gemm_ld(ldx, "ldx");
+  if (s != TTQ_OK) return s;
+  s = check_y(Y, TTQ_F16, T, d_out, ldy);
+  if (s != TTQ_OK) return s;
+  if (T == 0) return ok();
+  TTQ_NEED(Wexp);
+  if (r > 0) {
+    TTQ_NEED(B);
+    TTQ_NEED(Z);
+  }
+  hipError_t e = ttq::launch_dense_gemm(T, d_in, d_out, r, X, ldx, Wexp, B, Z, Y, ldy, TTQ_DENSE_FORM,
+                                        static_cast<hipStream_t>(stream));
+  return hip_status(e, "dense_gemm launch");
 }
 
 }  // extern "C"

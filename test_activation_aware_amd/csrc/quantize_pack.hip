@@ -32,6 +32,15 @@
 // v = w * sq is one v_fma_mix_f32 (fp16 operand, fp32 arithmetic) and the
 // codes are packed bytewise with v_cvt_pk_u8_f32.
 //
+// Optionally (EXPAND) the workgroup also writes the effective fp16 weight of
+// its slab, W_hat[n][j] = fp16(fp16((c - z) s) * fp16(d_j^(-1/2))): the
+// pages' closed form Q[W D^(1/2)] D^(-1/2) (paper-daily.com deep reading,
+// section 2) with exactly the fp16 operations by which the fused projection
+// kernel dequantises a weight pair ((1024 + c) - (1024 + z) is c - z exactly,
+// then two packed fp16 multiplies, each rounded to nearest even), so a
+// dense GEMM on W_hat gives that kernel's outputs bit for bit.  The values
+// replace the slab in LDS and leave as coalesced 16-byte stores.
+//
 // Codes take a reciprocal fast path.  With rcp = v_rcp_f32(s) (relative
 // error at most 2^-23) and u = fma(v, rcp, z), |u - (v/s + z)| < 2^-18
 // because |v/s + z| <= N + 1.  Whenever u is more than 2^-16 away from every
@@ -99,10 +108,13 @@ __device__ __forceinline__ constexpr int step_pos(int h, int w) {
   else return Q * h + w;
 }
 
-template <int Q, int G>
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+template <int Q, int G, bool EXPAND>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const _Float16* __restrict__ W, const float* __restrict__ D, int d_in,
-    uint32_t* __restrict__ codes, _Float16* __restrict__ scales, _Float16* __restrict__ zeros) {
+    uint32_t* __restrict__ codes, _Float16* __restrict__ scales, _Float16* __restrict__ zeros,
+    const _Float16* __restrict__ dinv16, _Float16* __restrict__ wexp) {
   constexpr int LPG = G >= 32 ? G / 32 : 1;  // blocks per group
   constexpr int SG = G < 32 ? 32 / G : 1;     // groups inside one block (g = 16: 2)
   constexpr int CPG = 32 / SG;                // channels of the block per such group
@@ -248,18 +260,60 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       }
     };
     float far = 0.0f;  // largest distance of u from its rounded value
-    pack([&](int k) {
-      const int ch = slot_channel(k), sg = ch / CPG;
-      const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
-      const float c = rintf(u);
-      far = fmaxf(far, fabsf(u - c));
-      return c;
-    });
-    if (far > 0.5f - 0x1p-16f)  // rare: redo the block with the IEEE division
+    if constexpr (!EXPAND) {
       pack([&](int k) {
         const int ch = slot_channel(k), sg = ch / CPG;
-        return fminf(fmaxf(rintf(v[ch] / s[sg]) + zf[sg], 0.0f), N);
+        const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
+        const float c = rintf(u);
+        far = fmaxf(far, fabsf(u - c));
+        return c;
       });
+      if (far > 0.5f - 0x1p-16f)  // rare: redo the block with the IEEE division
+        pack([&](int k) {
+          const int ch = slot_channel(k), sg = ch / CPG;
+          return fminf(fmaxf(rintf(v[ch] / s[sg]) + zf[sg], 0.0f), N);
+        });
+    } else {
+      // the codes replace v in place (the rare exact path rereads the slab)
+#pragma unroll
+      for (int ch = 0; ch < 32; ++ch) {
+        const int sg = ch / CPG;
+        const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
+        v[ch] = rintf(u);
+        far = fmaxf(far, fabsf(u - v[ch]));
+      }
+      if (far > 0.5f - 0x1p-16f) {
+        const _Float16* src = &wt[r * kRowPitch + bl * 32];
+#pragma unroll
+        for (int ch = 0; ch < 32; ch += 2) {
+          const uint32_t raw = *reinterpret_cast<const uint32_t*>(src + ch);
+          const int sg = ch / CPG;
+          v[ch] = fminf(fmaxf(rintf(mul_lo(raw, sq[bl * 32 + ch]) / s[sg]) + zf[sg], 0.0f), N);
+          v[ch + 1] = fminf(fmaxf(rintf(mul_hi(raw, sq[bl * 32 + ch + 1]) / s[sg]) + zf[sg], 0.0f), N);
+        }
+      }
+      pack([&](int k) { return v[slot_channel(k)]; });
+    }
+    if constexpr (EXPAND) {
+      // W_hat of the block, in place of its slab in LDS (this thread's own
+      // row segment: no other thread reads it)
+      _Float16* dst16 = &wt[r * kRowPitch + bl * 32];
+#pragma unroll
+      for (int ch = 0; ch < 32; ch += 8) {
+        const uint4 dv = *reinterpret_cast<const uint4*>(dinv16 + c0 + bl * 32 + ch);
+        const uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sg = (ch + 2 * e) / CPG;
+          const h2 cz = {(_Float16)(v[ch + 2 * e] - zf[sg]), (_Float16)(v[ch + 2 * e + 1] - zf[sg])};
+          h2 wv = cz * h2{s16[sg], s16[sg]};
+          wv = wv * __builtin_bit_cast(h2, dvw[e]);
+          o[e] = __builtin_bit_cast(uint32_t, wv);
+        }
+        *reinterpret_cast<uint4*>(dst16 + ch) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
     uint32_t* dst = &outc[(ksl * 32 + r) * SW];
 #pragma unroll
     for (int w = 0; w < Q; ++w) dst[step_pos<Q>(h, w)] = word[w];
@@ -276,6 +330,17 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   }
   __syncthreads();
 
+  if constexpr (EXPAND) {
+    // W_hat rows of the slab, the load's piece order (one row per 16 lanes)
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int p = tid + i * kThreads;
+      const int row = p / kPR, col = (p % kPR) * 8;
+      if (col < width)
+        *reinterpret_cast<uint4*>(wexp + (int64_t)(nt * 32 + row) * d_in + c0 + col) =
+            *reinterpret_cast<const uint4*>(&wt[row * kRowPitch + col]);
+    }
+  }
   // codes: steps [c0/64, c0/64 + width/64) of tile nt are contiguous
   {
     const int words = (width / 64) * 32 * SW;
@@ -295,43 +360,44 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   }
 }
 
+template <int Q, bool EX>
+hipError_t launch_qe(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
+                     _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, hipStream_t s) {
+  dim3 grid((unsigned)((d_in + kCols - 1) / kCols), (unsigned)(d_out / 32));
+#define TTQ_QP(GV) hipLaunchKernelGGL((quantize_pack_kernel<Q, GV, EX>), grid, dim3(kThreads), 0, s, W, D, d_in, \
+                                      codes, scales, zeros, dinv16, wexp)
+  switch (g) {
+    case 16: TTQ_QP(16); break;
+    case 32: TTQ_QP(32); break;
+    case 64: TTQ_QP(64); break;
+    default: TTQ_QP(128); break;
+  }
+#undef TTQ_QP
+  return hipGetLastError();
+}
+
 template <int Q>
 hipError_t launch_q(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
-                    _Float16* scales, _Float16* zeros, hipStream_t s) {
-  dim3 grid((unsigned)((d_in + kCols - 1) / kCols), (unsigned)(d_out / 32));
-  switch (g) {
-    case 16:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 16>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
-                         scales, zeros);
-      break;
-    case 32:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 32>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
-                         scales, zeros);
-      break;
-    case 64:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 64>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
-                         scales, zeros);
-      break;
-    default:
-      hipLaunchKernelGGL((quantize_pack_kernel<Q, 128>), grid, dim3(kThreads), 0, s, W, D, d_in, codes,
-                         scales, zeros);
-      break;
-  }
-  return hipGetLastError();
+                    _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, hipStream_t s) {
+  if (wexp != nullptr) return launch_qe<Q, true>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, s);
+  return launch_qe<Q, false>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, s);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W, const float* D,
-                                uint32_t* codes, void* scales, void* zeros, hipStream_t s) {
+                                uint32_t* codes, void* scales, void* zeros, const void* dinv16, void* wexp,
+                                hipStream_t s) {
   const _Float16* w = static_cast<const _Float16*>(W);
   _Float16* sc = static_cast<_Float16*>(scales);
   _Float16* ze = static_cast<_Float16*>(zeros);
+  const _Float16* dv = static_cast<const _Float16*>(dinv16);
+  _Float16* we = static_cast<_Float16*>(wexp);
   switch (q) {
-    case 2: return launch_q<2>(d_out, d_in, g, w, D, codes, sc, ze, s);
-    case 3: return launch_q<3>(d_out, d_in, g, w, D, codes, sc, ze, s);
-    case 5: return launch_q<5>(d_out, d_in, g, w, D, codes, sc, ze, s);
-    default: return launch_q<4>(d_out, d_in, g, w, D, codes, sc, ze, s);
+    case 2: return launch_q<2>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
+    case 3: return launch_q<3>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
+    case 5: return launch_q<5>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
+    default: return launch_q<4>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
   }
 }
 

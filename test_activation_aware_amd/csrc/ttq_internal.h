@@ -23,9 +23,12 @@ hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float
                              const float* A, float* D, float* dinvsqrt, void* dinv16, float* partial, float* Z,
                              hipStream_t s);
 
+// Codes, scales and zeros of W D^(1/2); with wexp != NULL also the effective
+// fp16 weight W_hat = fp16(fp16((c - z) s) * dinv16) [d_out][d_in] (dinv16:
+// fp16 D^(-1/2) [d_in]).
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W,
                                 const float* D, uint32_t* codes, void* scales, void* zeros,
-                                hipStream_t s);
+                                const void* dinv16, void* wexp, hipStream_t s);
 
 hipError_t launch_residual(int d_out, int d_in, int r, const void* W, const float* B,
                            const float* A, void* W_res, hipStream_t s);
@@ -76,5 +79,12 @@ hipError_t launch_wlowbit_gemm_rawx(int64_t T, int d_in, int d_out, int q, int g
                                     int64_t ldx, const void* dinv16, const uint32_t* codes, const void* scales,
                                     const void* zeros, const float* B, const float* Z, void* Y, int64_t ldy,
                                     hipStream_t s);
+
+// The projection of a long prompt from the effective fp16 weight W_hat
+// [d_out][d_in] (written by the quantiser): Y = W_hat X + B Z, fp16 X and Y.
+// form selects the wave layout (0: 4 waves of 128 x 128, 1: 8 waves of
+// 128 x 64).  Same results as launch_wlowbit_gemm_rawx on the matching codes.
+hipError_t launch_dense_gemm(int64_t T, int d_in, int d_out, int r, const void* X, int64_t ldx, const void* Wt,
+                             const float* B, const float* Z, void* Y, int64_t ldy, int form, hipStream_t s);
 
 }  // namespace ttq

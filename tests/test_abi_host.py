@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 4
+    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 5
     for s in range(7):
         assert lib.ttq_status_string(s).decode().startswith("TTQ_")
     assert lib.ttq_status_string(99) == b"unknown ttq_status"

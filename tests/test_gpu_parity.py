@@ -99,6 +99,18 @@ def check_quant_given_d(layer, Wq, q, g):
     assert zg.view(np.uint16).tobytes() == z0.view(np.uint16).tobytes(), "zeros differ"
 
 
+def effective_weight16(codes, s16, z16, dinv16, g):
+    """The fp16 operand the projection kernels feed the matrix cores for each
+    weight: fp16(fp16((c - z) s) * fp16(d_j^(-1/2))), each product of two
+    fp16 values rounded once to nearest even (numpy forms the product of two
+    float16 values exactly in float32 and rounds it once to float16).  The
+    oracle's projection uses the exact (c - z) s d_j^(-1/2) instead; the two
+    roundings are inside the output tolerance."""
+    cz = (codes.astype(np.int32) - np.repeat(z16.astype(np.int32), g, axis=1)).astype(np.float16)
+    a = cz * np.repeat(s16.astype(np.float16), g, axis=1)
+    return a * np.asarray(dinv16, np.float16)[None, :]
+
+
 def oracle_dinvsqrt(D32):
     return (1.0 / np.sqrt(D32.astype(np.float64))).astype(np.float32)
 
@@ -381,6 +393,85 @@ def test_gemm_parity_full_cfg5(q, r, raw):
 ])
 def test_gemm_full_256_token_tiles(T, q, g, r, raw, d_out):
     _gemm_case(5, T, q, g, r, raw=raw, d_out=d_out, product_svd=True)
+
+
+# ---------------------------------------------------------------------------
+# the dense projection on the effective fp16 weight (long prompts)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,T,q,g,r,d_out", [
+    (5, 16384, 4, 32, 0, None), (5, 8741, 4, 32, 0, 8160), (5, 4097, 2, 64, 16, None), (5, 300, 3, 32, 0, None),
+    (4, 8192, 4, 32, 16, None), (3, 1000, 5, 128, 0, None), (2, 65, 3, 32, 16, None), (1, 1, 4, 16, 0, None),
+])
+def test_wexp_gemm_parity(cfg, T, q, g, r, d_out):
+    """ttq_wexp_gemm on W_hat formed from the oracle's codes: the oracle's Y
+    within the tolerance (every row and tile), and the raw-input low-bit
+    kernel's Y on the same codes bit for bit (same fp16 operands, same K
+    order)."""
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg, T=T, d_out=d_out)
+    X = X.astype(np.float16)
+    D = oracle.colstats(X, w.p, w.lam, w.alpha)
+    B = A = None
+    if r:
+        B, A = ttq.svd_factors(W, r)
+    Wq = oracle.residual(W, B, A) if r else W
+    c, s, z = oracle.quantize(Wq, D, q, g)
+    dv16 = oracle_dinvsqrt(D).astype(np.float16)
+    Wh = effective_weight16(c, s, z, dv16, g)
+    say(f"wexp gemm cfg={cfg} T={T} d_out={W.shape[0]} q={q} g={g} r={r}")
+    Xd = dev(X)
+    Zd = ttq.ttq_lowrank_z(Xd, dev(A)) if r else None
+    Yd = ttq.ttq_wexp_gemm(Xd, dev(Wh), B=dev(B) if r else None, Z=Zd)
+    Yg = host(Yd)
+    if T > 64:
+        Yf = host(ttq.ttq_wlowbit_gemm_raw(Xd, dev(dv16), dev(oracle.device_codes(c, q)),
+                                           dev(oracle.tile_groups(s)), dev(oracle.tile_groups(z)), q, g,
+                                           W.shape[0], B=dev(B) if r else None, Z=Zd))
+        assert Yg.tobytes() == Yf.tobytes(), "dense and low-bit projections differ"
+    del Yd, Xd
+    Y0 = oracle.linear(X, c, s, z, D, g, B, A)
+    if T >= 256 and W.shape[0] >= 256:
+        check_y(Yg, Y0)
+    else:
+        assert rel_fro(Yg, Y0) <= Y_TOL
+
+
+def test_handle_dense_path():
+    """A handle with room for W_hat (the default for long prompts): prepare on
+    the Qwen3-32B q_proj prompt writes W_hat equal to its definition from the
+    handle's own codes, scales, zeros and fp16 D^(-1/2); the projection runs
+    the dense GEMM and equals the low-bit kernel on the same codes bit for
+    bit; decode calls keep using the codes."""
+    w = wl.CONFIGS[5]
+    X, W = cfg_inputs(5)
+    T = X.shape[0]
+    assert T >= ttq.ttq_dense_min_tokens(W.shape[0])
+    layer = ttq.TTQLinear(dev(W), q=4, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+    assert layer.wexp is not None
+    Xd = dev(X)
+    layer.prepare(Xd)
+    Y = host(layer.linear(Xd))
+    cg = oracle.codes_from_device(host(layer.codes).view(np.uint32), 4, W.shape[0], W.shape[1])
+    sg = oracle.untile_groups(host(layer.scales), W.shape[0], W.shape[1] // 32)
+    zg = oracle.untile_groups(host(layer.zeros), W.shape[0], W.shape[1] // 32)
+    Wh = effective_weight16(cg, sg, zg, host(layer.dinvsqrt16), 32)
+    assert host(layer.wexp).view(np.uint16).tobytes() == Wh.view(np.uint16).tobytes(), "W_hat differs"
+    Yf = host(ttq.ttq_wlowbit_gemm_raw(Xd, layer.dinvsqrt16, layer.codes, layer.scales, layer.zeros, 4, 32,
+                                       W.shape[0]))
+    assert Y.tobytes() == Yf.tobytes()
+    # a shorter prompt in the same handle takes the low-bit kernel, and a
+    # projection longer than that prompt does not use a stale W_hat
+    Xs = dev(X[:1000])
+    layer.prepare(Xs)
+    Ys = host(layer.linear(Xs))
+    Yl = host(layer.linear(Xd))
+    Yr = host(ttq.ttq_wlowbit_gemm_raw(Xd, layer.dinvsqrt16, layer.codes, layer.scales, layer.zeros, 4, 32,
+                                       W.shape[0]))
+    assert Yl.tobytes() == Yr.tobytes()
+    Ysr = host(ttq.ttq_wlowbit_gemm_raw(Xs, layer.dinvsqrt16, layer.codes, layer.scales, layer.zeros, 4, 32,
+                                        W.shape[0]))
+    assert Ys.tobytes() == Ysr.tobytes()
+    layer.close()
 
 
 # ---------------------------------------------------------------------------
