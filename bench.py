@@ -51,22 +51,25 @@ def parse():
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qwen3_32b_qproj_q4g32r0.md")
-GEMM_SOURCE = os.path.join(ROOT, "test_activation_aware_amd", "csrc", "wlowbit_gemm_impl.h")
+CSRC = os.path.join(ROOT, "test_activation_aware_amd", "csrc")
+DENSE_SOURCE = os.path.join(CSRC, "dense_gemm.hip")          # the step's GEMM (long prompts)
+LOWBIT_SOURCE = os.path.join(CSRC, "wlowbit_gemm_impl.h")    # the low-bit GEMM on the codes
 
 
-def gemm_traffic():
-    """HBM bytes per GEMM launch from the committed counter runs, or None when
-    the GEMM source has changed since they were taken."""
+def gemm_traffic(source):
+    """HBM bytes per launch of the GEMM built from `source`, from the committed
+    counter runs, or None when that source has changed since they were
+    taken.  The profile records one line per kernel source:
+        - <file name> sha256 <hex>, traffic bytes per launch <n>"""
     try:
         text = open(TRAFFIC_PROFILE).read()
-        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        src = hashlib.sha256(open(source, "rb").read()).hexdigest()
     except OSError:
         return None
-    sha = re.search(r"source sha256 of wlowbit_gemm_impl\.h: ([0-9a-f]{64})", text)
-    val = re.search(r"traffic bytes per launch: (\d+)", text)
-    if not sha or not val or sha.group(1) != src:
+    m = re.search(re.escape(os.path.basename(source)) + r" sha256 ([0-9a-f]{64}), traffic bytes per launch (\d+)", text)
+    if not m or m.group(1) != src:
         return None
-    return int(val.group(1))
+    return int(m.group(2))
 
 
 def log(msg):
@@ -193,11 +196,15 @@ def main():
               for k in (10, 50, 90)}
 
     gemm_flops = 2.0 * T * d * d_out
+    dense = layer.wexp is not None and T >= ttq.ttq_dense_min_tokens(d_out)
     result["projection_k_tok_s"] = T / t_gm_step / 1e3
     result["roofline"] = {"bound": "mfma", "achieved": gemm_flops / t_gm_step / 1e12,
                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": gemm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                          "traffic": gemm_traffic(), "kernel": "ttq_wlowbit_gemm_raw",
+                          "traffic": gemm_traffic(DENSE_SOURCE if dense else LOWBIT_SOURCE),
+                          "kernel": ("dense_gemm_kernel: fp16 GEMM on the effective weight W_hat formed by "
+                                     "the prepare step (ttq_linear, long prompts)" if dense else
+                                     "wlowbit_gemm_kernel: low-bit GEMM on the packed codes (ttq_linear)"),
                           "launch_us": t_gm_step * 1e6}
 
     # ---- per-kernel times, back to back (same inputs, same launch configuration) ----
@@ -212,6 +219,9 @@ def main():
         t_ps = time_graph(lambda: ttq.ttq_prescale(X, R, out=Xs), n_k, torch)
         t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm_raw(X, layer.dinvsqrt16, layer.codes, layer.scales,
                                                           layer.zeros, q, g, d_out, out=Y), n_k, torch)
+        t_dg = time_loop(lambda: ttq.ttq_wexp_gemm(X, layer.wexp, out=Y), n_k, torch) if layer.wexp is not None \
+            else None
+        t_prep = time_graph(lambda: layer.prepare(X), n_k, torch)
         t_gm_pre = time_loop(lambda: ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out,
                                                           out=Y), n_k, torch)
         cs_bytes = T * d * 2 + 8 * d
@@ -253,13 +263,20 @@ def main():
             # still the path for fp32 input)
             "wlowbit_gemm_raw": {"us": t_gm * 1e6, "TFLOPs": gm_flops / t_gm / 1e12,
                                  "frac_mfma": gm_flops / t_gm / 1e12 / MFMA_F16_PEAK_TFLOPS},
+            # the whole prepare step (colstats, quantize_pack and, for a
+            # handle with room for it, the effective weight), graph replay
+            "prepare": {"us": t_prep * 1e6, "k_tok_s": T / t_prep / 1e3},
             "prescale": {"us": t_ps * 1e6, "GBs": ps_bytes / t_ps / 1e9,
                          "frac_hbm": ps_bytes / t_ps / 1e9 / HBM_PEAK_GBS},
             "wlowbit_gemm_prescaled": {"us": t_gm_pre * 1e6, "TFLOPs": gm_flops / t_gm_pre / 1e12,
                                        "frac_mfma": gm_flops / t_gm_pre / 1e12 / MFMA_F16_PEAK_TFLOPS},
-            "wlowbit_gemm_in_step": {"us": t_gm_step * 1e6, **gm_pct, "TFLOPs": gm_flops / t_gm_step / 1e12,
-                                     "frac_mfma": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS},
+            "gemm_in_step": {"us": t_gm_step * 1e6, **gm_pct, "TFLOPs": gm_flops / t_gm_step / 1e12,
+                             "frac_mfma": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                             "kernel": "dense_gemm_kernel" if dense else "wlowbit_gemm_kernel"},
         }
+        if t_dg is not None:
+            kernels["dense_gemm"] = {"us": t_dg * 1e6, "TFLOPs": gm_flops / t_dg / 1e12,
+                                     "frac_mfma": gm_flops / t_dg / 1e12 / MFMA_F16_PEAK_TFLOPS}
         # context: torch's dense fp16 GEMM (hipBLASLt) of the same shape on the
         # same activations, i.e. what an unquantised q_proj costs on this GPU
         Wd = torch.randn((d_out, d), dtype=torch.float16, device="cuda") * 0.01
@@ -290,8 +307,9 @@ def main():
         layer16 = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, B=B, A=A)
 
         def step16():
-            layer16.prepare(X)
-            layer16.linear(X, out=Y)
+            # ttq_prefill: with r = 16 the column statistic and Z = X A^T come
+            # from one read of X
+            layer16.prefill(X, out=Y)
         settle(step16, args.settle_ms, torch)
         for _ in range(args.warmup):
             step16()

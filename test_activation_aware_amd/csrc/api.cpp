@@ -15,10 +15,6 @@
 #include "../../include/ttq.h"
 #include "ttq_internal.h"
 
-#ifndef TTQ_DENSE_FORM
-#define TTQ_DENSE_FORM 0  // wave layout of the dense GEMM (launch_dense_gemm)
-#endif
-
 struct ttq_handle {
   ttq_config cfg;
   ttq_buffers buf;
@@ -468,7 +464,7 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
     hipError_t e = hipSuccess;
     if (c.r > 0) e = ttq::launch_prescale_z(T, c.d_in, X, false, ldx, h->buf.dinvsqrt, nullptr, h->buf.A, z, st);
     if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
-    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, TTQ_DENSE_FORM, st);
+    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, st);
     return hip_status(e, "dense_gemm launch");
   }
   if (xdt == TTQ_F16 && T > ttq::kDecodeMaxT) {
@@ -528,7 +524,7 @@ ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   h->prepared = true;
   h->wexp_valid = expand;
   if (expand)
-    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, TTQ_DENSE_FORM, st);
+    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, st);
   else
     e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
                                       h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
@@ -558,7 +554,7 @@ ttq_status ttq_wexp_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t r, cons
     TTQ_NEED(B);
     TTQ_NEED(Z);
   }
-  hipError_t e = ttq::launch_dense_gemm(T, d_in, d_out, r, X, ldx, Wexp, B, Z, Y, ldy, TTQ_DENSE_FORM,
+  hipError_t e = ttq::launch_dense_gemm(T, d_in, d_out, r, X, ldx, Wexp, B, Z, Y, ldy,
                                         static_cast<hipStream_t>(stream));
   return hip_status(e, "dense_gemm launch");
 }

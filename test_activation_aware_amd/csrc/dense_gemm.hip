@@ -11,16 +11,21 @@
 // order of the MFMAs is the same, so the outputs are the same bit for bit.
 //
 // CDNA4 design (gfx950, wave64, v_mfma_f32_32x32x16_f16):
-//   * Workgroup tile 256 output channels x 256 tokens of Y^T; the waves form
-//     a WN x WM grid, each owning (8 / WN) x (8 / WM) fragments of 32 x 32
-//     with fp32 accumulators in AGPRs (4 waves of 4 x 4 fragments: 256
-//     accumulator registers, one wave per SIMD; or 8 waves of 4 x 2).
-//   * K loop in 32-channel steps through a four-stage LDS ring (X tile and
-//     W_hat tile, 16 KB each per stage: 128 KB), filled only by direct-to-LDS
-//     buffer loads issued three steps ahead; one wait and one barrier per
-//     step.  64-byte tile rows carry an XOR swizzle of their four 16-byte
-//     chunks (chunk ^ (row / 4) % 4), applied through the source offsets, so
-//     the 16 lanes of one LDS read phase hit 16 distinct bank groups.
+//   * Workgroup tile 256 output channels x 256 tokens of Y^T; eight waves
+//     in a 2 x 4 grid, each owning 4 x 2 fragments of 32 x 32 (128 channels x
+//     64 tokens) with fp32 accumulators in AGPRs: 128 accumulator registers,
+//     two waves per SIMD, 6 LDS reads per 8 MFMAs.
+//   * K loop in 64-channel steps through two LDS stages (X tile and W_hat
+//     tile, 32 KB each per stage: 128 KB), filled only by direct-to-LDS
+//     buffer loads.  One wait and one barrier per step, before its last
+//     16-channel sub-step: by then every wave has read the step's operands
+//     out of its stage (the last sub-step's operands are already in
+//     registers), so the loads of step k + 2 go into that stage right after
+//     the barrier, while the last sub-step's MFMAs run and the next step's
+//     operands come from the other stage.  A load thus has one step to land.
+//     128-byte tile rows carry an XOR swizzle of their eight 16-byte chunks
+//     (chunk ^ (row / 2) % 8), applied through the source offsets, so the 16
+//     lanes of one LDS read phase hit 16 distinct bank groups.
 //   * MFMA A = W_hat fragment (rows = output channels), B = X fragment
 //     (columns = tokens); operands of the next sub-step are read from LDS
 //     under the current sub-step's MFMAs.
@@ -42,8 +47,7 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 256;  // output channels per workgroup
 constexpr int BM = 256;  // tokens per workgroup
-constexpr int BK = 32;   // input channels per step
-constexpr int NS = 4;    // LDS stages
+constexpr int BK = 64;   // input channels per step
 constexpr int kXcds = 8;
 
 template <int I>
@@ -83,9 +87,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, in
                                            voff, soff, 0, 0);
 }
 
-// XOR swizzle of the four 16-byte chunks of a 64-byte tile row: rows 4k ..
-// 4k + 3 share a 256-byte bank window, so the row group picks the permutation
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// XOR swizzle of the eight 16-byte chunks of a 128-byte tile row: rows 2k and
+// 2k + 1 share a 256-byte bank window, so the row pair picks the permutation
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
@@ -112,11 +116,10 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
   constexpr int FM = 8 / WM;                 // 32-token fragments per wave
   constexpr int SL = BM * BK * 2 / 16;       // 16-byte slots per tile and stage (X and W alike)
   constexpr int LPW = SL / kThreads;         // loads per wave per tile and step
-  constexpr int LSTEP = 2 * LPW;             // loads per wave per step
   static_assert(SL % kThreads == 0 && BM == BN, "slot split");
 
-  __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * BK], xs1[BM * BK], xs2[BM * BK], xs3[BM * BK];
-  __shared__ __attribute__((aligned(16))) _Float16 ws0[BN * BK], ws1[BN * BK], ws2[BN * BK], ws3[BN * BK];
+  __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * BK], xs1[BM * BK];
+  __shared__ __attribute__((aligned(16))) _Float16 ws0[BN * BK], ws1[BN * BK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,32 +188,26 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
   }
 
   auto xstage = [&](auto st) -> _Float16* {
-    constexpr int S = decltype(st)::value;
-    if constexpr (S == 0) return xs0;
-    else if constexpr (S == 1) return xs1;
-    else if constexpr (S == 2) return xs2;
-    else return xs3;
+    if constexpr (decltype(st)::value == 0) return xs0;
+    else return xs1;
   };
   auto wstage = [&](auto st) -> _Float16* {
-    constexpr int S = decltype(st)::value;
-    if constexpr (S == 0) return ws0;
-    else if constexpr (S == 1) return ws1;
-    else if constexpr (S == 2) return ws2;
-    else return ws3;
+    if constexpr (decltype(st)::value == 0) return ws0;
+    else return ws1;
   };
 
-  // Loads: slot p = 64 (wave + NW j) + lane -> tile row p / 4, physical chunk
-  // p % 4 holding logical chunk (p % 4) ^ swz(row); rows of slot j are row_0 +
-  // 16 NW j with the same swizzle, so the lane's offset is shared and j enters
+  // Loads: slot p = 64 (wave + NW j) + lane -> tile row p / 8, physical chunk
+  // p % 8 holding logical chunk (p % 8) ^ swz(row); rows of slot j are row_0 +
+  // 8 NW j with the same swizzle, so the lane's offset is shared and j enters
   // the scalar offset.
   const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(X + m0 * ldx, (T - m0) * ldx * 2);
   const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(Wt + (int64_t)n0 * d_in, (int64_t)(d_out - n0) * d_in * 2);
-  const int lrow = wave * 16 + (lane >> 2);
-  const int lchunk = (lane & 3) ^ swz(lrow);
+  const int lrow = wave * 8 + (lane >> 3);
+  const int lchunk = (lane & 7) ^ swz(lrow);
   const int xoff = (int)(lrow * ldx * 2) + 16 * lchunk;
   const int woff = lrow * d_in * 2 + 16 * lchunk;
-  const int xjstride = (int)(16 * NW * ldx * 2);
-  const int wjstride = 16 * NW * d_in * 2;
+  const int xjstride = (int)(8 * NW * ldx * 2);
+  const int wjstride = 8 * NW * d_in * 2;
 
   auto load_lds = [&](int kt, _Float16* xs, _Float16* ws) {
 #pragma unroll
@@ -230,64 +227,66 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
 
   h8 aop[2][FN], bop[2][FM];
 
-  // prologue: steps 0..2 requested; steps 0 and 1 landed
+  // prologue: steps 0 and 1 requested, step 0 landed, its first operands read
   load_lds(0, xs0, ws0);
-  if (ksteps > 1) load_lds(1, xs1, ws1);
-  if (ksteps > 2) load_lds(2, xs2, ws2);
-  if (ksteps > 2) wait_vmem<LSTEP>();
-  else wait_vmem<0>();
+  wait_vmem<0>();
+  load_lds(min(1, ksteps - 1), xs1, ws1);
   block_barrier();
 #pragma unroll
   for (int i = 0; i < FN; ++i) aop[0][i] = read_frag(ws0, wn * 32 * FN + 32 * i, 0);
 #pragma unroll
   for (int j = 0; j < FM; ++j) bop[0][j] = read_frag(xs0, wm * 32 * FM + 32 * j, 0);
 
+  // one K step on stage ST
   auto step = [&](auto stc, int kt) {
-    constexpr int ST = decltype(stc)::value;
-    constexpr int N1 = (ST + 1) % NS, N3 = (ST + 3) % NS;
-    const bool more = kt + 3 < ksteps;
-    if (more) load_lds(kt + 3, xstage(ic<N3>{}), wstage(ic<N3>{}));
-    unroll<2>([&](auto sc_) {
+    constexpr int ST = decltype(stc)::value, N1 = ST ^ 1;
+    unroll<4>([&](auto sc_) {
       constexpr int S = decltype(sc_)::value;
+      constexpr int P = S & 1, PN = P ^ 1;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (S == 3) {
+        // step kt + 1 has landed for every wave; nobody reads stage ST any
+        // more, so step kt + 2 goes there.  Unconditional (the last steps
+        // repeat step ksteps - 1 into a stage nobody reads again), so the
+        // loads share a block with the MFMAs they are scheduled between.
+        wait_vmem<0>();
+        block_barrier();
+        load_lds(min(kt + 2, ksteps - 1), xstage(ic<ST>{}), wstage(ic<ST>{}));
+      }
       // the next sub-step's operands (after the last step: stale, in-bounds
       // LDS data that is never used)
-      const _Float16* xsrc = (S == 0) ? xstage(ic<ST>{}) : xstage(ic<N1>{});
-      const _Float16* wsrc = (S == 0) ? wstage(ic<ST>{}) : wstage(ic<N1>{});
-      constexpr int SN = S ^ 1;
+      const _Float16* xsrc = (S < 3) ? xstage(ic<ST>{}) : xstage(ic<N1>{});
+      const _Float16* wsrc = (S < 3) ? wstage(ic<ST>{}) : wstage(ic<N1>{});
+      constexpr int SN = (S + 1) & 3;
 #pragma unroll
-      for (int i = 0; i < FN; ++i) aop[SN][i] = read_frag(wsrc, wn * 32 * FN + 32 * i, SN);
+      for (int i = 0; i < FN; ++i) aop[PN][i] = read_frag(wsrc, wn * 32 * FN + 32 * i, SN);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) bop[SN][j] = read_frag(xsrc, wm * 32 * FM + 32 * j, SN);
+      for (int j = 0; j < FM; ++j) bop[PN][j] = read_frag(xsrc, wm * 32 * FM + 32 * j, SN);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[S][i], bop[S][j], acc[i][j], 0, 0, 0);
-      // MFMAs interleaved with the LDS reads of the next operands
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[P][i], bop[P][j], acc[i][j], 0, 0, 0);
+      // the next sub-step's LDS reads first (a whole sub-step of MFMAs to
+      // land; issued between MFMAs they left the next sub-step waiting), then
+      // the MFMAs; after the barrier the step's direct-to-LDS loads go
+      // between them
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
 #pragma unroll
       for (int m = 0; m < FN * FM; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (m < FN + FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (S == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     });
-    // steps up to kt + 2 have landed for this wave (only kt + 3 may be in
-    // flight); after the barrier for every wave, and stage ST is free
-    if (more) wait_vmem<LSTEP>();
-    else wait_vmem<0>();
-    block_barrier();
   };
 
-  for (int kt = 0;; kt += 4) {
+  for (int kt = 0;; kt += 2) {
     step(ic<0>{}, kt);
     if (kt + 1 >= ksteps) break;
     step(ic<1>{}, kt + 1);
     if (kt + 2 >= ksteps) break;
-    step(ic<2>{}, kt + 2);
-    if (kt + 3 >= ksteps) break;
-    step(ic<3>{}, kt + 3);
-    if (kt + 4 >= ksteps) break;
   }
+  wait_vmem<0>();  // the repeated tail loads
 
   // epilogue: lane holds token l32 of each token fragment, channels
   // 8 (e / 4) + 4 hh + e % 4 of each row fragment
@@ -324,14 +323,11 @@ hipError_t launch_w(int64_t T, int d_in, int d_out, const void* X, int64_t ldx, 
 }  // namespace
 
 hipError_t launch_dense_gemm(int64_t T, int d_in, int d_out, int r, const void* X, int64_t ldx, const void* Wt,
-                             const float* B, const float* Z, void* Y, int64_t ldy, int form, hipStream_t s) {
+                             const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (form == 1) {
-    if (r > 0) return launch_w<2, 4, true>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
-    return launch_w<2, 4, false>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
-  }
-  if (r > 0) return launch_w<2, 2, true>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
-  return launch_w<2, 2, false>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
+  // eight waves of 128 channels x 64 tokens
+  if (r > 0) return launch_w<2, 4, true>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
+  return launch_w<2, 4, false>(T, d_in, d_out, X, ldx, Wt, B, Z, Y, ldy, s);
 }
 
 }  // namespace ttq

@@ -82,9 +82,8 @@ hipError_t launch_wlowbit_gemm_rawx(int64_t T, int d_in, int d_out, int q, int g
 
 // The projection of a long prompt from the effective fp16 weight W_hat
 // [d_out][d_in] (written by the quantiser): Y = W_hat X + B Z, fp16 X and Y.
-// form selects the wave layout (0: 4 waves of 128 x 128, 1: 8 waves of
-// 128 x 64).  Same results as launch_wlowbit_gemm_rawx on the matching codes.
+// Same results as launch_wlowbit_gemm_rawx on the matching codes.
 hipError_t launch_dense_gemm(int64_t T, int d_in, int d_out, int r, const void* X, int64_t ldx, const void* Wt,
-                             const float* B, const float* Z, void* Y, int64_t ldy, int form, hipStream_t s);
+                             const float* B, const float* Z, void* Y, int64_t ldy, hipStream_t s);
 
 }  // namespace ttq

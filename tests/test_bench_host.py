@@ -10,16 +10,16 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_traffic_matches_committed_kernel():
-    t = bench.gemm_traffic()
-    assert t is not None and t > 0
+def test_traffic_matches_committed_kernels():
+    for src in (bench.DENSE_SOURCE, bench.LOWBIT_SOURCE):
+        t = bench.gemm_traffic(src)
+        assert t is not None and t > 0, src
 
 
-def test_traffic_is_null_for_another_source(tmp_path, monkeypatch):
-    src = tmp_path / "k.hip"
-    src.write_text(open(bench.GEMM_SOURCE).read() + "\n// changed\n")
-    monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
-    assert bench.gemm_traffic() is None
+def test_traffic_is_null_for_another_source(tmp_path):
+    src = tmp_path / os.path.basename(bench.DENSE_SOURCE)
+    src.write_text(open(bench.DENSE_SOURCE).read() + "\n// changed\n")
+    assert bench.gemm_traffic(str(src)) is None
 
 
 def test_more_than_one_gpu_is_refused():
