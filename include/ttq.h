@@ -238,6 +238,20 @@ ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int6
                         float p, float lambda, float alpha, float* D, float* dinvsqrt,
                         float* workspace, size_t workspace_bytes, void* stream);
 
+/* The column statistic of ttq_colstats without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the partial sums
+ * live in a fixed array of the library on each GPU it runs on (8 MiB per
+ * GPU, held until the process ends; nothing is allocated or freed per call).
+ * Same arguments and results as ttq_colstats, bit for bit.  Limit: the
+ * partial sums of d channels must fit, i.e. d <= 16384 (TTQ_ERR_SHAPE
+ * otherwise).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race; a call's results
+ * never depend on what an earlier call left there.  The array of the device
+ * the stream belongs to is used (looked up on the first call per device). */
+ttq_status ttq_colstats_noalloc(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx, float p,
+                                float lambda, float alpha, float* D, float* dinvsqrt, void* stream);
+
 /* Quantise and pack W_src D^(1/2) (device fp16 [d_out][d_in], D device fp32
  * [d_in]) with the rules of the oracle: fp32 arithmetic, zero-inclusive
  * group range, fp16 scale rounded upward, z = rint(-mn/s),

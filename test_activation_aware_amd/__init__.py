@@ -32,7 +32,7 @@ from . import _capi
 from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 
 __all__ = [
-    "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_quantize_pack",
+    "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_colstats_noalloc", "ttq_quantize_pack",
     "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_wlowbit_gemm_raw",
     "ttq_query_sizes", "ttq_dense_min_tokens", "ttq_wexp_gemm",
     "ttq_colstats_workspace_bytes", "ttq_linear_workspace_bytes", "ttq_abi_version", "code_shape",
@@ -115,6 +115,20 @@ def ttq_colstats(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5, D=None
                               _dev(dinvsqrt, "dinvsqrt", torch.float32),
                               _dev(workspace, "workspace", torch.float32),
                               workspace.numel() * 4, _stream()), "ttq_colstats")
+    return D, dinvsqrt
+
+
+def ttq_colstats_noalloc(X, p: float = 2.0, lam: float = 0.4, alpha: float = 0.5, D=None, dinvsqrt=None):
+    """ttq_colstats with the partial sums in the library's fixed per-GPU
+    scratch (no workspace; for callers that cannot allocate, d <= 16384)."""
+    torch = _torch()
+    x, dt, T, ldx = _x_args(X)
+    d = X.shape[1]
+    D = torch.empty(d, dtype=torch.float32, device=X.device) if D is None else D
+    dinvsqrt = torch.empty(d, dtype=torch.float32, device=X.device) if dinvsqrt is None else dinvsqrt
+    check(load().ttq_colstats_noalloc(x, dt, T, d, ldx, p, lam, alpha, _dev(D, "D", torch.float32),
+                                      _dev(dinvsqrt, "dinvsqrt", torch.float32), _stream()),
+          "ttq_colstats_noalloc")
     return D, dinvsqrt
 
 

@@ -64,6 +64,7 @@ SIGNATURES = {
     "ttq_prefill": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, _S, _P]),
     "ttq_colstats_workspace_bytes": (_S, [_I64, _I64]),
     "ttq_colstats": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P, _S, _P]),
+    "ttq_colstats_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P]),
     "ttq_quantize_pack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "ttq_residual": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "ttq_lowrank_z": (ctypes.c_int, [_I64, _I32, _I32, _P, ctypes.c_int, _I64, _P, _P, _P]),

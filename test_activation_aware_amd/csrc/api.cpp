@@ -285,6 +285,24 @@ ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int6
   return hip_status(e, "colstats launch");
 }
 
+ttq_status ttq_colstats_noalloc(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx, float p,
+                                float lambda, float alpha, float* D, float* dinvsqrt, void* stream) {
+  if (d <= 0 || d % 8 != 0) return fail(TTQ_ERR_SHAPE, "d=%lld must be a positive multiple of 8", (long long)d);
+  ttq_status s = check_x(X, xdt, T, d, ldx);
+  if (s != TTQ_OK) return s;
+  if (T < 1) return fail(TTQ_ERR_SHAPE, "T=%lld: the statistic needs at least one token", (long long)T);
+  s = check_stats(alpha, lambda, p);
+  if (s != TTQ_OK) return s;
+  TTQ_NEED(D);
+  TTQ_NEED(dinvsqrt);
+  if (d > ttq::kColstatsScratchMaxD)
+    return fail(TTQ_ERR_SHAPE, "d=%lld: the fixed scratch (%zu bytes) holds the partial sums of at most %d channels",
+                (long long)d, ttq::kColstatsScratchBytes, ttq::kColstatsScratchMaxD);
+  hipError_t e = ttq::launch_colstats_noalloc(X, xdt == TTQ_F32, T, d, ldx, p, lambda, alpha, D, dinvsqrt,
+                                              static_cast<hipStream_t>(stream));
+  return hip_status(e, "colstats launch (fixed scratch)");
+}
+
 ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g, const void* W_src,
                              const float* D, uint32_t* codes, void* scales, void* zeros,
                              void* stream) {

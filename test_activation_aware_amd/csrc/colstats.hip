@@ -28,7 +28,17 @@
 // lanes that hold the same channels are added by a fixed tree of DPP row
 // rotations; one partial row per workgroup (16 TG tokens) goes to the same
 // finalize pass.
+#include <mutex>
+
 #include "ttq_internal.h"
+
+// Fixed scratch of ttq_colstats_noalloc, for callers that cannot allocate
+// device memory: the partial sums of the statistic, kColstatsScratchBytes on
+// every GPU the library runs on, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (in host code the name is a
+// host-side stand-in, not a device address): it looks up each device's
+// address once with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) float scratch[ttq::kColstatsScratchBytes / sizeof(float)];
 
 namespace ttq {
 
@@ -321,6 +331,57 @@ hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float
   hipLaunchKernelGGL(colstats_finalize, dim3((unsigned)((d + 31) / 32)), dim3(256), 0, s, partial, chunks, (int64_t)d,
                      T, (double)lambda, (double)alpha, D, dinvsqrt, static_cast<_Float16*>(dinv16));
   return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device the work of stream s runs on (the current device for the null
+// stream), and that device's address of `scratch`: looked up once per device
+// with that device current (the caller's current device is restored).
+hipError_t scratch_for_stream(hipStream_t s, float** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (s != nullptr) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return e;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_colstats_noalloc(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx, float p,
+                                   float lambda, float alpha, float* D, float* dinvsqrt, hipStream_t s) {
+  if ((size_t)colstats_chunks(T) * (size_t)d * sizeof(float) > kColstatsScratchBytes) return hipErrorInvalidValue;
+  float* partial = nullptr;
+  hipError_t e = scratch_for_stream(s, &partial);
+  if (e != hipSuccess) return e;
+  // every partial the finalize pass reads is written first by the partial
+  // pass of the same call: nothing needs clearing between calls
+  return launch_colstats(X, x_f32, T, d, ldx, p, lambda, alpha, D, dinvsqrt, nullptr, partial, s);
 }
 
 hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx, float p,

@@ -11,6 +11,16 @@ namespace ttq {
 // be NULL): an fp16 copy of D^(-1/2).
 constexpr int kColstatsMaxChunks = 128;      // row chunks of the partial pass
 int colstats_chunks(int64_t T);              // chunks used for T tokens
+
+// The same from a fixed per-device scratch array of the library (no
+// workspace argument, nothing allocated): kColstatsScratchBytes hold the
+// partial sums of up to kColstatsScratchMaxD channels at any T.
+// hipErrorInvalidValue when colstats_chunks(T) * d floats do not fit.  Calls that overlap on one
+// GPU share the array and race.
+constexpr int kColstatsScratchMaxD = 16384;
+constexpr size_t kColstatsScratchBytes = (size_t)kColstatsMaxChunks * kColstatsScratchMaxD * sizeof(float);  // 8 MiB
+hipError_t launch_colstats_noalloc(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx, float p,
+                                   float lambda, float alpha, float* D, float* dinvsqrt, hipStream_t s);
 hipError_t launch_colstats(const void* X, bool x_f32, int64_t T, int64_t d, int64_t ldx,
                            float p, float lambda, float alpha, float* D, float* dinvsqrt,
                            void* dinv16, float* partial, hipStream_t s);

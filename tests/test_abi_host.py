@@ -168,6 +168,11 @@ def test_null_and_alignment(lib):
     assert lib.ttq_prescale(P, 1, 4, 128, 128, None, P, None) == _capi.TTQ_ERR_NULL
     assert lib.ttq_prescale(P, 1, 4, 128, 128, P, MIS, None) == _capi.TTQ_ERR_ALIGN
     assert lib.ttq_prescale(None, 1, 0, 128, 128, None, None, None) == _capi.TTQ_OK
+    # the statistic with the fixed per-GPU scratch refuses channel counts past it
+    assert lib.ttq_colstats_noalloc(P, 1, 64, 16384 + 64, 16384 + 64, 2.0, 0.4, 0.5, P, P, None) \
+        == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_colstats_noalloc(P, 1, 0, 128, 128, 2.0, 0.4, 0.5, P, P, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_colstats_noalloc(P, 1, 4, 128, 128, 2.0, 0.4, 0.5, None, P, None) == _capi.TTQ_ERR_NULL
     # residual and lowrank_z are built for r = 16 only
     assert lib.ttq_residual(64, 128, 8, P, P, P, P, None) == _capi.TTQ_ERR_UNSUPPORTED
     assert lib.ttq_lowrank_z(4, 128, 0, P, 1, 128, P, P, None) == _capi.TTQ_ERR_INVALID_ARG
