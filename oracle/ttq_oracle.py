@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "colstats", "colstats_f64", "svd_factors", "residual", "quantize", "pack",
+    "colstats", "colstats_f64", "svd_factors", "svd_right_basis", "lowrank_refresh", "residual", "quantize", "pack",
     "unpack", "dequant", "linear", "linear_dense", "rtn_reference_levels",
     "tiled_code_index", "tile_codes", "untile_codes", "tile_groups", "untile_groups",
     "SLOT_CODE8", "interleave8", "deinterleave8", "device_codes", "codes_from_device",
@@ -97,6 +97,50 @@ def svd_factors(W, r: int):
     B = U[:, :r] * root[None, :]
     A = root[:, None] * Vt[:r, :]
     return B.astype(np.float32), A.astype(np.float32)
+
+
+def svd_right_basis(W, r: int) -> np.ndarray:
+    """The top-r right singular vectors of W as an orthonormal basis [d][r]
+    (fp64): the starting point of the online refresh below, at which it
+    reproduces the static factors of svd_factors."""
+    W64 = np.asarray(W).astype(np.float64)
+    _, _, Vt = np.linalg.svd(W64, full_matrices=False)
+    return Vt[:r].T.copy()
+
+
+def lowrank_refresh(W, D32, V):
+    """One online update of the rank-r factors for a prompt with statistic D.
+
+    [pd] §5 (limitations): the low-rank factors are initialised statically,
+    and an online PCA could update them at extra cost; [gfr] §2B: B, A stay
+    static to save cost, though adapting them online is possible.  The pages
+    fix no update rule.  Reading taken: the method weights the quantisation
+    error of W by the activation statistic ([pd] §2: the error of W D^(1/2)),
+    so the factors track the principal subspace of the activation-weighted
+    weight M = W D^(1/2), and "online PCA" is one step of subspace (block
+    power) iteration on M^T M per prompt, warm-started from the previous
+    right basis V (orthonormal [d][r]):
+
+        P  = M^T (M V)                 (d x r)
+        V' = orth(P)                   (QR, R with a positive diagonal)
+        B  = M V',   A = V'^T D^(-1/2) (so B A = M V' V'^T D^(-1/2))
+
+    and the residual W - B A is then quantised as usual.  Starting from the
+    top-r right singular vectors of W with D = 1 this reproduces the static
+    factors' product; repeated steps with a fixed D converge to the top-r
+    subspace of M, where |(W - B A) D^(1/2)|_F^2 is the Eckart-Young minimum
+    sum_{i > r} sigma_i(M)^2.  All in fp64; returns (V', B, A) as fp64."""
+    W64 = np.asarray(W).astype(np.float64)
+    sq = np.sqrt(np.asarray(D32).astype(np.float64))
+    V64 = np.asarray(V).astype(np.float64)
+    M = W64 * sq[None, :]
+    P = M.T @ (M @ V64)
+    Q, R = np.linalg.qr(P)
+    sign = np.where(np.diag(R) < 0, -1.0, 1.0)
+    Vn = Q * sign[None, :]
+    B = M @ Vn
+    A = Vn.T / sq[None, :]
+    return Vn, B, A
 
 
 def residual(W, B, A) -> np.ndarray:

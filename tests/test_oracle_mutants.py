@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "ttq_oracle.py")
 PINS = [os.path.join(ROOT, "tests", f) for f in (
     "test_oracle_colstats.py", "test_oracle_quantize.py", "test_oracle_pack.py",
-    "test_oracle_lowrank.py", "test_oracle_linear.py")]
+    "test_oracle_lowrank.py", "test_oracle_linear.py", "test_oracle_refresh.py")]
 
 MUTANTS = {
     "sum_not_mean": ("mean = powed.sum(axis=0) / T", "mean = powed.sum(axis=0)"),
@@ -32,6 +32,11 @@ MUTANTS = {
                       "W16.astype(np.float64) + B.astype(np.float64) @ A.astype(np.float64)).astype(np.float16)"),
     "lowrank_term_dropped": ("Y = Y + (X64 @ A64.T) @ B64.T", "Y = Y"),
     "slot_order_inverted": ("SLOT_CODE8 = (0, 2, 4, 6, 1, 3, 5, 7)", "SLOT_CODE8 = (0, 4, 1, 5, 2, 6, 3, 7)"),
+    "refresh_weight_by_d": ("    M = W64 * sq[None, :]\n    P = M.T", "    M = W64 * (sq * sq)[None, :]\n    P = M.T"),
+    "refresh_no_unweighting": ("    A = Vn.T / sq[None, :]", "    A = Vn.T.copy()"),
+    "refresh_unweighted_B": ("    B = M @ Vn\n", "    B = W64 @ Vn\n"),
+    "refresh_not_orthonormalised": ("    Vn = Q * sign[None, :]", "    Vn = P / np.linalg.norm(P, axis=0)[None, :]"),
+    "refresh_one_sided": ("    P = M.T @ (M @ V64)", "    P = M.T @ M[:, :V64.shape[1]]"),
 }
 
 
