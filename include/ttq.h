@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTQ_ABI_VERSION 5
+#define TTQ_ABI_VERSION 6
 
 typedef enum ttq_status {
   TTQ_OK = 0,
@@ -223,6 +223,25 @@ size_t ttq_prefill_workspace_bytes(int64_t T, int32_t d_in, int32_t d_out, int32
 ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, void* Y,
                        int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ttq_prepare with an online refresh of the rank-16 factors first (r = 16
+ * only).  The pages keep B, A static after their SVD initialisation and
+ * note that an online PCA could update them at extra cost (paper-daily.com
+ * deep reading, section 5, limitations; gist.science French summary,
+ * section 2B).  Here, per prompt: D = colstats(X); one subspace-iteration
+ * step of the right basis V toward the principal subspace of the
+ * activation-weighted weight W D^(1/2) (ttq_lowrank_refresh); B, A from it,
+ * written into the handle's B and A buffers (caller-owned device memory,
+ * rewritten in place); W_res = fp16(W - B A) into the handle's wres buffer;
+ * then quantize_pack as in ttq_prepare.  V: device fp32 [d_in][16], an
+ * orthonormal basis on the first call (the right singular vectors of W give
+ * back the static factors for a uniform D), updated in place.  workspace:
+ * device memory of at least ttq_lowrank_refresh_workspace_bytes(d_out, d_in,
+ * 16) bytes, owned by the caller.  The handle borrows W (ttq_set_weight):
+ * keep it alive and unchanged.  d_in must be a multiple of 128.  Must not
+ * overlap a ttq_linear on the same handle. */
+ttq_status ttq_prepare_refresh(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, float* V,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Smallest number of fp16 tokens for which a handle with a wexp buffer takes
  * the dense path (pure host; -1 for d_out <= 0). */
 int64_t ttq_dense_min_tokens(int32_t d_out);
@@ -251,6 +270,22 @@ ttq_status ttq_colstats(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int6
  * the stream belongs to is used (looked up on the first call per device). */
 ttq_status ttq_colstats_noalloc(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx, float p,
                                 float lambda, float alpha, float* D, float* dinvsqrt, void* stream);
+
+/* One online step of the rank-16 factors (the sub-step of
+ * ttq_prepare_refresh; same passages): with M = W D^(1/2),
+ *   P = M^T (M V),  V' = P R^-1 where R^T R = P^T P (Cholesky, fp64),
+ *   B = M V',  A = V'^T D^(-1/2)   (so B A = M V' V'^T D^(-1/2)).
+ * W device fp16 [d_out][d_in]; D device fp32 [d_in]; V device fp32
+ * [d_in][16] (orthonormal; replaced by V'); B device fp32 [d_out][16] and A
+ * device fp32 [16][d_in] (written).  Products of W with the basis run on the
+ * matrix cores with fp16 W and the fp32 basis split in two fp16 parts (about
+ * 22 bits) or in fp32; the 16 x 16 algebra in fp64.  A direction the weighted
+ * weight does not span gives zero columns of B and zero rows of A.  r must be
+ * 16, d_in a multiple of 128, d_out of 32.  workspace: at least
+ * ttq_lowrank_refresh_workspace_bytes(d_out, d_in, 16) bytes. */
+size_t ttq_lowrank_refresh_workspace_bytes(int32_t d_out, int32_t d_in, int32_t r);
+ttq_status ttq_lowrank_refresh(int32_t d_out, int32_t d_in, int32_t r, const void* W, const float* D, float* V,
+                               float* B, float* A, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Quantise and pack W_src D^(1/2) (device fp16 [d_out][d_in], D device fp32
  * [d_in]) with the rules of the oracle: fp32 arithmetic, zero-inclusive

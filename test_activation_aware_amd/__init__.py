@@ -34,7 +34,7 @@ from ._capi import TTQError, TTQ_F16, TTQ_F32, check, load
 __all__ = [
     "TTQError", "TTQLinear", "load", "svd_factors", "ttq_colstats", "ttq_colstats_noalloc", "ttq_quantize_pack",
     "ttq_residual", "ttq_lowrank_z", "ttq_prescale", "ttq_wlowbit_gemm", "ttq_wlowbit_gemm_raw",
-    "ttq_query_sizes", "ttq_dense_min_tokens", "ttq_wexp_gemm",
+    "ttq_query_sizes", "ttq_dense_min_tokens", "ttq_wexp_gemm", "ttq_lowrank_refresh",
     "ttq_colstats_workspace_bytes", "ttq_linear_workspace_bytes", "ttq_abi_version", "code_shape",
     "group_shape",
 ]
@@ -242,6 +242,26 @@ def ttq_wlowbit_gemm_raw(X, dinv16, codes, scales, zeros, q: int, g: int, d_out:
     return out
 
 
+def ttq_lowrank_refresh(W, D, V, B=None, A=None, workspace=None):
+    """One online step of the rank-16 factors: V (fp32 [d_in][16], updated in
+    place) advanced toward the principal subspace of W D^(1/2); returns the
+    new B [d_out][16] and A [16][d_in] (fp32)."""
+    torch = _torch()
+    d_out, d_in = W.shape
+    r = V.shape[1]
+    dev = W.device
+    B = torch.empty((d_out, r), dtype=torch.float32, device=dev) if B is None else B
+    A = torch.empty((r, d_in), dtype=torch.float32, device=dev) if A is None else A
+    nbytes = load().ttq_lowrank_refresh_workspace_bytes(d_out, d_in, r)
+    if workspace is None:
+        workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
+    check(load().ttq_lowrank_refresh(d_out, d_in, r, _dev(W, "W", torch.float16), _dev(D, "D", torch.float32),
+                                     _dev(V, "V", torch.float32), _dev(B, "B", torch.float32),
+                                     _dev(A, "A", torch.float32), ctypes.c_void_p(workspace.data_ptr()),
+                                     workspace.numel(), _stream()), "ttq_lowrank_refresh")
+    return B, A
+
+
 def ttq_dense_min_tokens(d_out: int) -> int:
     return load().ttq_dense_min_tokens(d_out)
 
@@ -269,7 +289,7 @@ def ttq_wexp_gemm(X, Wexp, B=None, Z=None, out=None):
     return out
 
 
-def svd_factors(W, r: int):
+def svd_factors(W, r: int, basis: bool = False):
     """Static rank-r factors B [d'][r], A [r][d] (fp32, balanced split
     B = U_r S_r^(1/2), A = S_r^(1/2) V_r^T) of the top-r SVD of the weight,
     computed once on the host (paper-daily.com deep reading of arXiv
@@ -284,13 +304,18 @@ def svd_factors(W, r: int):
     ones used, keep fp64 accuracy.  At the Qwen3-32B q_proj shape
     (8192 x 5120) this takes a few seconds; a randomised range finder with a
     handful of power iterations does not converge there, because the
-    spectrum of a Gaussian weight is nearly flat at its top."""
+    spectrum of a Gaussian weight is nearly flat at its top.
+
+    basis=True also returns the orthonormal right basis V [d_in][r] (fp32):
+    the starting point of the online refresh (ttq_lowrank_refresh), which
+    with a uniform statistic gives back these factors' product."""
     import scipy.linalg
 
     W64 = np.asarray(W, dtype=np.float64)
     d_out, d_in = W64.shape
     if r == 0:
-        return np.zeros((d_out, 0), np.float32), np.zeros((0, d_in), np.float32)
+        empty = (np.zeros((d_out, 0), np.float32), np.zeros((0, d_in), np.float32))
+        return empty + (np.zeros((d_in, 0), np.float32),) if basis else empty
     if r < 0 or r > min(d_out, d_in):
         raise ValueError(f"rank r={r} must be in [0, min(d_out, d_in) = {min(d_out, d_in)}]")
     tall = d_out >= d_in
@@ -308,8 +333,8 @@ def svd_factors(W, r: int):
         U = vecs
         V = (W64.T @ U) * inv[None, :]
     root = np.where(live, np.sqrt(S), 0.0)
-    return ((U * root[None, :]).astype(np.float32),
-            (root[:, None] * V.T).astype(np.float32))
+    factors = ((U * root[None, :]).astype(np.float32), (root[:, None] * V.T).astype(np.float32))
+    return factors + (V.astype(np.float32),) if basis else factors
 
 
 class TTQLinear:
@@ -317,10 +342,13 @@ class TTQLinear:
     the C library only records pointers to them."""
 
     def __init__(self, W, q: int = 4, g: int = 32, alpha: float = 0.5, lam: float = 0.4,
-                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None, expand=None):
+                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None, expand=None,
+                 refresh: bool = False):
         """expand: give the handle room for the effective fp16 weight, so that
         prompts of at least ttq_dense_min_tokens(d_out) fp16 tokens run the
-        dense projection (default: when T_max reaches that length)."""
+        dense projection (default: when T_max reaches that length).
+        refresh (r = 16): prepare() refreshes the rank-16 factors online for
+        each prompt (ttq_prepare_refresh), starting from the SVD basis."""
         torch = _torch()
         if W.dtype != torch.float16 or W.device.type != "cuda" or not W.is_contiguous():
             raise ValueError("W must be a contiguous fp16 GPU tensor [d_out][d_in]")
@@ -346,8 +374,16 @@ class TTQLinear:
         if expand is None:
             expand = T_max >= lib.ttq_dense_min_tokens(self.d_out)
         self.wexp = torch.empty_like(W) if expand else None
+        self.V = self.refresh_workspace = None
+        if refresh and r != 16:
+            raise ValueError("the online refresh is built for r = 16")
         if r > 0:
-            if B is None or A is None:
+            if refresh:
+                B, A, V = svd_factors(W.float().cpu().numpy(), r, basis=True)
+                self.V = torch.as_tensor(np.ascontiguousarray(V), dtype=torch.float32).to(dev)
+                nbytes = lib.ttq_lowrank_refresh_workspace_bytes(self.d_out, self.d_in, r)
+                self.refresh_workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
+            elif B is None or A is None:
                 B, A = svd_factors(W.float().cpu().numpy(), r)
             self.B = torch.as_tensor(np.ascontiguousarray(B), dtype=torch.float32).to(dev)
             self.A = torch.as_tensor(np.ascontiguousarray(A), dtype=torch.float32).to(dev)
@@ -367,10 +403,17 @@ class TTQLinear:
         check(lib.ttq_set_weight(self._h, ctypes.c_void_p(W.data_ptr()), _stream()), "ttq_set_weight")
 
     def prepare(self, X) -> None:
-        """Per-prompt prefill step: D, D^(-1/2), codes, scales and zeros."""
+        """Per-prompt prefill step: D, D^(-1/2), codes, scales and zeros (and,
+        for a refreshing layer, the rank-16 factors and W_res first)."""
         x, dt, T, ldx = _x_args(X)
         if X.shape[1] != self.d_in:
             raise ValueError(f"X has {X.shape[1]} channels, the layer {self.d_in}")
+        if self.V is not None:
+            ws = self.refresh_workspace
+            check(load().ttq_prepare_refresh(self._h, x, dt, T, ldx, ctypes.c_void_p(self.V.data_ptr()),
+                                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()),
+                  "ttq_prepare_refresh")
+            return
         check(load().ttq_prepare(self._h, x, dt, T, ldx, _stream()), "ttq_prepare")
 
     def linear(self, X, out=None):

@@ -65,6 +65,9 @@ SIGNATURES = {
     "ttq_colstats_workspace_bytes": (_S, [_I64, _I64]),
     "ttq_colstats": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P, _S, _P]),
     "ttq_colstats_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _F, _F, _F, _P, _P, _P]),
+    "ttq_prepare_refresh": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _S, _P]),
+    "ttq_lowrank_refresh_workspace_bytes": (_S, [_I32, _I32, _I32]),
+    "ttq_lowrank_refresh": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttq_quantize_pack": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "ttq_residual": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "ttq_lowrank_z": (ctypes.c_int, [_I64, _I32, _I32, _P, ctypes.c_int, _I64, _P, _P, _P]),
@@ -80,7 +83,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 5  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
+ABI_VERSION = 6  # TTQ_ABI_VERSION of include/ttq.h that these signatures match
 
 
 def load() -> ctypes.CDLL:

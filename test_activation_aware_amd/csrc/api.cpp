@@ -19,6 +19,7 @@ struct ttq_handle {
   ttq_config cfg;
   ttq_buffers buf;
   const void* wsrc;  // W (r = 0) or buf.wres (r > 0)
+  const void* w;     // W itself (the online refresh of the factors reads it)
   bool weight_bound;
   bool prepared;
   bool wexp_valid;  // the last prepare wrote the effective fp16 weight
@@ -241,6 +242,7 @@ ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle
   h->cfg = *cfg;
   h->buf = *bufs;
   h->wsrc = nullptr;
+  h->w = nullptr;
   h->weight_bound = false;
   h->prepared = false;
   h->wexp_valid = false;
@@ -253,6 +255,7 @@ void ttq_destroy(ttq_handle* h) { delete h; }
 ttq_status ttq_set_weight(ttq_handle* h, const void* W, void* stream) {
   if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
   TTQ_NEED(W);
+  h->w = W;
   if (h->cfg.r == 0) {
     h->wsrc = W;
     h->weight_bound = true;
@@ -575,6 +578,69 @@ ttq_status ttq_wexp_gemm(int64_t T, int32_t d_in, int32_t d_out, int32_t r, cons
   hipError_t e = ttq::launch_dense_gemm(T, d_in, d_out, r, X, ldx, Wexp, B, Z, Y, ldy,
                                         static_cast<hipStream_t>(stream));
   return hip_status(e, "dense_gemm launch");
+}
+
+size_t ttq_lowrank_refresh_workspace_bytes(int32_t d_out, int32_t d_in, int32_t r) {
+  if (d_out <= 0 || d_in <= 0 || r != 16) return 0;
+  return ttq::lowrank_refresh_ws_bytes(d_out, d_in);
+}
+
+namespace {
+ttq_status check_refresh(int32_t d_out, int32_t d_in, int32_t r, const void* W, const float* D, const float* V,
+                         const float* B, const float* A, const void* workspace, size_t workspace_bytes) {
+  if (r != 16) return fail(r <= 0 ? TTQ_ERR_INVALID_ARG : TTQ_ERR_UNSUPPORTED, "r=%d, the refresh is built for r=16", r);
+  ttq_status s = check_dims(d_in, d_out, 32);
+  if (s != TTQ_OK) return s;
+  if (d_in % 128 != 0) return fail(TTQ_ERR_SHAPE, "d_in=%d must be a multiple of 128 for the refresh", d_in);
+  TTQ_NEED(W);
+  TTQ_NEED(D);
+  TTQ_NEED(V);
+  TTQ_NEED(B);
+  TTQ_NEED(A);
+  TTQ_NEED(workspace);
+  const size_t need = ttq::lowrank_refresh_ws_bytes(d_out, d_in);
+  if (workspace_bytes < need) return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  return TTQ_OK;
+}
+}  // namespace
+
+ttq_status ttq_lowrank_refresh(int32_t d_out, int32_t d_in, int32_t r, const void* W, const float* D, float* V,
+                               float* B, float* A, void* workspace, size_t workspace_bytes, void* stream) {
+  ttq_status s = check_refresh(d_out, d_in, r, W, D, V, B, A, workspace, workspace_bytes);
+  if (s != TTQ_OK) return s;
+  hipError_t e = ttq::launch_lowrank_refresh(d_out, d_in, W, D, V, B, A, workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, "lowrank_refresh launch");
+}
+
+ttq_status ttq_prepare_refresh(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, int64_t ldx, float* V,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (h == nullptr) return fail(TTQ_ERR_NULL, "handle is NULL");
+  if (!h->weight_bound) return fail(TTQ_ERR_INVALID_ARG, "ttq_set_weight has not been called");
+  const ttq_config& c = h->cfg;
+  ttq_status s = check_x(X, xdt, T, c.d_in, ldx);
+  if (s != TTQ_OK) return s;
+  if (T < 1) return fail(TTQ_ERR_SHAPE, "T=%lld: prepare needs at least one token", (long long)T);
+  if (T > h->buf.T_max) return fail(TTQ_ERR_SHAPE, "T=%lld exceeds the handle's T_max=%lld", (long long)T, (long long)h->buf.T_max);
+  // the handle's factor buffers are caller-owned device memory; the refresh rewrites them
+  float* B = const_cast<float*>(h->buf.B);
+  float* A = const_cast<float*>(h->buf.A);
+  s = check_refresh(c.d_out, c.d_in, c.r, h->w, h->buf.D, V, B, A, workspace, workspace_bytes);
+  if (s != TTQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.D,
+                                      h->buf.dinvsqrt, dinv16(h), h->buf.workspace, st);
+  if (e != hipSuccess) return hip_status(e, "colstats launch");
+  e = ttq::launch_lowrank_refresh(c.d_out, c.d_in, h->w, h->buf.D, V, B, A, workspace, st);
+  if (e != hipSuccess) return hip_status(e, "lowrank_refresh launch");
+  e = ttq::launch_residual(c.d_out, c.d_in, c.r, h->w, B, A, h->buf.wres, st);
+  if (e != hipSuccess) return hip_status(e, "residual launch");
+  const bool expand = use_dense(h, xdt, T);
+  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->buf.wres, h->buf.D, h->buf.codes, h->buf.scales,
+                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
+  h->prepared = true;
+  h->wexp_valid = expand;
+  return ok();
 }
 
 }  // extern "C"

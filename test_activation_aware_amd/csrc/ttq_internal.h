@@ -40,6 +40,14 @@ hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W
                                 const float* D, uint32_t* codes, void* scales, void* zeros,
                                 const void* dinv16, void* wexp, hipStream_t s);
 
+// One online step of the rank-16 factors for a prompt's statistic D: the
+// orthonormal right basis V [d_in][16] is advanced by one subspace-iteration
+// step on (W D^(1/2))^T (W D^(1/2)) and B [d_out][16], A [16][d_in] are
+// formed from it (all fp32).  d_in a multiple of 128, d_out of 32.
+size_t lowrank_refresh_ws_bytes(int d_out, int d_in);
+hipError_t launch_lowrank_refresh(int d_out, int d_in, const void* W, const float* D, float* V, float* B,
+                                  float* A, void* workspace, hipStream_t s);
+
 hipError_t launch_residual(int d_out, int d_in, int r, const void* W, const float* B,
                            const float* A, void* W_res, hipStream_t s);
 

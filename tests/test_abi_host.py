@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 5
+    assert lib.ttq_abi_version() == _capi.ABI_VERSION == 6
     for s in range(7):
         assert lib.ttq_status_string(s).decode().startswith("TTQ_")
     assert lib.ttq_status_string(99) == b"unknown ttq_status"
@@ -173,6 +173,13 @@ def test_null_and_alignment(lib):
         == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_colstats_noalloc(P, 1, 0, 128, 128, 2.0, 0.4, 0.5, P, P, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_colstats_noalloc(P, 1, 4, 128, 128, 2.0, 0.4, 0.5, None, P, None) == _capi.TTQ_ERR_NULL
+    # the online refresh: r = 16 only, d_in a multiple of 128, a workspace
+    ws = lib.ttq_lowrank_refresh_workspace_bytes(8192, 5120, 16)
+    assert ws > 0 and lib.ttq_lowrank_refresh_workspace_bytes(8192, 5120, 8) == 0
+    assert lib.ttq_lowrank_refresh(64, 256, 8, P, P, P, P, P, P, 1 << 30, None) == _capi.TTQ_ERR_UNSUPPORTED
+    assert lib.ttq_lowrank_refresh(64, 192, 16, P, P, P, P, P, P, 1 << 30, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_lowrank_refresh(64, 256, 16, P, P, None, P, P, P, 1 << 30, None) == _capi.TTQ_ERR_NULL
+    assert lib.ttq_lowrank_refresh(64, 256, 16, P, P, P, P, P, P, 16, None) == _capi.TTQ_ERR_SHAPE
     # residual and lowrank_z are built for r = 16 only
     assert lib.ttq_residual(64, 128, 8, P, P, P, P, None) == _capi.TTQ_ERR_UNSUPPORTED
     assert lib.ttq_lowrank_z(4, 128, 0, P, 1, 128, P, P, None) == _capi.TTQ_ERR_INVALID_ARG

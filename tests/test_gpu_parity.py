@@ -475,6 +475,80 @@ def test_handle_dense_path():
 
 
 # ---------------------------------------------------------------------------
+# online refresh of the rank-16 factors
+# ---------------------------------------------------------------------------
+def _refresh_compare(W, D, V0, Vg, Bg, Ag, tag):
+    """GPU refresh result against the oracle's from the same inputs: the
+    product B A and the projector V' V'^T within 1e-5, V' orthonormal."""
+    Vo, Bo, Ao = oracle.lowrank_refresh(W, D, V0)
+    BAo = Bo @ Ao
+    BAg = Bg.astype(np.float64) @ Ag.astype(np.float64)
+    e_ba = np.linalg.norm(BAg - BAo) / np.linalg.norm(BAo)
+    Vg64 = Vg.astype(np.float64)
+    e_pr = np.linalg.norm(Vg64 @ (Vg64.T @ Vo) - Vo) / np.sqrt(Vo.shape[1])
+    e_on = np.abs(Vg64.T @ Vg64 - np.eye(Vg.shape[1])).max()
+    say(f"  {tag}: B A rel {e_ba:.2e}, subspace {e_pr:.2e}, orthonormality {e_on:.2e}")
+    assert e_ba <= 1e-5 and e_pr <= 1e-5 and e_on <= 1e-5
+    return Vo
+
+
+@pytest.mark.parametrize("cfg,d_out", [(2, None), (4, None), (5, None), (5, 4096 + 32)])
+def test_lowrank_refresh_parity(cfg, d_out):
+    """ttq_lowrank_refresh from the SVD basis with two prompts' statistics in
+    turn, against oracle.lowrank_refresh from the same inputs; then W_res from
+    the GPU's factors bit-exact with the oracle's residual of them."""
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg, T=1024, d_out=d_out)
+    X2 = wl.activations(cfg, 1024, w.d, w.x_dtype, w.n_outliers, w.outlier_factor, prompt=1)
+    V0 = oracle.svd_right_basis(W, 16).astype(np.float32)
+    say(f"refresh cfg={cfg} d_out={W.shape[0]}")
+    Vd = dev(V0)
+    Wd = dev(W)
+    for step, Xp in enumerate((X, X2)):
+        D = oracle.colstats(Xp, w.p, w.lam, w.alpha)
+        Vin = host(Vd).copy()
+        Bd, Ad = ttq.ttq_lowrank_refresh(Wd, dev(D), Vd)
+        _refresh_compare(W, D, Vin, host(Vd), host(Bd), host(Ad), f"step {step}")
+    Rg = host(ttq.ttq_residual(Wd, Bd, Ad))
+    assert Rg.view(np.uint16).tobytes() == oracle.residual(W, host(Bd), host(Ad)).view(np.uint16).tobytes()
+
+
+@pytest.mark.parametrize("cfg,q,T", [(2, 3, None), (5, 2, 8192), (5, 4, None)])
+def test_e2e_prepare_refresh(cfg, q, T):
+    """A refreshing handle: prepare (statistic, refresh, residual, quantise)
+    then the projection.  D within 1e-5; B A within 1e-5 of the oracle's
+    refresh from the SVD basis with the oracle's D; W_res bit-exact given the
+    GPU's B, A; codes, scales and zeros bit-exact given the GPU's D and W_res;
+    Y within 1e-3 of the oracle's own pipeline (its D, refresh, residual,
+    codes and projection)."""
+    w = wl.CONFIGS[cfg]
+    X, W = cfg_inputs(cfg, T=T)
+    T = X.shape[0]
+    say(f"e2e refresh cfg={cfg} q={q} T={T}")
+    layer = ttq.TTQLinear(dev(W), q=q, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, refresh=True)
+    V0 = host(layer.V).copy()
+    Xd = dev(X)
+    layer.prepare(Xd)
+    Yg = host(layer.linear(Xd))
+    D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
+    Dg = host(layer.D)
+    assert np.max(np.abs(Dg.astype(np.float64) - D0) / D0) <= D_TOL
+    Bg, Ag = host(layer.B), host(layer.A)
+    _refresh_compare(W, D0, V0, host(layer.V), Bg, Ag, "refresh")
+    Wq = oracle.residual(W, Bg, Ag)
+    assert host(layer.wres).view(np.uint16).tobytes() == Wq.view(np.uint16).tobytes(), "W_res differs"
+    check_quant_given_d(layer, Wq, q, 32)
+    _, Bo, Ao = oracle.lowrank_refresh(W, D0, V0)
+    Bo, Ao = Bo.astype(np.float32), Ao.astype(np.float32)
+    c0, s0, z0 = oracle.quantize(oracle.residual(W, Bo, Ao), D0, q, 32)
+    Y0 = oracle.linear(X, c0, s0, z0, D0, 32, Bo, Ao)
+    e = rel_fro(Yg, Y0)
+    say(f"  prefill rel_fro={e:.3e}")
+    assert np.all(np.isfinite(Yg)) and e <= Y_TOL
+    layer.close()
+
+
+# ---------------------------------------------------------------------------
 # end to end through the handle API (prepare once, project prefill + decode)
 # ---------------------------------------------------------------------------
 def _e2e(cfg, q, g, r, T=None, prompt=0, alpha=None, decode_T=(), prefill=False):
