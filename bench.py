@@ -316,8 +316,25 @@ def main():
         t16 = time_loop(step16, args.steps, torch)
         Zbuf = torch.empty((T, 16), dtype=torch.float32, device="cuda")
         t_z = time_loop(lambda: ttq.ttq_lowrank_z(X, layer16.A, out=Zbuf), n_k, torch)
-        r16 = {"value": T / t16 / 1e3, "ms_per_step": t16 * 1e3, "lowrank_z_us": t_z * 1e6}
+        t_p16 = time_loop(lambda: layer16.prepare(X), n_k, torch)
+        r16 = {"value": T / t16 / 1e3, "ms_per_step": t16 * 1e3, "lowrank_z_us": t_z * 1e6,
+               "prepare_us": t_p16 * 1e6}
         layer16.close()
+        # the same step with the online refresh of the rank-16 factors: per
+        # prompt one subspace-iteration step from the previous right basis,
+        # then W_res and its quantisation, then the projection
+        log("bench: r=16 with the online refresh")
+        layerR = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, refresh=True)
+
+        def stepR():
+            layerR.prefill(X, out=Y)
+        settle(stepR, args.settle_ms, torch)
+        for _ in range(args.warmup):
+            stepR()
+        tR = time_loop(stepR, args.steps, torch)
+        t_pR = time_loop(lambda: layerR.prepare(X), n_k, torch)
+        r16["refresh"] = {"value": T / tR / 1e3, "ms_per_step": tR * 1e3, "prepare_us": t_pR * 1e6}
+        layerR.close()
         del rng
 
     # ---- other code widths and group sizes on the same prompt and weight ----

@@ -211,9 +211,10 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
  * zeros into the handle (as ttq_prepare) and Y = the projection of X (as
  * ttq_linear).  With r = 16, fp16 input and T > 64 the column statistic and
  * Z = X A^T come from one read of X (the form the two separate calls cannot
- * use, since ttq_linear may see other inputs than the prompt); D is then
- * summed in another fixed grouping than ttq_prepare's and may differ from it
- * in the last bits (both within 1e-5 of the exact statistic).  Otherwise it
+ * use, since ttq_linear may see other inputs than the prompt); D and Z are
+ * then summed in other fixed groupings than those of ttq_prepare and
+ * ttq_linear and may differ from theirs in the last bits (D within 1e-5 of
+ * the exact statistic either way, Z within fp32 rounding).  Otherwise it
  * is exactly ttq_prepare followed by ttq_linear.  workspace: device memory of
  * at least ttq_prefill_workspace_bytes(T, d_in, d_out, r, xdt) bytes, owned
  * by the caller; the handle's own workspace is used too (by the statistic of

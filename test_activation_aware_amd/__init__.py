@@ -437,8 +437,12 @@ class TTQLinear:
     def prefill(self, X, out=None):
         """The whole per-prompt step, prepare(X) then linear(X), in one call
         (ttq_prefill: with r = 16 and fp16 input the statistic and A X come
-        from one read of X).  Returns Y [T][d_out]."""
+        from one read of X).  A refreshing layer runs prepare(X) (with the
+        refresh) and then linear(X).  Returns Y [T][d_out]."""
         torch = _torch()
+        if self.V is not None:
+            self.prepare(X)
+            return self.linear(X, out=out)
         x, dt, T, ldx = _x_args(X)
         if X.shape[1] != self.d_in:
             raise ValueError(f"X has {X.shape[1]} channels, the layer {self.d_in}")

@@ -19,11 +19,12 @@
 // Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X) (paper-daily.com deep
 // reading, section 2: static low-rank factors applied to the raw input), from
 // the same read of X.  A workgroup owns 16 TG tokens and all d channels; its
-// 4 waves take 32-channel chunks round-robin.  Lane l holds token l % 16 and
+// 8 waves take 32-channel chunks round-robin.  Lane l holds token l % 16 and
 // channels 8 (l / 16) .. + 8 of a chunk, the operand layout of a 16x16x32
 // fp16 MFMA whose other operand is the matching slice of A^T (A split into
-// two fp16 parts, so Z keeps about 22 bits; the same operands, chunk order
-// and wave order as ttq_lowrank_z, so Z is the same bit for bit).  For the
+// two fp16 parts, so Z keeps about 22 bits; the operands of ttq_lowrank_z,
+// with the chunks summed in another grouping, so Z agrees with it to fp32
+// rounding, not bit for bit).  For the
 // statistic each lane squares its 8 channels over its TG tokens, and the 16
 // lanes that hold the same channels are added by a fixed tree of DPP row
 // rotations; one partial row per workgroup (16 TG tokens) goes to the same
@@ -171,11 +172,13 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+constexpr int kZWaves = 8;  // waves of the fused pass, each on every 8th chunk
+
 template <int PMODE, int TG>
-__global__ __launch_bounds__(256) void colstats_z_partial(int64_t T, int d, const _Float16* __restrict__ X,
+__global__ __launch_bounds__(64 * kZWaves) void colstats_z_partial(int64_t T, int d, const _Float16* __restrict__ X,
                                                           int64_t ldx, float p, const float* __restrict__ A,
                                                           float* __restrict__ partial, float* __restrict__ Z) {
-  __shared__ f4 zred[kWaves][TG][64];
+  __shared__ f4 zred[kZWaves][TG][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kb = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * kTok * TG;
@@ -228,19 +231,19 @@ __global__ __launch_bounds__(256) void colstats_z_partial(int64_t T, int d, cons
     a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
     a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
   };
-  // kU chunks per pass, all their loads requested before any is used; chunks
-  // are accumulated in the order c = wave, wave + 4, ... (as ttq_lowrank_z)
-  constexpr int kU = TG >= 4 ? 2 : 4;
+  // kU chunks per pass, all their loads requested before any is used; a wave
+  // accumulates its chunks in the order c = wave, wave + 8, ...
+  constexpr int kU = 4;
   int c = wave;
-  for (; c + 4 * (kU - 1) < nchunks; c += 4 * kU) {
+  for (; c + kZWaves * (kU - 1) < nchunks; c += kZWaves * kU) {
     h8 x[kU][TG];
     float a[kU][8];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) load_chunk((c + 4 * u) * kChunk, x[u], a[u]);
+    for (int u = 0; u < kU; ++u) load_chunk((c + kZWaves * u) * kChunk, x[u], a[u]);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) chunk((c + 4 * u) * kChunk, x[u], a[u]);
+    for (int u = 0; u < kU; ++u) chunk((c + kZWaves * u) * kChunk, x[u], a[u]);
   }
-  for (; c < nchunks; c += 4) {
+  for (; c < nchunks; c += kZWaves) {
     h8 x[TG];
     float a[8];
     load_chunk(c * kChunk, x, a);
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void colstats_z_partial(int64_t T, int d, cons
   }
 
   // lane l holds Z[t0 + 16 g + 4 (l / 16) + i][l % 16], i = 0..3, for this
-  // wave's chunks; the 4 waves' partials are added in wave order
+  // wave's chunks; the 8 waves' partials are added in wave order
 #pragma unroll
   for (int g = 0; g < TG; ++g) zred[wave][g][lane] = acc[g];
   __syncthreads();
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256) void colstats_z_partial(int64_t T, int d, cons
     const int g = wave;
     f4 s = zred[0][g][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 1; w < kZWaves; ++w) {
       const f4 v = zred[w][g][lane];
       s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
     }
@@ -300,7 +303,7 @@ int colstats_chunks(int64_t T) {
 }
 
 // tokens per workgroup of the fused pass: 64 while that leaves a workgroup
-// per CU, else 16 (the grouping of ttq_lowrank_z, so Z is the same)
+// per CU, else 16 tokens
 int colstats_z_tg(int64_t T) { return T >= 64 * 256 ? 4 : 1; }
 
 int colstats_z_chunks(int64_t T) {
@@ -314,7 +317,7 @@ hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float
   const int tg = colstats_z_tg(T);
   const int chunks = colstats_z_chunks(T);
   const _Float16* x = static_cast<const _Float16*>(X);
-  const dim3 grid((unsigned)chunks), block(kThreads);
+  const dim3 grid((unsigned)chunks), block(64 * kZWaves);
 #define TTQ_CZ(PM, TGV) hipLaunchKernelGGL((colstats_z_partial<PM, TGV>), grid, block, 0, s, T, d, x, ldx, p, A, partial, Z)
   if (tg == 4) {
     if (p == 2.0f) TTQ_CZ(2, 4);
