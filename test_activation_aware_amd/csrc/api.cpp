@@ -463,6 +463,12 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   const size_t need = linear_ws_bytes(T, c.d_in, c.d_out, c.r);
   if (workspace_bytes < need) return fail(TTQ_ERR_SHAPE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c.r == 0 && T == 1) {
+    // one token: the dot-product form, pre-scaling the input itself
+    hipError_t e = ttq::launch_wlowbit_gemv_raw(c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, h->buf.dinvsqrt,
+                                                h->buf.codes, h->buf.scales, h->buf.zeros, Y, st);
+    return hip_status(e, "wlowbit_gemv launch");
+  }
   if (c.r == 0 && T <= ttq::kFuseMaxT) {
     // a few tokens: one kernel pre-scales the input itself (same results)
     hipError_t e = ttq::launch_wlowbit_decode_raw(T, c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, ldx,

@@ -84,7 +84,20 @@ hipError_t launch_wlowbit_decode_splitk(int64_t T, int d_in, int d_out, int q, i
                                         const void* scales, const void* zeros, void* Y, int64_t ldy,
                                         void* workspace, hipStream_t s);
 
-// The projection; T <= kDecodeMaxT goes to the decode kernel.
+// The projection of a single token (T = 1): a dot-product form of the
+// decode, one workgroup per 32-row tile.  launch_wlowbit_gemv takes the
+// pre-scaled input Xs [d_in] (and Z [16], B for r > 0; Y fp16 or fp32);
+// launch_wlowbit_gemv_raw the raw x (fp16 or fp32) and D^(-1/2), r = 0, Y of
+// x's type.  The two give the same bits for the same input.
+hipError_t launch_wlowbit_gemv(int d_in, int d_out, int q, int g, int r, const void* Xs, const uint32_t* codes,
+                               const void* scales, const void* zeros, const float* B, const float* Z, void* Y,
+                               bool y_f32, hipStream_t s);
+hipError_t launch_wlowbit_gemv_raw(int d_in, int d_out, int q, int g, const void* X, bool x_f32,
+                                   const float* dinvsqrt, const uint32_t* codes, const void* scales,
+                                   const void* zeros, void* Y, hipStream_t s);
+
+// The projection; T = 1 goes to the dot-product form, T <= kDecodeMaxT to the
+// decode kernel.
 hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
                                int64_t ldxs, const uint32_t* codes, const void* scales,
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,

@@ -356,6 +356,17 @@ def test_decode_parity(cfg, T, q, g, r):
     _gemm_case(cfg, T, q, g, r)
 
 
+@pytest.mark.parametrize("cfg,q,g,r", [(5, q, g, 0) for q in (2, 3, 4, 5) for g in (16, 32, 64, 128)] + [
+    (5, 4, 32, 16), (5, 3, 128, 16), (5, 5, 16, 16), (2, 3, 32, 16), (1, 4, 32, 0), (1, 5, 128, 0),
+    (3, 2, 16, 0), (4, 5, 64, 16), (4, 4, 128, 0), (3, 4, 128, 16),
+])
+def test_gemv_parity(cfg, q, g, r):
+    """T = 1 on the pre-scaled input takes the dot-product form: every code
+    width and group size (G = 128 with wave ranges that end inside a group at
+    d_in = 5120), the rank-16 term, fp32 output (cfg 1)."""
+    _gemm_case(cfg, 1, q, g, r)
+
+
 def test_gemm_parity_strided_input():
     _gemm_case(3, 300, 4, 32, 0, pad_ld=64)
     _gemm_case(3, 40, 4, 32, 0, pad_ld=64)
