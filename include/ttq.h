@@ -154,12 +154,16 @@ const char* ttq_status_string(ttq_status s);
  * the next call into the library on this thread. */
 const char* ttq_last_error(void);
 
-/* Pure host: checks cfg and fills *out for prompts of up to T_max tokens. */
+/* Pure host: checks cfg and fills *out for prompts of up to T_max tokens.
+ * (Bookkeeping of this library's buffers; the pages define no such call.) */
 ttq_status ttq_query_sizes(const ttq_config* cfg, int64_t T_max, ttq_sizes* out);
 
 /* Pure host: creates an opaque host object recording cfg and the device
  * pointers in *bufs (not owning them).  Buffers are checked against
- * ttq_query_sizes(cfg, bufs->T_max).  Destroy with ttq_destroy. */
+ * ttq_query_sizes(cfg, bufs->T_max).  Destroy with ttq_destroy.  The handle
+ * is the per-layer state the pages carry from prefill to decode: the
+ * hyper-parameters fixed per layer (paper-daily.com deep reading, section 2)
+ * and the quantisation computed at prefill (section 6). */
 ttq_status ttq_create(const ttq_config* cfg, const ttq_buffers* bufs, ttq_handle** out);
 void ttq_destroy(ttq_handle* h);
 
@@ -173,7 +177,11 @@ ttq_status ttq_set_weight(ttq_handle* h, const void* W, void* stream);
 
 /* Per-prompt prefill step, prepare(X, W, q, g, alpha, lambda, p) with W and
  * the hyper-parameters bound in the handle:
- *   D, D^(-1/2) = colstats(X)  then  codes, scales, zeros = quantize(W_res, D).
+ *   D, D^(-1/2) = colstats(X)  then  codes, scales, zeros = quantize(W_res, D)
+ * (paper-daily.com deep reading, section 2: the diagonal from the prompt's own
+ * activations, then group RTN of W D^(1/2); section 6: once per prompt at
+ * prefill; nubint.ai review, proposed-method section: weights quantised on
+ * the fly by group-wise RTN with QDQ).
  * D^(-1/2) is written as fp32 followed by an fp16 copy (ttq_sizes).
  * X: device [T][ldx] of dtype xdt, 1 <= T <= T_max. */
 ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
@@ -181,6 +189,9 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
 
 /* The low-bit projection with the handle's current quantisation:
  *   Y = Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
+ * (paper-daily.com deep reading, section 2: the closed form and the low-rank
+ * term; section 5: a low-bit kernel on the pre-scaled input; section 6:
+ * decode steps reuse the prefill's parameters).
  * X: device [T][ldx] of dtype xdt; Y: device [T][ldy] of the same dtype,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
@@ -250,7 +261,10 @@ int64_t ttq_dense_min_tokens(int32_t d_out);
 /* ---- Sub-steps, exported so each kernel can be checked on its own ---- */
 
 /* Column statistic: D[j] = fp32((mean_{t<T} |X[t][j]|^p + lambda)^alpha) and
- * dinvsqrt[j] = fp32(1/sqrt(D[j])), j < d.  Partial sums go to workspace
+ * dinvsqrt[j] = fp32(1/sqrt(D[j])), j < d (paper-daily.com deep reading,
+ * section 2: the online AWQ diagonal with shrinkage lambda and exponent
+ * alpha; gist.science German summary, section 2: the p-norm of each input
+ * channel over the prompt).  Partial sums go to workspace
  * (fp32, at least ttq_colstats_workspace_bytes(T, d) bytes).  Sums are
  * taken in a fixed order: the result is deterministic. */
 size_t ttq_colstats_workspace_bytes(int64_t T, int64_t d);
@@ -289,7 +303,9 @@ ttq_status ttq_lowrank_refresh(int32_t d_out, int32_t d_in, int32_t r, const voi
                                float* B, float* A, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Quantise and pack W_src D^(1/2) (device fp16 [d_out][d_in], D device fp32
- * [d_in]) with the rules of the oracle: fp32 arithmetic, zero-inclusive
+ * [d_in]), the group RTN of the activation-weighted weight
+ * (paper-daily.com deep reading, section 2: RTN QDQ per group of W D^(1/2);
+ * nubint.ai review, proposed-method section), with these rules: fp32 arithmetic, zero-inclusive
  * group range, fp16 scale rounded upward, z = rint(-mn/s),
  * c = clamp(rint(v/s) + z, 0, 2^q-1), round half to even, IEEE division.
  * Writes codes, scales, zeros (layouts above).  Any D > 0 may be supplied
@@ -299,17 +315,23 @@ ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g,
                              void* scales, void* zeros, void* stream);
 
 /* W_res = fp16(W - B A): W device fp16 [d_out][d_in], B device fp32
- * [d_out][r], A device fp32 [r][d_in]; products summed in fp64. */
+ * [d_out][r], A device fp32 [r][d_in]; products summed in fp64
+ * (paper-daily.com deep reading, section 2: W split into B A plus a
+ * quantised residual; gist.science French summary, section 2B). */
 ttq_status ttq_residual(int32_t d_out, int32_t d_in, int32_t r, const void* W,
                         const float* B, const float* A, void* W_res, void* stream);
 
-/* Z = X A^T: X device [T][ldx] (dtype xdt), A device fp32 [r][d_in],
+/* Z = X A^T, the input of the low-rank term B (A X) (paper-daily.com deep
+ * reading, section 2; gist.science French summary, section 2B):
+ * X device [T][ldx] (dtype xdt), A device fp32 [r][d_in],
  * Z device fp32 [T][r], fp32 accumulation (A enters the matrix cores as two
  * fp16 parts, about 22 bits).  r must be 16. */
 ttq_status ttq_lowrank_z(int64_t T, int32_t d_in, int32_t r, const void* X, ttq_dtype xdt,
                          int64_t ldx, const float* A, float* Z, void* stream);
 
-/* Xs = fp16(dinvsqrt * X): X device [T][ldx] (dtype xdt), dinvsqrt device
+/* Xs = fp16(dinvsqrt * X), the pre-scaled input D^(-1/2) X of the closed
+ * form (paper-daily.com deep reading, section 2; section 5: the low-bit
+ * kernel runs on the pre-scaled input): X device [T][ldx] (dtype xdt), dinvsqrt device
  * fp32 [d_in], Xs device fp16 [T][d_in] (dense rows, the channel order of
  * X).  Each product is taken in fp32 and rounded to fp16; d_in must be a
  * multiple of 64. */
@@ -317,7 +339,10 @@ ttq_status ttq_prescale(const void* X, ttq_dtype xdt, int64_t T, int32_t d_in, i
                         const float* dinvsqrt, void* Xs, void* stream);
 
 /* Y = V_hat Xs + B Z with V_hat[n][k] = (code - z) * s, fp16 operands on the
- * matrix cores and fp32 accumulation.  Xs: device fp16 [T][ldxs] as written
+ * matrix cores and fp32 accumulation: Q[W_res D^(1/2)] (D^(-1/2) X) + B (A X)
+ * on the pre-scaled input (paper-daily.com deep reading, sections 2 and 5;
+ * thelatestinai.com, Tables 4-8: the query projection timed on the Qwen3
+ * shapes of Table 15).  Xs: device fp16 [T][ldxs] as written
  * by ttq_prescale (ldxs >= d_in, a multiple of 8); codes/scales/zeros as
  * produced by ttq_quantize_pack; B device fp32 [d_out][r] and Z device fp32
  * [T][r] (both ignored when r = 0).  Y: device [T][ldy] of dtype ydt. */

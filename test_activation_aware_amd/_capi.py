@@ -8,7 +8,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libttq.so")
+# the in-tree build; TTQ_LIBRARY names another build of the same ABI (for
+# example one with sanitizers on its host code)
+LIB_PATH = os.environ.get("TTQ_LIBRARY") or os.path.join(PKG, "libttq.so")
 
 TTQ_OK = 0
 TTQ_ERR_INVALID_ARG = 1

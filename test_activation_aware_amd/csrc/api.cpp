@@ -103,12 +103,25 @@ ttq_status check_cfg(const ttq_config* cfg) {
   return check_stats(cfg->alpha, cfg->lambda, cfg->p);
 }
 
+// Largest byte extent of a strided matrix argument, (rows - 1) * ld + cols
+// elements: 2^48 bytes, beyond any device memory, so that no offset a kernel
+// forms overflows 64 bits.
+constexpr int64_t kMaxExtentBytes = int64_t(1) << 48;
+bool extent_ok(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  if (rows <= 1) return cols <= kMaxExtentBytes / elem;
+  const int64_t max_elems = kMaxExtentBytes / elem;
+  return ld <= (max_elems - cols) / (rows - 1);
+}
+
 ttq_status check_x(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t ldx) {
   if (xdt != TTQ_F16 && xdt != TTQ_F32) return fail(TTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)xdt);
   if (T < 0) return fail(TTQ_ERR_SHAPE, "T=%lld is negative", (long long)T);
   if (T > (int64_t(1) << 31)) return fail(TTQ_ERR_SHAPE, "T=%lld too large", (long long)T);
   if (ldx < d) return fail(TTQ_ERR_SHAPE, "ldx=%lld < d=%lld", (long long)ldx, (long long)d);
   if (ldx % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldx=%lld is not a multiple of 8", (long long)ldx);
+  if (!extent_ok(T, d, ldx, xdt == TTQ_F32 ? 4 : 2))
+    return fail(TTQ_ERR_SHAPE, "T=%lld rows of stride ldx=%lld span more than 2^48 bytes", (long long)T,
+                (long long)ldx);
   if (T > 0) TTQ_NEED(X);
   return TTQ_OK;
 }
@@ -165,6 +178,9 @@ ttq_status check_y(const void* Y, ttq_dtype ydt, int64_t T, int64_t d_out, int64
   if (ydt != TTQ_F16 && ydt != TTQ_F32) return fail(TTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)ydt);
   if (ldy < d_out) return fail(TTQ_ERR_SHAPE, "ldy=%lld < d_out=%lld", (long long)ldy, (long long)d_out);
   if (ldy % 8 != 0) return fail(TTQ_ERR_ALIGN, "ldy=%lld is not a multiple of 8", (long long)ldy);
+  if (!extent_ok(T, d_out, ldy, ydt == TTQ_F32 ? 4 : 2))
+    return fail(TTQ_ERR_SHAPE, "T=%lld rows of stride ldy=%lld span more than 2^48 bytes", (long long)T,
+                (long long)ldy);
   if (T > 0) TTQ_NEED(Y);
   return TTQ_OK;
 }

@@ -136,6 +136,10 @@ def test_null_and_alignment(lib):
     assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.0, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
     assert lib.ttq_colstats(P, 1, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 4, None) == _capi.TTQ_ERR_SHAPE
     assert lib.ttq_colstats(P, 7, 4, 128, 128, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_INVALID_ARG
+    # strides whose row offsets would leave 64 bits (or any device memory)
+    assert lib.ttq_colstats(P, 1, 4, 128, 1 << 62, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_colstats(P, 0, 3, 128, 1 << 45, 2.0, 0.4, 0.5, P, P, P, 1 << 20, None) == _capi.TTQ_ERR_SHAPE
+    assert lib.ttq_prescale(P, 1, 1 << 20, 128, 1 << 40, P, P, None) == _capi.TTQ_ERR_SHAPE
     # gemm: ldy too small, r = 16 without Z, bad output dtype, T = 0 is an accepted no-op
     assert lib.ttq_wlowbit_gemm(8, 128, 64, 4, 32, 0, P, 128, P, P, P, None, None, P, 1, 32, None) \
         == _capi.TTQ_ERR_SHAPE
