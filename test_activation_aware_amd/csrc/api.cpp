@@ -145,7 +145,7 @@ size_t colstats_ws_bytes(int64_t T, int64_t d) {
 }
 
 // ttq_linear's workspace: Xs (fp16 [T][d_in]) then, for r > 0, Z (fp32 [T][r]);
-// for r = 0 and a few tokens (kFuseMaxT < T <= kDecodeMaxT) the split-K
+// for r = 0 and a few tokens (kFewTokMaxT < T <= kDecodeMaxT) the split-K
 // partial products instead, when they are larger
 size_t xs_bytes(int64_t T, int64_t d) { return ((size_t)T * (size_t)d * 2 + 255) & ~(size_t)255; }
 size_t linear_ws_bytes(int64_t T, int64_t d, int64_t d_out, int32_t r) {
@@ -485,14 +485,18 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
                                                 h->buf.codes, h->buf.scales, h->buf.zeros, Y, st);
     return hip_status(e, "wlowbit_gemv launch");
   }
-  if (c.r == 0 && T <= ttq::kFuseMaxT) {
-    // a few tokens: one kernel pre-scales the input itself (same results)
-    hipError_t e = ttq::launch_wlowbit_decode_raw(T, c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, ldx,
-                                                  h->buf.dinvsqrt, h->buf.codes, h->buf.scales, h->buf.zeros,
-                                                  Y, ldy, st);
-    return hip_status(e, "wlowbit_decode launch");
+  if (xdt == TTQ_F16 && T >= 2 && T <= ttq::kFewTokMaxT) {
+    // a few fp16 tokens: the few-token form on X itself, D^(-1/2) applied on
+    // the weight side (Z = X A^T first when r > 0)
+    float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
+    hipError_t e = hipSuccess;
+    if (c.r > 0) e = ttq::launch_prescale_z(T, c.d_in, X, false, ldx, h->buf.dinvsqrt, nullptr, h->buf.A, z, st);
+    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
+    e = ttq::launch_wlowbit_fewtok(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
+                                   h->buf.scales, h->buf.zeros, h->buf.B, z, Y, false, ldy, st);
+    return hip_status(e, "wlowbit_fewtok launch");
   }
-  if (c.r == 0 && T <= ttq::kDecodeMaxT) {
+  if (c.r == 0 && T > ttq::kFewTokMaxT && T <= ttq::kDecodeMaxT) {
     // up to 64 tokens: split-K over 256-row workgroups, partials in the workspace
     hipError_t e = ttq::launch_wlowbit_decode_splitk(T, c.d_in, c.d_out, c.q, c.g, X, xdt == TTQ_F32, ldx,
                                                      h->buf.dinvsqrt, h->buf.codes, h->buf.scales,

@@ -60,6 +60,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, vo
                                            voff, 0, 0, 0);
 }
 
+// Zero, as an opaque value the compiler cannot form before v is in a
+// register.  A direct-to-LDS copy is not a dependence the compiler tracks for
+// the LDS reads of its destination: addressing those reads with
+// after_load(v), v a word of a global load issued after the copy, makes them
+// wait for that load and so, since a wave's loads complete in issue order,
+// for the copy.
+__device__ __forceinline__ int after_load(uint32_t v) {
+  int z = 0;
+  asm("" : "+v"(z) : "v"(v));
+  return z;
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 

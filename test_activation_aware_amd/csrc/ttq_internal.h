@@ -64,17 +64,7 @@ hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, i
                                  const float* B, const float* Z, void* Y, bool y_f32, int64_t ldy,
                                  hipStream_t s);
 
-// The same for T <= kFuseMaxT and r = 0, straight from the raw input X
-// (fp16 or fp32, row stride ldx) and D^(-1/2): one launch, the pre-scaling
-// done inside; Y has X's dtype.  Bit-identical to launch_prescale_z followed
-// by launch_wlowbit_decode.
-constexpr int kFuseMaxT = 4;
-hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
-                                     int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
-                                     const void* scales, const void* zeros, void* Y, int64_t ldy,
-                                     hipStream_t s);
-
-// The same for kFuseMaxT < T <= kDecodeMaxT and r = 0 from the raw input:
+// The same for kFewTokMaxT < T <= kDecodeMaxT and r = 0 from the raw input:
 // split-K over 256-row workgroups that share one pre-scaled copy of their
 // input slice, fp32 partials in `workspace` (decode_splitk_ws_bytes), then a
 // reduction in split order.  Y has X's dtype.
@@ -96,8 +86,17 @@ hipError_t launch_wlowbit_gemv_raw(int d_in, int d_out, int q, int g, const void
                                    const float* dinvsqrt, const uint32_t* codes, const void* scales,
                                    const void* zeros, void* Y, hipStream_t s);
 
-// The projection; T = 1 goes to the dot-product form, T <= kDecodeMaxT to the
-// decode kernel.
+// The projection of 2 <= T <= kFewTokMaxT tokens, one workgroup per 32-row
+// tile on the matrix cores: dinv16 == NULL, X is the pre-scaled Xs (Y fp16 or
+// fp32, B and Z for r > 0); dinv16 = fp16(D^(-1/2)), X is the raw fp16 input
+// with D^(-1/2) applied on the weight side (Y fp16).  X rows of stride ldx.
+constexpr int kFewTokMaxT = 16;
+hipError_t launch_wlowbit_fewtok(int64_t T, int d_in, int d_out, int q, int g, int r, const void* X, int64_t ldx,
+                                 const void* dinv16, const uint32_t* codes, const void* scales, const void* zeros,
+                                 const float* B, const float* Z, void* Y, bool y_f32, int64_t ldy, hipStream_t s);
+
+// The projection; T = 1 goes to the dot-product form, T <= kFewTokMaxT to the
+// few-token form, T <= kDecodeMaxT to the decode kernel.
 hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int r, const void* Xs,
                                int64_t ldxs, const uint32_t* codes, const void* scales,
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,

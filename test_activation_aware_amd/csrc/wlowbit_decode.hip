@@ -1,4 +1,5 @@
-// The TTQ low-bit projection for few tokens (decode, T <= 64): the same
+// The TTQ low-bit projection for decode batches of 17 to 64 tokens (one and
+// up to 16 tokens have forms of their own): the same
 //   Y = Q[(W - B A) D^(1/2)] (D^(-1/2) X) + B (A X)
 // as ttq_wlowbit_gemm, reusing the prefill's codes, scales and zeros
 // (paper-daily.com deep reading, section 6: quantisation parameters computed
@@ -16,9 +17,10 @@
 //     per step from LDS), then the codes of up to 16 steps at once
 //     (registers), and keeps the pre-scaled input of the next 2 - 4 steps in
 //     flight; requests are kept in order of use, since waiting for one load
-//     waits for every older one.  Per 16-channel sub-step: one v_mfma_f32_32x32x16_f16 per 32
-//     tokens, A = dequantised weights (the register dequantisation of the
-//     prefill kernel), B = the pre-scaled input (small; it stays in L2).
+//     waits for every older one.  Per 16-channel sub-step: one
+//     v_mfma_f32_32x32x16_f16 per 32 tokens, A = dequantised weights (the
+//     register dequantisation of the prefill kernel), B = the pre-scaled
+//     input (small; it stays in L2).
 //   * The 8 partial products meet in LDS in a fixed order (deterministic) and
 //     are stored as fp16 or fp32.
 //   * Rank-16 term: B16 x Z_hi + B16 x Z_lo (Z split into two fp16 parts)
@@ -50,30 +52,22 @@ __device__ __forceinline__ void store4(TY* p, const float* v) {
   }
 }
 
-// NF = token fragments of 32 (T <= 32 * NF).  TX = void: the input is the
-// pre-scaled Xs.  TX = _Float16 / float: the input is the raw X (row stride
-// ldx) and D^(-1/2); each wave pre-scales the rows it needs into LDS itself
-// (T <= kFuseMaxT, r = 0), with the prescale pass's arithmetic, so one launch
-// does the whole call.
-template <int Q, int G, typename TY, bool LOWRANK, int NF, typename TX>
+// NF = token fragments of 32 (T <= 32 * NF); the input is the pre-scaled Xs.
+template <int Q, int G, typename TY, bool LOWRANK, int NF>
 __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     int T, int d_in, int d_out, const _Float16* __restrict__ Xs, int64_t ldxs,
-    const TX* __restrict__ Xr, int64_t ldx, const float* __restrict__ dinv,
     // (codes deliberately not __restrict__: loads from a restrict read-only
     // pointer count as invariant, and the compiler then re-issues one next to
     // its use instead of keeping the early request, which waits for all)
     const uint32_t* codes, const _Float16* __restrict__ scales,
     const _Float16* __restrict__ zeros, const float* __restrict__ Bf, const float* __restrict__ Z,
     TY* __restrict__ Y, int64_t ldy) {
-  constexpr bool FUSED = !std::is_void<TX>::value;
-  static_assert(!FUSED || (NF == 1 && !LOWRANK), "the fused input path is for T <= kFuseMaxT, r = 0");
   constexpr int SW = 2 * Q;                     // code words per row per step
   constexpr int kXAhead = (NF == 1) ? 4 : 2;    // steps of input requested ahead of use
   // groups a round of kRound steps can touch, in 16-byte pieces of 8 halfs
   constexpr int kGroupPieces = ((kRound * 64 + 2 * G - 2) / G + 1 + 15) / 16 * 64;
-  // per wave: the pre-scaled rows of a round (fused path), later the wave's
-  // partial products (NF x 64 lanes x 64 bytes)
-  constexpr int kWaveBuf = kFuseMaxT * kRound * 64 * 2 > NF * 64 * 64 ? kFuseMaxT * kRound * 64 * 2 : NF * 64 * 64;
+  // per wave: its partial products (NF x 64 lanes x 64 bytes)
+  constexpr int kWaveBuf = NF * 64 * 64;
   __shared__ __attribute__((aligned(16))) char wbuf[kWaves][kWaveBuf];
   __shared__ __attribute__((aligned(16))) _Float16 sgrp[kWaves][2][kGroupPieces * 8];
 
@@ -106,20 +100,11 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
   const _Float16* xrow[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) xrow[f] = Xs + (int64_t)min(32 * f + l32, T - 1) * ldxs + 8 * hh;
-  // fused path: pre-scaled row t of the round at xsl[t * kRound * 8 + 8 (k - k0) + piece]
-  h8* xsl = reinterpret_cast<h8*>(&wbuf[wave][0]);
-  const int tl = min(l32, T - 1);
-  int kcur0 = 0;  // first step of the current round (fused path)
   auto load_x = [&](int k, h8 (&xb)[4][NF]) {
-    if constexpr (FUSED) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xb[s][0] = xsl[tl * kRound * 8 + 8 * (k - kcur0) + 2 * s + hh];
-    } else {
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
-    }
+      for (int f = 0; f < NF; ++f) xb[s][f] = *reinterpret_cast<const h8*>(xrow[f] + k * 64 + 16 * s);
   };
   _Float16* ssc = &sgrp[wave][0][0];
   _Float16* szr = &sgrp[wave][1][0];
@@ -151,61 +136,18 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
     // the request order is the order of use (a wait for a load waits for every
     // older one): keep the scheduler from interleaving the groups of loads
     __builtin_amdgcn_sched_barrier(0);
-    // fused path: this round's channels of the T raw rows and of D^(-1/2)
-    // (lane takes the 8-channel pieces cp = lane, lane + 64), requested before
-    // the codes so that pre-scaling them waits for these loads only
-    constexpr int kPJ = kRound * 8 / 64;
-    XRaw<TX> xraw[FUSED ? kPJ : 1][FUSED ? kFuseMaxT : 1];
-    float4 dva[FUSED ? kPJ : 1], dvb[FUSED ? kPJ : 1];
-    if constexpr (FUSED) {
-      kcur0 = k0;
-#pragma unroll
-      for (int j = 0; j < kPJ; ++j) {  // clamped, unconditional loads (see the codes)
-        const int c = k0 * 64 + 8 * min(64 * j + lane, nk * 8 - 1);
-        dva[j] = *reinterpret_cast<const float4*>(dinv + c);
-        dvb[j] = *reinterpret_cast<const float4*>(dinv + c + 4);
-#pragma unroll
-        for (int t = 0; t < kFuseMaxT; ++t) xraw[j][t].load(Xr + (int64_t)min(t, T - 1) * ldx + c);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
     // the pre-scaled input of the next kXAhead steps in flight (from L2,
-    // requested before the codes; on the fused path from LDS, once written)
+    // requested before the codes)
     h8 xr[kXAhead][4][NF];
-    if constexpr (!FUSED) {
 #pragma unroll
-      for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
+    __builtin_amdgcn_sched_barrier(0);
     // codes of up to kRound steps in flight at once
     CodeStep<Q> cs[kRound];
 #pragma unroll
     for (int i = 0; i < kRound; ++i)  // (unconditional: a load under a branch costs a full wait)
       cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, ke - 1) * 32 * SW, hh);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (FUSED) {
-      // pre-scale into the wave's LDS slice with the prescale pass's
-      // arithmetic: fp16(fp32(x) * D^(-1/2)), channel order kept
-      // (every slot of the slice is written, the unused ones with copies: a
-      // store under a branch would let the compiler sink the loads)
-#pragma unroll
-      for (int j = 0; j < kPJ; ++j) {
-        const float dv[8] = {dva[j].x, dva[j].y, dva[j].z, dva[j].w, dvb[j].x, dvb[j].y, dvb[j].z, dvb[j].w};
-#pragma unroll
-        for (int t = 0; t < kFuseMaxT; ++t) {
-          float x[8];
-          xraw[j][t].get(x);
-          h8 o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (_Float16)(x[e] * dv[e]);
-          xsl[t * kRound * 8 + 64 * j + lane] = o;
-        }
-      }
-    }
-    if constexpr (FUSED) {
-#pragma unroll
-      for (int i = 0; i < kXAhead; ++i) load_x(min(k0 + i, ke - 1), xr[i]);
-    }
 
 #pragma unroll
     for (int i = 0; i < kRound; ++i) {
@@ -214,7 +156,9 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
         const h8 (&xb)[4][NF] = xr[i % kXAhead];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int grp = (k * 64 + 16 * s) / G - g0;
+          // (scales and zeros were copied to LDS before the codes were
+          // requested: read after this step's codes arrived)
+          const int grp = (k * 64 + 16 * s) / G - g0 + after_load(cs[i].a[0]);
           const _Float16 sv = ssc[grp * 32 + l32];
           const _Float16 nv = (_Float16)(-1024.0f) - szr[grp * 32 + l32];  // -(1024 + z), exact
           const h2 sc = {sv, sv}, nz = {nv, nv};
@@ -283,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Split-K form for kFuseMaxT < T <= kDecodeMaxT (r = 0, raw input).  With 32
+// Split-K form for kFewTokMaxT < T <= kDecodeMaxT (r = 0, raw input).  With 32
 // rows per workgroup every workgroup re-reads the whole input, T x d_in x 2
 // bytes from L2 (168 MB per call at T = 64 on the Qwen3-32B shape, six times
 // the packed weight).  Here workgroup (row group, split) covers 8 tiles = 256
@@ -301,6 +245,20 @@ __host__ __device__ inline int splitk_per(int ksteps) {
   const int ks0 = max(kWaves, (ksteps + kSplitPerMax - 1) / kSplitPerMax);
   return (ksteps + ks0 - 1) / ks0;
 }
+// Workgroup b of a 1-D grid of groups x parts -> (group, part).  Workgroups
+// are dispatched to the 8 XCDs round-robin (b % 8); when the group count is a
+// multiple of 8 every part of a group lands on the XCD of the group (group %
+// 8), so what the parts of a group write stays in that XCD's L2 for the
+// kernel that reads it back.
+struct GroupPart {
+  int group, part;
+};
+__host__ __device__ inline GroupPart xcd_group_part(int b, int groups, int parts) {
+  if (groups % 8 != 0) return {b / parts, b % parts};
+  const int xcd = b % 8, j = b / 8;
+  return {xcd + 8 * (j / parts), j % parts};
+}
+
 __host__ __device__ inline int splitk_count(int ksteps) {
   const int per = splitk_per(ksteps);
   return (ksteps + per - 1) / per;
@@ -324,9 +282,11 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
   const int ksteps = d_in / 64, ng = d_in / G, ntiles = d_out / 32;
   const int per = splitk_per(ksteps);
-  const int k0 = blockIdx.y * per, nk = min(per, ksteps - k0);  // nk >= 1
-  const bool tile_ok = (int)blockIdx.x * kWaves + wave < ntiles;
-  const int nt = min((int)blockIdx.x * kWaves + wave, ntiles - 1);  // waves past the end duplicate, never store
+  const GroupPart gp = xcd_group_part(blockIdx.x, (ntiles + kWaves - 1) / kWaves, splitk_count(ksteps));
+  const int split = gp.part;
+  const int k0 = split * per, nk = min(per, ksteps - k0);  // nk >= 1
+  const bool tile_ok = gp.group * kWaves + wave < ntiles;
+  const int nt = min(gp.group * kWaves + wave, ntiles - 1);  // waves past the end duplicate, never store
 
   uint32_t mask = ((1u << Q) - 1u) * 0x00010001u;  // code bits in both halves
   uint32_t magic = 0x64006400u;
@@ -410,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
       const int k = k0 + i;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int grp = (k * 64 + 16 * s4) / G - g0;
+        const int grp = (k * 64 + 16 * s4) / G - g0 + after_load(cs[i].a[0]);
         const _Float16 sv = ssc[grp * 32 + l32];
         const _Float16 nv = (_Float16)(-1024.0f) - szr[grp * 32 + l32];  // -(1024 + z), exact
         const h2 sc = {sv, sv}, nz = {nv, nv};
@@ -438,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
     for (int f = 0; f < NF; ++f) {
       const int t = 32 * f + l32;
       if (t < T) {
-        float* pr = P + ((int64_t)blockIdx.y * T + t) * d_out + nt * 32 + 4 * hh;
+        float* pr = P + ((int64_t)split * T + t) * d_out + nt * 32 + 4 * hh;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4)
           *reinterpret_cast<float4*>(pr + 8 * e4) =
@@ -448,30 +408,41 @@ __global__ __launch_bounds__(kThreads) void wlowbit_decode_splitk_kernel(
   }
 }
 
-// Y[t][n] = sum of the splits' partials, in split order.  Up to 8 splits
-// (d_in <= 5120) all partials of a thread are requested at once.
+// Y[t][n] = sum of the splits' partials, in split order.  Workgroup b takes
+// part of the outputs of one 256-row group (kReduceParts parts per group),
+// on the XCD whose L2 holds that group's partials (xcd_group_part); each
+// thread adds kReduceVec float4 of outputs, every split's partial requested
+// before any is added (up to 8 splits).
+constexpr int kReduceParts = 8;
+constexpr int kReduceThreads = 256;
 template <typename TY>
-__global__ __launch_bounds__(64) void splitk_reduce_kernel(int T, int d_out, int KS, const float* __restrict__ P,
-                                                           TY* __restrict__ Y, int64_t ldy) {
-  const int n4s = d_out / 4;
-  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (i >= (int64_t)T * n4s) return;
-  const int t = (int)(i / n4s), n4 = (int)(i % n4s);
-  const int64_t sstride = (int64_t)T * n4s;  // float4 between consecutive splits
-  const float4* p0 = reinterpret_cast<const float4*>(P) + (int64_t)t * n4s + n4;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](const float4& p) { v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w; };
-  if (KS <= 8) {
-    float4 p[8];
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(int T, int d_out, int KS,
+                                                                       const float* __restrict__ P,
+                                                                       TY* __restrict__ Y, int64_t ldy) {
+  const int groups = (d_out / 32 + kWaves - 1) / kWaves;
+  const GroupPart gp = xcd_group_part(blockIdx.x, groups, kReduceParts);
+  const int n0 = gp.group * 256;                  // first row of the group
+  const int rows4 = min(256, d_out - n0) / 4;     // float4 per token row of the group
+  const int per = (T * rows4 + kReduceParts - 1) / kReduceParts;
+  const int i0 = gp.part * per, i1 = min(i0 + per, T * rows4);
+  const int64_t sstride = (int64_t)T * (d_out / 4);  // float4 between consecutive splits
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += kReduceThreads) {
+    const int t = i / rows4, n4 = n0 / 4 + i % rows4;
+    const float4* p0 = reinterpret_cast<const float4*>(P) + (int64_t)t * (d_out / 4) + n4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](const float4& p) { v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w; };
+    if (KS <= 8) {
+      float4 p[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) p[s] = p0[min(s, KS - 1) * sstride];
+      for (int s = 0; s < 8; ++s) p[s] = p0[min(s, KS - 1) * sstride];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < KS) add(p[s]);
-  } else {
-    for (int s = 0; s < KS; ++s) add(p0[s * sstride]);
+      for (int s = 0; s < 8; ++s)
+        if (s < KS) add(p[s]);
+    } else {
+      for (int s = 0; s < KS; ++s) add(p0[s * sstride]);
+    }
+    store4<TY>(Y + (int64_t)t * ldy + 4 * n4, v);
   }
-  store4<TY>(Y + (int64_t)t * ldy + 4 * n4, v);
 }
 
 template <int Q, int G, typename TY, bool LR>
@@ -483,59 +454,13 @@ hipError_t launch_nf(int T, int d_in, int d_out, const void* Xs, int64_t ldxs, c
   const _Float16* sc = static_cast<const _Float16*>(scales);
   const _Float16* ze = static_cast<const _Float16*>(zeros);
   TY* y = static_cast<TY*>(Y);
-  const void* none = nullptr;
   if (T <= 32)
-    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 1, void>), grid, dim3(kThreads), 0, s, T, d_in, d_out,
-                       xs, ldxs, none, (int64_t)0, (const float*)nullptr, codes, sc, ze, B, Z, y, ldy);
+    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 1>), grid, dim3(kThreads), 0, s, T, d_in, d_out, xs,
+                       ldxs, codes, sc, ze, B, Z, y, ldy);
   else
-    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 2, void>), grid, dim3(kThreads), 0, s, T, d_in, d_out,
-                       xs, ldxs, none, (int64_t)0, (const float*)nullptr, codes, sc, ze, B, Z, y, ldy);
+    hipLaunchKernelGGL((wlowbit_decode_kernel<Q, G, TY, LR, 2>), grid, dim3(kThreads), 0, s, T, d_in, d_out, xs,
+                       ldxs, codes, sc, ze, B, Z, y, ldy);
   return hipGetLastError();
-}
-
-// raw input, r = 0, T <= kFuseMaxT: Y has the input's dtype
-template <int Q, typename TX>
-hipError_t launch_fused(int g, int T, int d_in, int d_out, const void* X, int64_t ldx, const float* dinv,
-                        const uint32_t* codes, const void* scales, const void* zeros, void* Y, int64_t ldy,
-                        hipStream_t s) {
-  const dim3 grid((unsigned)(d_out / 32));
-  const _Float16* none = nullptr;
-  const TX* x = static_cast<const TX*>(X);
-  const _Float16* sc = static_cast<const _Float16*>(scales);
-  const _Float16* ze = static_cast<const _Float16*>(zeros);
-  TX* y = static_cast<TX*>(Y);
-  const float* nf = nullptr;
-  switch (g) {
-    case 16:
-      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 16, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
-                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
-      break;
-    case 32:
-      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 32, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
-                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
-      break;
-    case 64:
-      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 64, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
-                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
-      break;
-    default:
-      hipLaunchKernelGGL((wlowbit_decode_kernel<Q, 128, TX, false, 1, TX>), grid, dim3(kThreads), 0, s, T, d_in,
-                         d_out, none, (int64_t)0, x, ldx, dinv, codes, sc, ze, nf, nf, y, ldy);
-      break;
-  }
-  return hipGetLastError();
-}
-
-template <typename TX>
-hipError_t launch_fused_q(int q, int g, int T, int d_in, int d_out, const void* X, int64_t ldx,
-                          const float* dinv, const uint32_t* codes, const void* scales, const void* zeros,
-                          void* Y, int64_t ldy, hipStream_t s) {
-  switch (q) {
-    case 2: return launch_fused<2, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
-    case 3: return launch_fused<3, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
-    case 5: return launch_fused<5, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
-    default: return launch_fused<4, TX>(g, T, d_in, d_out, X, ldx, dinv, codes, scales, zeros, Y, ldy, s);
-  }
 }
 
 template <int Q, int G, typename TY>
@@ -576,7 +501,8 @@ hipError_t launch_splitk_g(int T, int d_in, int d_out, const void* X, int64_t ld
                            const uint32_t* codes, const void* scales, const void* zeros, void* Y, int64_t ldy,
                            float* P, hipStream_t s) {
   const int ksteps = d_in / 64;
-  const dim3 grid((unsigned)((d_out / 32 + kWaves - 1) / kWaves), (unsigned)splitk_count(ksteps));
+  const int groups = (d_out / 32 + kWaves - 1) / kWaves, splits = splitk_count(ksteps);
+  const dim3 grid((unsigned)(groups * splits));
   const TX* x = static_cast<const TX*>(X);
   const _Float16* sc = static_cast<const _Float16*>(scales);
   const _Float16* ze = static_cast<const _Float16*>(zeros);
@@ -588,9 +514,8 @@ hipError_t launch_splitk_g(int T, int d_in, int d_out, const void* X, int64_t ld
                        ldx, dinv, codes, sc, ze, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n4 = (int64_t)T * (d_out / 4);
-  hipLaunchKernelGGL((splitk_reduce_kernel<TX>), dim3((unsigned)((n4 + 63) / 64)), dim3(64), 0, s, T, d_out,
-                     (int)grid.y, (const float*)P, static_cast<TX*>(Y), ldy);
+  hipLaunchKernelGGL((splitk_reduce_kernel<TX>), dim3((unsigned)(groups * kReduceParts)), dim3(kReduceThreads), 0, s,
+                     T, d_out, splits, (const float*)P, static_cast<TX*>(Y), ldy);
   return hipGetLastError();
 }
 
@@ -625,18 +550,8 @@ hipError_t launch_wlowbit_decode(int64_t T, int d_in, int d_out, int q, int g, i
   return launch_q<_Float16>(q, g, r, (int)T, d_in, d_out, Xs, ldxs, codes, scales, zeros, B, Z, Y, ldy, s);
 }
 
-hipError_t launch_wlowbit_decode_raw(int64_t T, int d_in, int d_out, int q, int g, const void* X, bool x_f32,
-                                     int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
-                                     const void* scales, const void* zeros, void* Y, int64_t ldy,
-                                     hipStream_t s) {
-  if (T <= 0 || T > kFuseMaxT) return hipErrorInvalidValue;
-  if (x_f32)
-    return launch_fused_q<float>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
-  return launch_fused_q<_Float16>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, s);
-}
-
 size_t decode_splitk_ws_bytes(int64_t T, int d_in, int d_out) {
-  if (T <= kFuseMaxT || T > kDecodeMaxT) return 0;
+  if (T <= kFewTokMaxT || T > kDecodeMaxT) return 0;
   return (size_t)splitk_count(d_in / 64) * (size_t)T * (size_t)d_out * sizeof(float);
 }
 
@@ -644,7 +559,7 @@ hipError_t launch_wlowbit_decode_splitk(int64_t T, int d_in, int d_out, int q, i
                                         int64_t ldx, const float* dinvsqrt, const uint32_t* codes,
                                         const void* scales, const void* zeros, void* Y, int64_t ldy,
                                         void* workspace, hipStream_t s) {
-  if (T <= kFuseMaxT || T > kDecodeMaxT) return hipErrorInvalidValue;
+  if (T <= kFewTokMaxT || T > kDecodeMaxT) return hipErrorInvalidValue;
   float* P = static_cast<float*>(workspace);
   if (x_f32)
     return launch_splitk<float>(q, g, (int)T, d_in, d_out, X, ldx, dinvsqrt, codes, scales, zeros, Y, ldy, P, s);

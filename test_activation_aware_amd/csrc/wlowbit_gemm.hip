@@ -23,6 +23,9 @@ hipError_t launch_wlowbit_gemm(int64_t T, int d_in, int d_out, int q, int g, int
                                const void* zeros, const float* B, const float* Z, void* Y, bool y_f32,
                                int64_t ldy, hipStream_t s) {
   if (T == 1) return launch_wlowbit_gemv(d_in, d_out, q, g, r, Xs, codes, scales, zeros, B, Z, Y, y_f32, s);
+  if (T <= kFewTokMaxT)
+    return launch_wlowbit_fewtok(T, d_in, d_out, q, g, r, Xs, ldxs, nullptr, codes, scales, zeros, B, Z, Y, y_f32, ldy,
+                                 s);
   if (T <= kDecodeMaxT)
     return launch_wlowbit_decode(T, d_in, d_out, q, g, r, Xs, ldxs, codes, scales, zeros, B, Z, Y, y_f32, ldy, s);
   const GemmArgs a{T, d_in, d_out, Xs, ldxs, nullptr, codes, scales, zeros, B, Z, Y, ldy};

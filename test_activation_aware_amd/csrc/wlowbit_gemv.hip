@@ -158,7 +158,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void wlowbit_gemv_kernel(
           sx += psv[s];
           const int ch = k * 64 + 16 * s;  // first channel of the sub-step
           if ((ch + 16) % G == 0) {        // the group ends with this sub-step
-            const int grp = ch / G - g0;
+            // (scales and zeros were copied to LDS before the codes were
+            // requested: reading them after this step's codes arrived)
+            const int grp = ch / G - g0 + after_load(cs[i].a[0]);
             const float sv = (float)ssc[grp * 32 + l32];
             const float zv = 1024.f + (float)szr[grp * 32 + l32];
             y += sv * (t - zv * sx);
@@ -196,6 +198,192 @@ __global__ __launch_bounds__(64 * kMaxWaves) void wlowbit_gemv_kernel(
       }
     }
     Y[n] = (TY)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// A few tokens (2 <= T <= 16): the same layout of the work on the matrix
+// cores.  Per 16-channel sub-step one v_mfma_f32_32x32x16_f16 per wave, A =
+// the dequantised weights of the tile (lane layout of the codes), B = 16
+// channels of the wave's input slice for the T tokens (columns past T repeat
+// the last token and are never stored).  The input slice of a round (T rows
+// x nk steps x 64 channels, fp16) is copied into the wave's part of LDS by
+// direct-to-LDS loads before the codes are requested, 16-byte pieces of a
+// token's row XOR-swizzled by the token (conflict-free reads); the round's
+// step count is what fits the wave's part (6 KB, 4 KB for g = 16).
+// XMODE 0: the input is the pre-scaled Xs.  XMODE 1: the raw fp16 X, with
+// D^(-1/2) applied to each dequantised weight pair as
+// fp16(fp16((c - z) s) * fp16(d^(-1/2))), the prefill kernel's effective
+// weight.  The 16 waves' 32 x 32 partial tiles meet in LDS; thread (token,
+// row) adds them in wave order.
+// ---------------------------------------------------------------------------
+// per wave: the round's input slice (less for g = 16, whose scales and
+// zeros take more room)
+__host__ __device__ constexpr int fewtok_xs_bytes(int G) { return G == 16 ? 4096 : 6144; }
+
+__host__ __device__ inline int fewtok_round(int T, int G) {
+  const int kr = fewtok_xs_bytes(G) / (128 * T);  // steps of 64 channels x T tokens x 2 bytes
+  return kr > kRound ? kRound : kr;
+}
+
+template <int Q, int G, typename TY, bool LOWRANK, int XMODE>
+__global__ __launch_bounds__(64 * kMaxWaves) void wlowbit_fewtok_kernel(
+    int T, int d_in, int per, const _Float16* X, int64_t ldx, const _Float16* __restrict__ dinv16,
+    const uint32_t* codes, const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    const float* __restrict__ Bf, const float* __restrict__ Z, TY* __restrict__ Y, int64_t ldy) {
+  constexpr int SW = 2 * Q;
+  constexpr int kXsBytes = fewtok_xs_bytes(G);
+  // groups of a round (rounds start at a group boundary unless G > 64), in
+  // 16-byte pieces, rounded up to whole 64-lane DMA instructions (lanes past
+  // the round's pieces copy the last one)
+  constexpr int kSzPieces = (((kRound * 64 + G - 1) / G + (G > 64 ? 1 : 0)) * 4 + 63) / 64 * 64;
+  constexpr int kRedBytes = kMaxWaves * 64 * 17 * 4;  // the partial tiles, lane rows padded to 17 floats
+  constexpr int kXBytes = kMaxWaves * kXsBytes;
+  // one LDS object for everything the direct-to-LDS loads write (the input
+  // slices, then the scales and zeros, then, XMODE 1, the round's fp16
+  // D^(-1/2)), per wave
+  constexpr int kSgBytes = kMaxWaves * 2 * kSzPieces * 16;
+  constexpr int kDvBytes = XMODE == 1 ? kMaxWaves * 1024 : 0;
+  static_assert(kRedBytes <= kXBytes + kSgBytes, "the partial tiles reuse the LDS of the slices and scales");
+  __shared__ __attribute__((aligned(16))) char xbuf[kXBytes + kSgBytes + kDvBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int nt = blockIdx.x;
+  const int ksteps = d_in / 64;
+  const int ng = d_in / G;
+  const int kr = fewtok_round(T, G);
+
+  uint32_t mask = ((1u << Q) - 1u) * 0x00010001u;
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(mask), "+v"(magic));
+
+  const int kb = min(wave * per, ksteps), ke = min(kb + per, ksteps);
+  const uint32_t* ctile = codes + (int64_t)nt * ksteps * 32 * SW + l32 * SW;
+  const _Float16* stile = scales + (int64_t)nt * ng * 32;
+  const _Float16* ztile = zeros + (int64_t)nt * ng * 32;
+  _Float16* ssc = reinterpret_cast<_Float16*>(xbuf + kXBytes + wave * 2 * kSzPieces * 16);
+  _Float16* szr = ssc + kSzPieces * 8;
+  _Float16* dvw = reinterpret_cast<_Float16*>(xbuf + kXBytes + kSgBytes + (XMODE == 1 ? wave * 1024 : 0));
+  char* xw = xbuf + wave * kXsBytes;
+  const int tl = min(l32, T - 1);  // this lane's token column
+
+  f16x acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  for (int k0 = kb; k0 < ke; k0 += kr) {
+    const int nk = min(kr, ke - k0);
+    const int rowp = nk * 8;  // 16-byte pieces per token row of the slice
+    const int g0 = (k0 * 64) / G, g1 = ((k0 + nk) * 64 - 1) / G;
+    const int pieces = (g1 - g0 + 1) * 4;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous round's LDS reads are done
+    {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stile + (int64_t)g0 * 32, (int64_t)pieces * 16);
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(ztile + (int64_t)g0 * 32, (int64_t)pieces * 16);
+#pragma unroll
+      for (int j = 0; j < kSzPieces / 64; ++j) {
+        const int voff = min(64 * j + lane, pieces - 1) * 16;
+        lds_dma16(rs, voff, ssc + 64 * j * 8);
+        lds_dma16(rz, voff, szr + 64 * j * 8);
+      }
+      if constexpr (XMODE == 1) {
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dinv16 + (int64_t)k0 * 64, (int64_t)nk * 128);
+        lds_dma16(rd, min(lane, rowp - 1) * 16, dvw);
+      }
+      // the input slice: slot j of the wave's part holds token t = j / rowp,
+      // piece (i, c ^ (t & 7)) for j % rowp = 8 i + c (i = step of the round,
+      // c = 8-channel piece of the step); slots past T rows read clamped
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, ((int64_t)(T - 1) * ldx + d_in) * 2);
+      const int nslot = T * rowp;
+      for (int j0 = 0; j0 < nslot; j0 += 64) {
+        const int j = min(j0 + lane, nslot - 1);
+        const int t = j / rowp, rem = j - t * rowp;
+        const int ch = (k0 + (rem >> 3)) * 64 + 8 * ((rem & 7) ^ (t & 7));
+        lds_dma16(rx, (int)(((int64_t)t * ldx + ch) * 2), xw + j0 * 16);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    CodeStep<Q> cs[kRound];
+#pragma unroll
+    for (int i = 0; i < kRound; ++i) cs[i] = load_codes<Q>(ctile + (int64_t)min(k0 + i, k0 + nk - 1) * 32 * SW, hh);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int i = 0; i < kRound; ++i) {
+      if (i < nk) {
+        const int k = k0 + i;
+        // the step's LDS reads (scales, zeros, D^(-1/2), input slice) wait for
+        // its codes, which arrive after the round's direct-to-LDS copies
+        const int tie = after_load(cs[i].a[0]);
+        const _Float16* sst = ssc + tie;
+        const _Float16* szt = szr + tie;
+        const char* xwt = xw + tie;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int grp = (k * 64 + 16 * s) / G - g0;
+          const _Float16 sv = sst[grp * 32 + l32];
+          const _Float16 nv = (_Float16)(-1024.0f) - szt[grp * 32 + l32];  // -(1024 + z), exact
+          const h2 sc = {sv, sv}, nz = {nv, nv};
+          uint32_t pr[4];
+          code_pairs<Q>(cs[i], s, hh, mask, magic, pr);
+          h8 dv;
+          if constexpr (XMODE == 1) dv = *reinterpret_cast<const h8*>(dvw + tie + i * 64 + 16 * s + 8 * hh);
+          h8 a;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            h2 wv = (as_h2(pr[j]) + nz) * sc;
+            if constexpr (XMODE == 1) wv = wv * h2{dv[2 * j], dv[2 * j + 1]};
+            a[2 * j] = wv[0];
+            a[2 * j + 1] = wv[1];
+          }
+          const int piece = 8 * i + ((2 * s + hh) ^ (tl & 7));
+          const h8 b = *reinterpret_cast<const h8*>(xwt + (tl * rowp + piece) * 16);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if constexpr (LOWRANK) {
+    if (wave == 0) {
+      // + B Z: B (fp16) x Z split in two fp16 parts
+      const int n = nt * 32 + l32;
+      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
+      const float4 b0 = bp[0], b1 = bp[1];
+      const h8 bfr = {(_Float16)b0.x, (_Float16)b0.y, (_Float16)b0.z, (_Float16)b0.w,
+                      (_Float16)b1.x, (_Float16)b1.y, (_Float16)b1.z, (_Float16)b1.w};
+      const float4* zp = reinterpret_cast<const float4*>(Z + (int64_t)tl * 16 + 8 * hh);
+      const float4 z0 = zp[0], z1 = zp[1];
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      h8 zh, zl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hv = (_Float16)zv[e];
+        zh[e] = hv;
+        zl[e] = (_Float16)(zv[e] - (float)hv);
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr, zh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr, zl, acc, 0, 0, 0);
+    }
+  }
+
+  // ---- the waves' 32 x 32 partial tiles, added in wave order ----
+  __syncthreads();  // every wave is done with its input slice
+  float* red = reinterpret_cast<float*>(xbuf);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[(wave * 64 + lane) * 17 + e] = acc[e];
+  __syncthreads();
+  // thread (token j, row i): accumulator lane j + 32 ((i / 4) % 2), value
+  // (i / 8) * 4 + i % 4 of each wave
+  for (int idx = threadIdx.x; idx < T * 32; idx += blockDim.x) {
+    const int j = idx >> 5, i = idx & 31;
+    const int src = (j + 32 * ((i >> 2) & 1)) * 17 + (i >> 3) * 4 + (i & 3);
+    float v = 0.f;
+    for (int w = 0; w < nwaves; ++w) v += red[w * 64 * 17 + src];
+    Y[(int64_t)j * ldy + nt * 32 + i] = (TY)v;
   }
 }
 
@@ -245,6 +433,49 @@ hipError_t launch_qg(int q, int g, int d_in, int d_out, const void* Xs, const vo
 }
 
 }  // namespace
+
+hipError_t launch_wlowbit_fewtok(int64_t T, int d_in, int d_out, int q, int g, int r, const void* X, int64_t ldx,
+                                 const void* dinv16, const uint32_t* codes, const void* scales, const void* zeros,
+                                 const float* B, const float* Z, void* Y, bool y_f32, int64_t ldy, hipStream_t s) {
+  if (T < 2 || T > kFewTokMaxT || (dinv16 && y_f32)) return hipErrorInvalidValue;
+  const Shape sh = gemv_shape(d_in);
+  const dim3 grid((unsigned)(d_out / 32)), block(64 * sh.nw);
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const _Float16* dv = static_cast<const _Float16*>(dinv16);
+  const _Float16* sc = static_cast<const _Float16*>(scales);
+  const _Float16* ze = static_cast<const _Float16*>(zeros);
+#define TTQ_FT(QQ, GG, TY, LR, XM)                                                                           \
+  hipLaunchKernelGGL((wlowbit_fewtok_kernel<QQ, GG, TY, LR, XM>), grid, block, 0, s, (int)T, d_in, sh.per, x, ldx, \
+                     dv, codes, sc, ze, B, Z, static_cast<TY*>(Y), ldy)
+#define TTQ_FT_G(QQ)                                                                                           \
+  switch (g) {                                                                                                 \
+    case 16: TTQ_FT_FORM(QQ, 16); break;                                                                       \
+    case 32: TTQ_FT_FORM(QQ, 32); break;                                                                       \
+    case 64: TTQ_FT_FORM(QQ, 64); break;                                                                       \
+    default: TTQ_FT_FORM(QQ, 128); break;                                                                      \
+  }
+#define TTQ_FT_FORM(QQ, GG)                                    \
+  if (dv) {                                                    \
+    if (r > 0) TTQ_FT(QQ, GG, _Float16, true, 1);              \
+    else TTQ_FT(QQ, GG, _Float16, false, 1);                   \
+  } else if (y_f32) {                                          \
+    if (r > 0) TTQ_FT(QQ, GG, float, true, 0);                 \
+    else TTQ_FT(QQ, GG, float, false, 0);                      \
+  } else {                                                     \
+    if (r > 0) TTQ_FT(QQ, GG, _Float16, true, 0);              \
+    else TTQ_FT(QQ, GG, _Float16, false, 0);                   \
+  }
+  switch (q) {
+    case 2: TTQ_FT_G(2) break;
+    case 3: TTQ_FT_G(3) break;
+    case 5: TTQ_FT_G(5) break;
+    default: TTQ_FT_G(4) break;
+  }
+#undef TTQ_FT_FORM
+#undef TTQ_FT_G
+#undef TTQ_FT
+  return hipGetLastError();
+}
 
 hipError_t launch_wlowbit_gemv(int d_in, int d_out, int q, int g, int r, const void* Xs, const uint32_t* codes,
                                const void* scales, const void* zeros, const float* B, const float* Z, void* Y,

@@ -63,9 +63,10 @@ def test_query_sizes_cfg5(lib):
     assert sz.wres_bytes == 0
     assert sz.workspace_bytes == lib.ttq_colstats_workspace_bytes(16384, 5120) > 0
     assert sz.linear_workspace_bytes == lib.ttq_linear_workspace_bytes(16384, 5120, 8192, 0) == 16384 * 5120 * 2
-    # a few tokens (4 < T <= 64, r = 0): fp32 partials of 8 K splits, when larger than the pre-scaled input
+    # a few tokens (16 < T <= 64, r = 0): fp32 partials of 8 K splits, when larger than the pre-scaled input
     assert lib.ttq_linear_workspace_bytes(64, 5120, 8192, 0) == 8 * 64 * 8192 * 4
-    assert lib.ttq_linear_workspace_bytes(5, 5120, 8192, 0) == 8 * 5 * 8192 * 4
+    assert lib.ttq_linear_workspace_bytes(17, 5120, 8192, 0) == 8 * 17 * 8192 * 4
+    assert lib.ttq_linear_workspace_bytes(16, 5120, 8192, 0) == (16 * 5120 * 2 + 255) // 256 * 256
     assert lib.ttq_linear_workspace_bytes(4, 5120, 8192, 0) == (4 * 5120 * 2 + 255) // 256 * 256
     assert lib.ttq_linear_workspace_bytes(65, 5120, 8192, 0) == (65 * 5120 * 2 + 255) // 256 * 256
     assert lib.ttq_linear_workspace_bytes(64, 5120, 8192, 16) == 64 * 5120 * 2 + 64 * 16 * 4
