@@ -196,15 +196,20 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
  * quantisation.  fp16 input with T > 64: ttq_lowrank_z into `workspace`
- * when r > 0, then ttq_wlowbit_gemm_raw on X itself (D^(-1/2) applied to the
- * dequantised weights, with the fp16 copy ttq_prepare wrote).  fp32 input,
- * or r > 0 with T <= 64: ttq_prescale (fused with ttq_lowrank_z when r > 0:
- * one read of X) into `workspace`, then ttq_wlowbit_gemm.  With r = 0 and
- * few tokens the input is pre-scaled inside the projection kernels (the same
- * arithmetic): T <= 4, one kernel, `workspace` untouched; 4 < T <= 64, a
- * split-K kernel whose 256-row workgroups share their input slice, fp32
- * partial products in `workspace`, then a reduction in a fixed order (for
- * d_in <= 5120 the output equals ttq_wlowbit_gemm's bit for bit).
+ * when r > 0, then the dense GEMM on the effective weight the last prepare
+ * formed (ttq_wexp_gemm; prompts of at least ttq_dense_min_tokens(d_out)
+ * tokens on a handle with a wexp buffer) or ttq_wlowbit_gemm_raw on X itself
+ * (D^(-1/2) applied to the dequantised weights, with the fp16 copy
+ * ttq_prepare wrote).  r = 0, T = 1: one dot-product kernel that pre-scales
+ * the input itself (the same bits as ttq_prescale + ttq_wlowbit_gemm).  fp16
+ * input, 2 <= T <= 16: one few-token kernel on X with D^(-1/2) on the weight
+ * side (Z first when r > 0).  r = 0, 16 < T <= 64: a split-K kernel whose
+ * 256-row workgroups share their input slice, fp32 partial products in
+ * `workspace`, then a reduction in a fixed order (for d_in <= 5120 the
+ * output equals ttq_wlowbit_gemm's bit for bit).  Otherwise (fp32 input, or
+ * r > 0 with T <= 64 outside the cases above): ttq_prescale (fused with
+ * ttq_lowrank_z when r > 0: one read of X) into `workspace`, then
+ * ttq_wlowbit_gemm.
  * workspace: device memory of at least
  * ttq_linear_workspace_bytes(T, d_in, d_out, r) bytes, owned by the caller
  * (required for every T >= 1); the handle itself is only read, so calls on
