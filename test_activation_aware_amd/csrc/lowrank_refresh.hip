@@ -37,7 +37,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kR = 16;          // rank
 constexpr int kPCols = 128;     // channels per P-partial workgroup
-constexpr int kPRows = 1024;    // rows per P-partial chunk
+constexpr int kPRows = 512;     // rows per P-partial chunk
+constexpr int kPAhead = 8;      // 4-row slices whose loads a wave has in flight
 constexpr int kGramCols = 64;   // channels per finalize workgroup
 
 // Vs[k][j] = sqrt(D_j) V[j][k]: the weighted basis in the [16][d_in] layout
@@ -64,17 +65,20 @@ __global__ __launch_bounds__(256) void p_partial_kernel(int d_out, int d_in, con
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
   const _Float16* wp = W + (int64_t)cb + 8 * cl;
-  // 4-row slices n = r0 + 4 (wave + 4 i), two slices' loads in flight
+  // 4-row slices n = r0 + 4 (wave + 4 i), kPAhead slices' loads in flight
   int n = r0 + 4 * wave;
-  for (; n + 16 < r1; n += 32) {
-    const h8 wa = *reinterpret_cast<const h8*>(wp + (int64_t)(n + rl) * d_in);
-    const float ga = G[(int64_t)(n + rl) * kR + cl];
-    const h8 wb = *reinterpret_cast<const h8*>(wp + (int64_t)(n + 16 + rl) * d_in);
-    const float gb = G[(int64_t)(n + 16 + rl) * kR + cl];
+  for (; n + 16 * (kPAhead - 1) < r1; n += 16 * kPAhead) {
+    h8 wa[kPAhead];
+    float ga[kPAhead];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga, (float)wa[e], acc[e], 0, 0, 0);
+    for (int u = 0; u < kPAhead; ++u) {
+      wa[u] = *reinterpret_cast<const h8*>(wp + (int64_t)(n + 16 * u + rl) * d_in);
+      ga[u] = G[(int64_t)(n + 16 * u + rl) * kR + cl];
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(gb, (float)wb[e], acc[e], 0, 0, 0);
+    for (int u = 0; u < kPAhead; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[u], (float)wa[u][e], acc[e], 0, 0, 0);
   }
   for (; n < r1; n += 16) {  // d_out is a multiple of 32: whole 4-row slices
     const h8 wa = *reinterpret_cast<const h8*>(wp + (int64_t)(n + rl) * d_in);
@@ -116,7 +120,15 @@ __global__ __launch_bounds__(256) void p_final_gram_kernel(int d_in, int chunks,
   for (int i = 0; i < 4; ++i) {
     const int k = 4 * kq + i;
     double s = 0.0;
-    for (int c = 0; c < chunks; ++c) s += (double)partial[((int64_t)c * kR + k) * d_in + j];
+    int c = 0;
+    for (; c + 8 <= chunks; c += 8) {  // eight chunks' loads in flight, added in chunk order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = partial[((int64_t)(c + u) * kR + k) * d_in + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)v[u];
+    }
+    for (; c < chunks; ++c) s += (double)partial[((int64_t)c * kR + k) * d_in + j];
     const double pv = sq * s;
     ps[jl][k] = pv;
     P[(int64_t)j * kR + k] = pv;
@@ -147,8 +159,17 @@ __global__ __launch_bounds__(256) void cholesky_kernel(int blocks, const double*
   __shared__ double R[kR][kR];
   const int t = threadIdx.x;
   const int a = t >> 4, b = t & 15;
+  // (eight parts' loads in flight at a time, added in part order)
   double s = 0.0;
-  for (int q = 0; q < blocks; ++q) s += gram_part[((int64_t)q * kR + a) * kR + b];
+  int q = 0;
+  for (; q + 8 <= blocks; q += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = gram_part[((int64_t)(q + u) * kR + a) * kR + b];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; q < blocks; ++q) s += gram_part[((int64_t)q * kR + a) * kR + b];
   g[a][b] = s;
   R[a][b] = 0.0;
   __syncthreads();

@@ -199,17 +199,21 @@ hipError_t launch_tx(int64_t T, int d, const void* X, int64_t ldx, const float* 
                        dim3(256), 0, s, T, d, x, ldx, dinv, xs);
     return hipGetLastError();
   }
-  // 64 tokens per workgroup while that still leaves a workgroup per CU, else 16
-  const bool wide = T >= 64 * 256;
-  const dim3 grid((unsigned)((T + kTok * (wide ? 4 : 1) - 1) / (kTok * (wide ? 4 : 1))));
+  // 64 tokens per workgroup while that still leaves a workgroup per CU, else
+  // (Z alone) 32 from two workgroups per CU on, else 16: every workgroup reads
+  // all of A from L2, so fewer, wider workgroups read less of it
+  const int tg = T >= 64 * 256 ? 4 : (!Xs && T >= 32 * 256 ? 2 : 1);
+  const dim3 grid((unsigned)((T + kTok * tg - 1) / (kTok * tg)));
   if (Xs) {
-    if (wide)
+    if (tg == 4)
       hipLaunchKernelGGL((prescale_z_kernel<TX, true, true, 4>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
     else
       hipLaunchKernelGGL((prescale_z_kernel<TX, true, true, 1>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
   } else {
-    if (wide)
+    if (tg == 4)
       hipLaunchKernelGGL((prescale_z_kernel<TX, false, true, 4>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
+    else if (tg == 2)
+      hipLaunchKernelGGL((prescale_z_kernel<TX, false, true, 2>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
     else
       hipLaunchKernelGGL((prescale_z_kernel<TX, false, true, 1>), grid, dim3(256), 0, s, T, d, x, ldx, dinv, xs, A, Z);
   }

@@ -260,7 +260,7 @@ def test_residual_bitexact_cfg5_shape():
     assert Rg.view(np.uint16).tobytes() == R0.view(np.uint16).tobytes()
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 2048), (4, 333), (5, 16384), (1, 100)])
+@pytest.mark.parametrize("cfg,T", [(2, 2048), (4, 333), (5, 16384), (1, 100), (5, 8192), (4, 9001)])
 def test_lowrank_z(cfg, T):
     X, W = cfg_inputs(cfg, T=T, d_out=64)
     A = (np.random.default_rng(cfg).standard_normal((16, X.shape[1])) * 0.02).astype(np.float32)
