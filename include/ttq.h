@@ -126,7 +126,11 @@ typedef struct ttq_sizes {
  * ttq_dense_min_tokens(d_out) tokens also writes W_hat, and projections of
  * that many fp16 tokens run a dense fp16 GEMM on it: the dequantisation is
  * done once per prompt instead of once per 256-token tile, with the same
- * outputs bit for bit. */
+ * outputs bit for bit.  With r = 16 the buffer receives fp16(W_hat + B A)
+ * instead (the fp32 sum rounded once; section 2's Y = W_hat X + B (A X) is
+ * (W_hat + B A) X), so that GEMM is the whole projection, with no A X; its
+ * outputs are then within the tolerance of the low-bit kernel's, not the
+ * same bits. */
 typedef struct ttq_buffers {
   uint32_t* codes;
   void* scales;
@@ -195,12 +199,12 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T,
  * X: device [T][ldx] of dtype xdt; Y: device [T][ldy] of the same dtype,
  * fp32 accumulation.  Any T >= 0; T = 0 enqueues nothing.  Used for the
  * prefill tokens and, unchanged, for decode batches that reuse the prefill
- * quantisation.  fp16 input with T > 64: ttq_lowrank_z into `workspace`
- * when r > 0, then the dense GEMM on the effective weight the last prepare
- * formed (ttq_wexp_gemm; prompts of at least ttq_dense_min_tokens(d_out)
- * tokens on a handle with a wexp buffer) or ttq_wlowbit_gemm_raw on X itself
- * (D^(-1/2) applied to the dequantised weights, with the fp16 copy
- * ttq_prepare wrote).  r = 0, T = 1: one dot-product kernel that pre-scales
+ * quantisation.  fp16 input with T > 64: the dense GEMM on the effective
+ * weight the last prepare formed (ttq_wexp_gemm, the rank-16 term already in
+ * the weight; prompts of at least ttq_dense_min_tokens(d_out) tokens on a
+ * handle with a wexp buffer), or ttq_lowrank_z into `workspace` when r > 0
+ * and then ttq_wlowbit_gemm_raw on X itself (D^(-1/2) applied to the
+ * dequantised weights, with the fp16 copy ttq_prepare wrote).  r = 0, T = 1: one dot-product kernel that pre-scales
  * the input itself (the same bits as ttq_prescale + ttq_wlowbit_gemm).  fp16
  * input, 2 <= T <= 16: one few-token kernel on X with D^(-1/2) on the weight
  * side (Z first when r > 0).  r = 0, 16 < T <= 64: a split-K kernel whose
@@ -225,13 +229,16 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
  * the quantisation parameters are computed from the prompt at prefill; the
  * projection of the prompt follows).  Writes D, D^(-1/2), codes, scales and
  * zeros into the handle (as ttq_prepare) and Y = the projection of X (as
- * ttq_linear).  With r = 16, fp16 input and T > 64 the column statistic and
- * Z = X A^T come from one read of X (the form the two separate calls cannot
- * use, since ttq_linear may see other inputs than the prompt); D and Z are
- * then summed in other fixed groupings than those of ttq_prepare and
- * ttq_linear and may differ from theirs in the last bits (D within 1e-5 of
- * the exact statistic either way, Z within fp32 rounding).  Otherwise it
- * is exactly ttq_prepare followed by ttq_linear.  workspace: device memory of
+ * ttq_linear).  With r = 16, fp16 input and 64 < T below the dense
+ * projection's length (ttq_dense_min_tokens, or any T when the handle has
+ * no wexp buffer) the column statistic and Z = X A^T come from one read of
+ * X (the form the two separate calls cannot use, since ttq_linear may see
+ * other inputs than the prompt); D and Z are then summed in other fixed
+ * groupings than those of ttq_prepare and ttq_linear and may differ from
+ * theirs in the last bits (D within 1e-5 of the exact statistic either way,
+ * Z within fp32 rounding).  Otherwise it is exactly ttq_prepare followed by
+ * ttq_linear (for a long prompt with r = 16: no Z at all, the rank-16 term
+ * being folded into the effective weight).  workspace: device memory of
  * at least ttq_prefill_workspace_bytes(T, d_in, d_out, r, xdt) bytes, owned
  * by the caller; the handle's own workspace is used too (by the statistic of
  * the unfused form).  1 <= T <= T_max; the input stride ldx must stay below

@@ -140,6 +140,19 @@ bool use_dense(const ttq_handle* h, ttq_dtype xdt, int64_t T) {
   return h->buf.wexp != nullptr && xdt == TTQ_F16 && T > ttq::kDecodeMaxT && T >= dense_min_tokens(h->cfg.d_out);
 }
 
+// Codes, scales and zeros of W_src D^(1/2) for the prompt just measured; for
+// a prompt that takes the dense projection also the effective weight, with
+// the rank-16 term folded in when r > 0 (fp16(W_hat + B A)), so that the
+// dense GEMM on it is the whole projection.
+hipError_t quantize(const ttq_handle* h, ttq_dtype xdt, int64_t T, const void* W_src, hipStream_t st) {
+  const ttq_config& c = h->cfg;
+  const bool expand = use_dense(h, xdt, T);
+  const bool fold = expand && c.r > 0;
+  return ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, W_src, h->buf.D, h->buf.codes, h->buf.scales,
+                                   h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr,
+                                   fold ? h->buf.B : nullptr, fold ? h->buf.A : nullptr, st);
+}
+
 size_t colstats_ws_bytes(int64_t T, int64_t d) {
   return (size_t)ttq::colstats_chunks(T < 1 ? 1 : T) * (size_t)d * sizeof(float);
 }
@@ -335,7 +348,7 @@ ttq_status ttq_quantize_pack(int32_t d_out, int32_t d_in, int32_t q, int32_t g, 
   TTQ_NEED(scales);
   TTQ_NEED(zeros);
   hipError_t e = ttq::launch_quantize_pack(d_out, d_in, q, g, W_src, D, codes, scales, zeros, nullptr, nullptr,
-                                           static_cast<hipStream_t>(stream));
+                                           nullptr, nullptr, static_cast<hipStream_t>(stream));
   return hip_status(e, "quantize_pack launch");
 }
 
@@ -449,12 +462,10 @@ ttq_status ttq_prepare(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
   hipError_t e = ttq::launch_colstats(X, xdt == TTQ_F32, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.D,
                                       h->buf.dinvsqrt, dinv16(h), h->buf.workspace, st);
   if (e != hipSuccess) return hip_status(e, "colstats launch");
-  const bool expand = use_dense(h, xdt, T);
-  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes, h->buf.scales,
-                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
+  e = quantize(h, xdt, T, h->wsrc, st);
   if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
   h->prepared = true;
-  h->wexp_valid = expand;
+  h->wexp_valid = use_dense(h, xdt, T);
   return ok();
 }
 
@@ -507,11 +518,9 @@ ttq_status ttq_linear(const ttq_handle* h, const void* X, ttq_dtype xdt, int64_t
   float* z = c.r > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + xs_bytes(T, c.d_in)) : nullptr;
   if (h->wexp_valid && use_dense(h, xdt, T)) {
     // a long prompt: the dense GEMM on the effective weight the last prepare
-    // formed (same results as the raw-input GEMM on the codes)
-    hipError_t e = hipSuccess;
-    if (c.r > 0) e = ttq::launch_prescale_z(T, c.d_in, X, false, ldx, h->buf.dinvsqrt, nullptr, h->buf.A, z, st);
-    if (e != hipSuccess) return hip_status(e, "lowrank_z launch");
-    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, st);
+    // formed (r = 0: the raw-input GEMM's results on the codes bit for bit;
+    // r > 0: B A is already in the weight)
+    hipError_t e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, 0, X, ldx, h->buf.wexp, nullptr, nullptr, Y, ldy, st);
     return hip_status(e, "dense_gemm launch");
   }
   if (xdt == TTQ_F16 && T > ttq::kDecodeMaxT) {
@@ -559,22 +568,25 @@ ttq_status ttq_prefill(ttq_handle* h, const void* X, ttq_dtype xdt, int64_t T, i
     return ttq_linear(h, X, xdt, T, ldx, Y, ldy, workspace, workspace_bytes, stream);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_dense(h, xdt, T)) {
+    // a long prompt: B A is folded into the effective weight, so the
+    // statistic, the quantisation and one dense GEMM are the whole step
+    s = ttq_prepare(h, X, xdt, T, ldx, stream);
+    if (s != TTQ_OK) return s;
+    hipError_t e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, 0, X, ldx, h->buf.wexp, nullptr, nullptr, Y, ldy, st);
+    return hip_status(e, "dense_gemm launch");
+  }
   float* partial = static_cast<float*>(workspace);
   float* z = reinterpret_cast<float*>(static_cast<char*>(workspace) + fused_partial_bytes(T, c.d_in));
   hipError_t e = ttq::launch_colstats_z(X, T, c.d_in, ldx, c.p, c.lambda, c.alpha, h->buf.A, h->buf.D,
                                         h->buf.dinvsqrt, dinv16(h), partial, z, st);
   if (e != hipSuccess) return hip_status(e, "colstats_z launch");
-  const bool expand = use_dense(h, xdt, T);
-  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->wsrc, h->buf.D, h->buf.codes, h->buf.scales,
-                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
+  e = quantize(h, xdt, T, h->wsrc, st);
   if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
   h->prepared = true;
-  h->wexp_valid = expand;
-  if (expand)
-    e = ttq::launch_dense_gemm(T, c.d_in, c.d_out, c.r, X, ldx, h->buf.wexp, h->buf.B, z, Y, ldy, st);
-  else
-    e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
-                                      h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
+  h->wexp_valid = false;
+  e = ttq::launch_wlowbit_gemm_rawx(T, c.d_in, c.d_out, c.q, c.g, c.r, X, ldx, dinv16(h), h->buf.codes,
+                                    h->buf.scales, h->buf.zeros, h->buf.B, z, Y, ldy, st);
   return hip_status(e, "projection launch");
 }
 
@@ -660,12 +672,10 @@ ttq_status ttq_prepare_refresh(ttq_handle* h, const void* X, ttq_dtype xdt, int6
   if (e != hipSuccess) return hip_status(e, "lowrank_refresh launch");
   e = ttq::launch_residual(c.d_out, c.d_in, c.r, h->w, B, A, h->buf.wres, st);
   if (e != hipSuccess) return hip_status(e, "residual launch");
-  const bool expand = use_dense(h, xdt, T);
-  e = ttq::launch_quantize_pack(c.d_out, c.d_in, c.q, c.g, h->buf.wres, h->buf.D, h->buf.codes, h->buf.scales,
-                                h->buf.zeros, expand ? dinv16(h) : nullptr, expand ? h->buf.wexp : nullptr, st);
+  e = quantize(h, xdt, T, h->buf.wres, st);
   if (e != hipSuccess) return hip_status(e, "quantize_pack launch");
   h->prepared = true;
-  h->wexp_valid = expand;
+  h->wexp_valid = use_dense(h, xdt, T);
   return ok();
 }
 

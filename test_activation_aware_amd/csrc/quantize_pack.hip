@@ -41,6 +41,15 @@
 // dense GEMM on W_hat gives that kernel's outputs bit for bit.  The values
 // replace the slab in LDS and leave as coalesced 16-byte stores.
 //
+// With the rank-r factors as well (LOWRANK, r = 16), the written weight is
+// fp16(W_hat + B A): Y = Q[(W - B A) D^(1/2)] D^(-1/2) X + B (A X) is
+// (W_hat + B A) X, so a dense GEMM on it needs no A X.  Each wave forms the
+// 32 x 64 piece of B A over its two channel blocks on the matrix cores,
+// v_mfma_f32_32x32x16_f16 on fp16 hi / lo splits of both factors
+// (B_hi A_hi + B_hi A_lo + B_lo A_hi, fp32 accumulation: within about 2^-21
+// of B A, far inside the final fp16 rounding), and adds it to W_hat in LDS
+// in fp32 before the one rounding to fp16.
+//
 // Codes take a reciprocal fast path.  With rcp = v_rcp_f32(s) (relative
 // error at most 2^-23) and u = fma(v, rcp, z), |u - (v/s + z)| < 2^-18
 // because |v/s + z| <= N + 1.  Whenever u is more than 2^-16 away from every
@@ -109,12 +118,16 @@ __device__ __forceinline__ constexpr int step_pos(int h, int w) {
 }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 
-template <int Q, int G, bool EXPAND>
+template <int Q, int G, bool EXPAND, bool LOWRANK>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const _Float16* __restrict__ W, const float* __restrict__ D, int d_in,
     uint32_t* __restrict__ codes, _Float16* __restrict__ scales, _Float16* __restrict__ zeros,
-    const _Float16* __restrict__ dinv16, _Float16* __restrict__ wexp) {
+    const _Float16* __restrict__ dinv16, _Float16* __restrict__ wexp, const float* __restrict__ Bf,
+    const float* __restrict__ Af) {
+  static_assert(EXPAND || !LOWRANK, "the low-rank term is folded into the effective weight only");
   constexpr int LPG = G >= 32 ? G / 32 : 1;  // blocks per group
   constexpr int SG = G < 32 ? 32 / G : 1;     // groups inside one block (g = 16: 2)
   constexpr int CPG = 32 / SG;                // channels of the block per such group
@@ -328,7 +341,68 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       outz[(bl / LPG) * 32 + r] = (_Float16)zf[0];
     }
   }
+  // LOWRANK: this lane's operands of its wave's B A piece, loaded once the
+  // quantisation no longer holds its registers.  Lane l (row l32 of the
+  // tile, factor half hh) holds B[row][8 hh .. 8 hh + 7] and, for each of the
+  // wave's two 32-channel blocks, A[8 hh .. 8 hh + 7][channel l32] (channels
+  // past the range clamped; their results are never used).
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  float4 bq[2];
+  float av[2][8];
+  if constexpr (LOWRANK) {
+    const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)(nt * 32 + l32) * 16 + 8 * hh);
+    bq[0] = bp[0];
+    bq[1] = bp[1];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int col = c0 + min(64 * wave + 32 * blk + l32, width - 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[blk][e] = Af[(int64_t)(8 * hh + e) * d_in + col];
+    }
+  }
   __syncthreads();
+
+  if constexpr (LOWRANK) {
+    // W_hat + B A over the wave's two blocks (the wave wrote W_hat of exactly
+    // these; the barrier above ordered those writes for the other lanes)
+    if (64 * wave < width) {
+      const float bv[8] = {bq[0].x, bq[0].y, bq[0].z, bq[0].w, bq[1].x, bq[1].y, bq[1].z, bq[1].w};
+      h8 bhi, blo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bhi[e] = (_Float16)bv[e];
+        blo[e] = (_Float16)(bv[e] - (float)bhi[e]);
+      }
+      f16x zero;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        h8 ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ahi[e] = (_Float16)av[blk][e];
+          alo[e] = (_Float16)(av[blk][e] - (float)ahi[e]);
+        }
+        // rows of the product = channels (A^T), columns = weight rows (B^T)
+        f16x acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhi, zero, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blo, acc, 0, 0, 0);
+        // lane: weight row l32, channels 8 (e / 4) + 4 hh + e % 4 of the block
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          _Float16* p = &wt[l32 * kRowPitch + 64 * wave + 32 * blk + 8 * e4 + 4 * hh];
+          const uint2 raw = *reinterpret_cast<const uint2*>(p);
+          const h2 w01 = __builtin_bit_cast(h2, raw.x), w23 = __builtin_bit_cast(h2, raw.y);
+          const h2 o01 = {(_Float16)((float)w01[0] + acc[4 * e4 + 0]), (_Float16)((float)w01[1] + acc[4 * e4 + 1])};
+          const h2 o23 = {(_Float16)((float)w23[0] + acc[4 * e4 + 2]), (_Float16)((float)w23[1] + acc[4 * e4 + 3])};
+          *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, o01), __builtin_bit_cast(uint32_t, o23));
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   if constexpr (EXPAND) {
     // W_hat rows of the slab, the load's piece order (one row per 16 lanes)
@@ -360,12 +434,13 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   }
 }
 
-template <int Q, bool EX>
+template <int Q, bool EX, bool LR>
 hipError_t launch_qe(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
-                     _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, hipStream_t s) {
+                     _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, const float* B,
+                     const float* A, hipStream_t s) {
   dim3 grid((unsigned)((d_in + kCols - 1) / kCols), (unsigned)(d_out / 32));
-#define TTQ_QP(GV) hipLaunchKernelGGL((quantize_pack_kernel<Q, GV, EX>), grid, dim3(kThreads), 0, s, W, D, d_in, \
-                                      codes, scales, zeros, dinv16, wexp)
+#define TTQ_QP(GV) hipLaunchKernelGGL((quantize_pack_kernel<Q, GV, EX, LR>), grid, dim3(kThreads), 0, s, W, D, d_in, \
+                                      codes, scales, zeros, dinv16, wexp, B, A)
   switch (g) {
     case 16: TTQ_QP(16); break;
     case 32: TTQ_QP(32); break;
@@ -378,26 +453,30 @@ hipError_t launch_qe(int d_out, int d_in, int g, const _Float16* W, const float*
 
 template <int Q>
 hipError_t launch_q(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
-                    _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, hipStream_t s) {
-  if (wexp != nullptr) return launch_qe<Q, true>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, s);
-  return launch_qe<Q, false>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, s);
+                    _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, const float* B,
+                    const float* A, hipStream_t s) {
+  if (wexp != nullptr && B != nullptr)
+    return launch_qe<Q, true, true>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, B, A, s);
+  if (wexp != nullptr)
+    return launch_qe<Q, true, false>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, B, A, s);
+  return launch_qe<Q, false, false>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, B, A, s);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W, const float* D,
                                 uint32_t* codes, void* scales, void* zeros, const void* dinv16, void* wexp,
-                                hipStream_t s) {
+                                const float* B, const float* A, hipStream_t s) {
   const _Float16* w = static_cast<const _Float16*>(W);
   _Float16* sc = static_cast<_Float16*>(scales);
   _Float16* ze = static_cast<_Float16*>(zeros);
   const _Float16* dv = static_cast<const _Float16*>(dinv16);
   _Float16* we = static_cast<_Float16*>(wexp);
   switch (q) {
-    case 2: return launch_q<2>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
-    case 3: return launch_q<3>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
-    case 5: return launch_q<5>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
-    default: return launch_q<4>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, s);
+    case 2: return launch_q<2>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, B, A, s);
+    case 3: return launch_q<3>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, B, A, s);
+    case 5: return launch_q<5>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, B, A, s);
+    default: return launch_q<4>(d_out, d_in, g, w, D, codes, sc, ze, dv, we, B, A, s);
   }
 }
 

@@ -35,10 +35,12 @@ hipError_t launch_colstats_z(const void* X, int64_t T, int d, int64_t ldx, float
 
 // Codes, scales and zeros of W D^(1/2); with wexp != NULL also the effective
 // fp16 weight W_hat = fp16(fp16((c - z) s) * dinv16) [d_out][d_in] (dinv16:
-// fp16 D^(-1/2) [d_in]).
+// fp16 D^(-1/2) [d_in]), and with B, A (fp32 rank-16 factors [d_out][16],
+// [16][d_in]; only together with wexp) W_hat + B A rounded once to fp16.
 hipError_t launch_quantize_pack(int d_out, int d_in, int q, int g, const void* W,
                                 const float* D, uint32_t* codes, void* scales, void* zeros,
-                                const void* dinv16, void* wexp, hipStream_t s);
+                                const void* dinv16, void* wexp, const float* B, const float* A,
+                                hipStream_t s);
 
 // One online step of the rank-16 factors for a prompt's statistic D: the
 // orthonormal right basis V [d_in][16] is advanced by one subspace-iteration

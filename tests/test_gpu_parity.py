@@ -490,6 +490,64 @@ def test_wexp_gemm_parity(cfg, T, q, g, r, d_out):
         assert rel_fro(Yg, Y0) <= Y_TOL
 
 
+@pytest.mark.parametrize("cfg,T,d,d_out,q,g", [
+    (5, 4097, 5056, None, 4, 32),      # 5056 = 39.5 x 128: a 64-channel last column range
+    (2, 4097, None, 8192, 3, 64),      # the planted rank-16 weight of the OPT-350M shape, 8192 rows
+])
+def test_handle_dense_lowrank(cfg, T, d, d_out, q, g):
+    """r = 16 on a long prompt: the handle's effective weight is
+    fp16(W_hat + B A) with W_hat from its own codes, scales, zeros and fp16
+    D^(-1/2) and B A the product of its factors, both prefill and
+    prepare + linear project with it alone, and Y is within the tolerance of
+    the oracle's Q[(W - B A) D^(1/2)] D^(-1/2) X + B (A X).
+
+    Weight bound, per element: 1/2 ulp of the fp16 result (its one rounding)
+    + 2^-17 sum_k |B_nk A_kj| (the fp32 MFMA sum of the three hi / lo
+    products, 48 terms, and the dropped lo x lo term) + 2^-24 sum_k (|B_nk| +
+    |A_kj|) (the absolute spacing of an fp16 lo part) + 2^-22 |S| (the fp32
+    addition)."""
+    w = wl.CONFIGS[cfg]
+    X, W = wl.config_inputs(cfg, T=T, d=d, d_out=d_out)
+    X = X.astype(np.float16)
+    assert T >= ttq.ttq_dense_min_tokens(W.shape[0])
+    say(f"dense lowrank cfg={cfg} T={T} d={W.shape[1]} d_out={W.shape[0]} q={q} g={g}")
+    layer = ttq.TTQLinear(dev(W), q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T)
+    assert layer.wexp is not None
+    Xd = dev(X)
+    Yp = host(layer.prefill(Xd))
+    B = host(layer.B).astype(np.float64)
+    A = host(layer.A).astype(np.float64)
+    d_o, d_i = W.shape
+    cg = oracle.codes_from_device(host(layer.codes).view(np.uint32), q, d_o, d_i)
+    sg = oracle.untile_groups(host(layer.scales), d_o, d_i // g)
+    zg = oracle.untile_groups(host(layer.zeros), d_o, d_i // g)
+    S = effective_weight16(cg, sg, zg, host(layer.dinvsqrt16), g).astype(np.float64) + B @ A
+    Wg = host(layer.wexp).astype(np.float64)
+    ulp = np.spacing(np.abs(Wg).astype(np.float16)).astype(np.float64)
+    bound = (0.5 * ulp + 2.0 ** -17 * (np.abs(B) @ np.abs(A)) + 2.0 ** -22 * np.abs(S)
+             + 2.0 ** -24 * (np.abs(B).sum(axis=1)[:, None] + np.abs(A).sum(axis=0)[None, :]))
+    err = np.abs(Wg - S)
+    say(f"  weight: max err / bound {np.max(err / bound):.3f}, "
+        f"{np.count_nonzero(Wg != S.astype(np.float16)) / S.size:.2e} differ from fp16(S)")
+    assert np.all(err <= bound)
+    del S, Wg, ulp, bound, err
+    # prepare + linear: the same weight, so the same Y bit for bit
+    layer.prepare(Xd)
+    Yl = host(layer.linear(Xd))
+    assert Yl.tobytes() == Yp.tobytes()
+    Bf, Af = host(layer.B), host(layer.A)
+    Wq = oracle.residual(W, Bf, Af)
+    D0 = oracle.colstats(X, w.p, w.lam, w.alpha)
+    c0, s0, z0 = oracle.quantize(Wq, D0, q, g)
+    flips = np.count_nonzero(cg != c0)
+    Y0 = oracle.linear(X, c0, s0, z0, D0, g, Bf, Af)
+    if flips == 0:
+        check_y(Yp, Y0, "prefill")
+    else:
+        assert rel_fro(Yp, Y0) <= Y_TOL
+    layer.close()
+
+
 def test_handle_dense_path():
     """A handle with room for W_hat (the default for long prompts): prepare on
     the Qwen3-32B q_proj prompt writes W_hat equal to its definition from the
