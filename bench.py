@@ -52,7 +52,7 @@ def parse():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_qwen3_32b_qproj_q4g32r0.md")
 CSRC = os.path.join(ROOT, "test_activation_aware_amd", "csrc")
-DENSE_SOURCE = os.path.join(CSRC, "dense_gemm.hip")          # the step's GEMM (long prompts)
+DENSE_SOURCE = os.path.join(CSRC, "dense_gemm.hip")          # the dense form's GEMM (handles with W_hat)
 LOWBIT_SOURCE = os.path.join(CSRC, "wlowbit_gemm_impl.h")    # the low-bit GEMM on the codes
 
 
@@ -204,7 +204,8 @@ def main():
                           "traffic": gemm_traffic(DENSE_SOURCE if dense else LOWBIT_SOURCE),
                           "kernel": ("dense_gemm_kernel: fp16 GEMM on the effective weight W_hat formed by "
                                      "the prepare step (ttq_linear, long prompts)" if dense else
-                                     "wlowbit_gemm_kernel: low-bit GEMM on the packed codes (ttq_linear)"),
+                                     "wlowbit_gemm_kernel: low-bit GEMM on the packed codes, raw fp16 input with "
+                                     "D^(-1/2) on the weight side (ttq_linear, long prompts)"),
                           "launch_us": t_gm_step * 1e6}
 
     # ---- per-kernel times, back to back (same inputs, same launch configuration) ----
@@ -219,8 +220,20 @@ def main():
         t_ps = time_graph(lambda: ttq.ttq_prescale(X, R, out=Xs), n_k, torch)
         t_gm = time_loop(lambda: ttq.ttq_wlowbit_gemm_raw(X, layer.dinvsqrt16, layer.codes, layer.scales,
                                                           layer.zeros, q, g, d_out, out=Y), n_k, torch)
-        t_dg = time_loop(lambda: ttq.ttq_wexp_gemm(X, layer.wexp, out=Y), n_k, torch) if layer.wexp is not None \
-            else None
+        # the dense form (GEMM on the effective weight W_hat, an opt-in of the
+        # handle API): its GEMM back to back and its whole step, on this machine
+        layer_d = ttq.TTQLinear(W, q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T, expand=True)
+        layer_d.prepare(X)
+        t_dg = time_loop(lambda: ttq.ttq_wexp_gemm(X, layer_d.wexp, out=Y), n_k, torch)
+
+        def step_d():
+            layer_d.prepare(X)
+            layer_d.linear(X, out=Y)
+        for _ in range(args.warmup):
+            step_d()
+        t_step_d = time_loop(step_d, args.steps, torch)
+        layer_d.close()
+        del layer_d
         t_prep = time_graph(lambda: layer.prepare(X), n_k, torch)
         t_gm_pre = time_loop(lambda: ttq.ttq_wlowbit_gemm(Xs, layer.codes, layer.scales, layer.zeros, q, g, d_out,
                                                           out=Y), n_k, torch)
@@ -274,9 +287,10 @@ def main():
                              "frac_mfma": gm_flops / t_gm_step / 1e12 / MFMA_F16_PEAK_TFLOPS,
                              "kernel": "dense_gemm_kernel" if dense else "wlowbit_gemm_kernel"},
         }
-        if t_dg is not None:
-            kernels["dense_gemm"] = {"us": t_dg * 1e6, "TFLOPs": gm_flops / t_dg / 1e12,
-                                     "frac_mfma": gm_flops / t_dg / 1e12 / MFMA_F16_PEAK_TFLOPS}
+        # the dense form of the step (a handle given room for W_hat)
+        kernels["dense_gemm"] = {"us": t_dg * 1e6, "TFLOPs": gm_flops / t_dg / 1e12,
+                                 "frac_mfma": gm_flops / t_dg / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                                 "step_ms": t_step_d * 1e3, "step_k_tok_s": T / t_step_d / 1e3}
         # context: torch's dense fp16 GEMM (hipBLASLt) of the same shape on the
         # same activations, i.e. what an unquantised q_proj costs on this GPU
         Wd = torch.randn((d_out, d), dtype=torch.float16, device="cuda") * 0.01
@@ -315,8 +329,10 @@ def main():
             step16()
         t16 = time_loop(step16, args.steps, torch)
         Zbuf = torch.empty((T, 16), dtype=torch.float32, device="cuda")
-        t_z = time_loop(lambda: ttq.ttq_lowrank_z(X, layer16.A, out=Zbuf), n_k, torch)
-        t_p16 = time_loop(lambda: layer16.prepare(X), n_k, torch)
+        # graph replays: an eager call's host side takes about as long as
+        # these kernels
+        t_z = time_graph(lambda: ttq.ttq_lowrank_z(X, layer16.A, out=Zbuf), n_k, torch)
+        t_p16 = time_graph(lambda: layer16.prepare(X), n_k, torch)
         r16 = {"value": T / t16 / 1e3, "ms_per_step": t16 * 1e3, "lowrank_z_us": t_z * 1e6,
                "prepare_us": t_p16 * 1e6}
         layer16.close()
@@ -332,7 +348,7 @@ def main():
         for _ in range(args.warmup):
             stepR()
         tR = time_loop(stepR, args.steps, torch)
-        t_pR = time_loop(lambda: layerR.prepare(X), n_k, torch)
+        t_pR = time_graph(lambda: layerR.prepare(X), n_k, torch)
         r16["refresh"] = {"value": T / tR / 1e3, "ms_per_step": tR * 1e3, "prepare_us": t_pR * 1e6}
         layerR.close()
         del rng

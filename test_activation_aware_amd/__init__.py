@@ -342,11 +342,14 @@ class TTQLinear:
     the C library only records pointers to them."""
 
     def __init__(self, W, q: int = 4, g: int = 32, alpha: float = 0.5, lam: float = 0.4,
-                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None, expand=None,
+                 p: float = 2.0, r: int = 0, T_max: int = 16384, B=None, A=None, expand=False,
                  refresh: bool = False):
         """expand: give the handle room for the effective fp16 weight, so that
         prompts of at least ttq_dense_min_tokens(d_out) fp16 tokens run the
-        dense projection (default: when T_max reaches that length).
+        dense projection on it (with r = 16 the weight also carries B A).
+        Off by default: the low-bit GEMM on the codes matched or beat the
+        dense form in the whole prefill step on all but one of the MI355X
+        boxes measured, and needs no d_out x d_in fp16 buffer.
         refresh (r = 16): prepare() refreshes the rank-16 factors online for
         each prompt (ttq_prepare_refresh), starting from the SVD basis."""
         torch = _torch()
@@ -371,8 +374,6 @@ class TTQLinear:
         self.dinvsqrt = self._dinv_buf[:4 * self.d_in].view(torch.float32)
         self.dinvsqrt16 = self._dinv_buf[4 * self.d_in:6 * self.d_in].view(torch.float16)
         self.workspace = torch.empty(max(1, sz.workspace_bytes // 4), dtype=torch.float32, device=dev)
-        if expand is None:
-            expand = T_max >= lib.ttq_dense_min_tokens(self.d_out)
         self.wexp = torch.empty_like(W) if expand else None
         self.V = self.refresh_workspace = None
         if refresh and r != 16:

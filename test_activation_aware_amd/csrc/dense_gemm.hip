@@ -144,39 +144,7 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
   f16x c0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) c0[e] = 0.f;
-  if constexpr (LOWRANK) {
-    // B16 x Z_hi + B16 x Z_lo before the K loop (Z split in two fp16 parts)
-    h8 bfr[FN];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int n = min(n0 + wn * 32 * FN + i * 32 + l32, d_out - 1);
-      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
-      const float4 b0 = bp[0], b1 = bp[1];
-      bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
-      bfr[i][2] = (_Float16)b0.z; bfr[i][3] = (_Float16)b0.w;
-      bfr[i][4] = (_Float16)b1.x; bfr[i][5] = (_Float16)b1.y;
-      bfr[i][6] = (_Float16)b1.z; bfr[i][7] = (_Float16)b1.w;
-    }
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int64_t t = min(m0 + wm * 32 * FM + j * 32 + l32, T - 1);
-      const float4* zp = reinterpret_cast<const float4*>(Z + t * 16 + 8 * hh);
-      const float4 z0 = zp[0], z1 = zp[1];
-      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      h8 zh, zl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 hv = (_Float16)zv[e];
-        zh[e] = hv;
-        zl[e] = (_Float16)(zv[e] - (float)hv);
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, c0, 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zl, acc[i][j], 0, 0, 0);
-      }
-    }
-  } else {
+  {
     uint32_t zr = 0u;
     asm volatile("" : "+v"(zr));
     const h2 zp = __builtin_bit_cast(h2, zr);
@@ -287,6 +255,41 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
     if (kt + 2 >= ksteps) break;
   }
   wait_vmem<0>();  // the repeated tail loads
+
+  if constexpr (LOWRANK) {
+    // B16 x Z_hi + B16 x Z_lo after the K loop (Z split in two fp16 parts),
+    // in the low-bit kernel's order
+    h8 bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int n = min(n0 + wn * 32 * FN + i * 32 + l32, d_out - 1);
+      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
+      const float4 b0 = bp[0], b1 = bp[1];
+      bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
+      bfr[i][2] = (_Float16)b0.z; bfr[i][3] = (_Float16)b0.w;
+      bfr[i][4] = (_Float16)b1.x; bfr[i][5] = (_Float16)b1.y;
+      bfr[i][6] = (_Float16)b1.z; bfr[i][7] = (_Float16)b1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t t = min(m0 + wm * 32 * FM + j * 32 + l32, T - 1);
+      const float4* zp = reinterpret_cast<const float4*>(Z + t * 16 + 8 * hh);
+      const float4 z0 = zp[0], z1 = zp[1];
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      h8 zh, zl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hv = (_Float16)zv[e];
+        zh[e] = hv;
+        zl[e] = (_Float16)(zv[e] - (float)hv);
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zl, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
 
   // epilogue: lane holds token l32 of each token fragment, channels
   // 8 (e / 4) + 4 hh + e % 4 of each row fragment

@@ -45,9 +45,10 @@
 //     the codes of channels 0 2 4 6 1 3 5 7 in slots 0..7, so every pair is
 //     two neighbouring channels and the fragment comes out in the input's own
 //     channel order.
-//   * Rank-r term: before the K loop each fragment gets two extra MFMAs,
+//   * Rank-r term: after the K loop each fragment gets two extra MFMAs,
 //     B16 x Z_hi and B16 x Z_lo with Z = Z_hi + Z_lo split into two fp16
-//     parts, so the fp32 Z keeps about 22 bits.
+//     parts, so the fp32 Z keeps about 22 bits (after the loop, so that their
+//     operands hold no registers during it).
 //   * Rows past T or d_out are read clamped to valid rows; a token's output
 //     depends only on its own row, and padding outputs are never stored.
 //   * Workgroup ids go round-robin over the 8 XCDs; ids are regrouped so each
@@ -296,38 +297,7 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
   f16x c0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) c0[e] = 0.f;
-  if constexpr (LOWRANK) {
-    h8 bfr[FN];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int n = min(n0 + wave * 32 * FN + i * 32 + l32, d_out - 1);
-      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
-      const float4 b0 = bp[0], b1 = bp[1];
-      bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
-      bfr[i][2] = (_Float16)b0.z; bfr[i][3] = (_Float16)b0.w;
-      bfr[i][4] = (_Float16)b1.x; bfr[i][5] = (_Float16)b1.y;
-      bfr[i][6] = (_Float16)b1.z; bfr[i][7] = (_Float16)b1.w;
-    }
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int64_t t = min(m0 + j * 32 + l32, T - 1);
-      const float4* zp = reinterpret_cast<const float4*>(Z + t * 16 + 8 * hh);
-      const float4 z0 = zp[0], z1 = zp[1];
-      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      h8 zh, zl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 hv = (_Float16)zv[e];
-        zh[e] = hv;
-        zl[e] = (_Float16)(zv[e] - (float)hv);
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, c0, 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zl, acc[i][j], 0, 0, 0);
-      }
-    }
-  } else {
+  {
     uint32_t zr = 0u;
     asm volatile("" : "+v"(zr));
     const h2 zp = as_h2(zr);
@@ -593,6 +563,41 @@ void wlowbit_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restr
     if (kt + 6 >= ksteps) break;
   }
 
+  if constexpr (LOWRANK) {
+    // the rank-16 term, added after the K loop: its operands are not held in
+    // registers across the loop
+    h8 bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int n = min(n0 + wave * 32 * FN + i * 32 + l32, d_out - 1);
+      const float4* bp = reinterpret_cast<const float4*>(Bf + (int64_t)n * 16 + 8 * hh);
+      const float4 b0 = bp[0], b1 = bp[1];
+      bfr[i][0] = (_Float16)b0.x; bfr[i][1] = (_Float16)b0.y;
+      bfr[i][2] = (_Float16)b0.z; bfr[i][3] = (_Float16)b0.w;
+      bfr[i][4] = (_Float16)b1.x; bfr[i][5] = (_Float16)b1.y;
+      bfr[i][6] = (_Float16)b1.z; bfr[i][7] = (_Float16)b1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int64_t t = min(m0 + j * 32 + l32, T - 1);
+      const float4* zp = reinterpret_cast<const float4*>(Z + t * 16 + 8 * hh);
+      const float4 z0 = zp[0], z1 = zp[1];
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      h8 zh, zl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hv = (_Float16)zv[e];
+        zh[e] = hv;
+        zl[e] = (_Float16)(zv[e] - (float)hv);
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zh, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[i], zl, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
   // ---- epilogue: lane holds token t = l32, channels 8*(e/4) + 4*hh + e%4 ----
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -630,15 +635,14 @@ hipError_t launch_fm(const GemmArgs& a, hipStream_t s) {
 }
 
 // 256-token tiles once there are enough of them to give every CU a few.
-// With 256-token tiles, q = 2 or 4, g >= 32 and no rank-16 term, eight waves
-// of one fragment each (two per SIMD: one wave's dequantisation and barrier
-// wait overlap the other's MFMAs) measured 1-1.4 % faster than four waves
-// of two and compile without spills at 128 registers; the other forms keep
-// four waves.
+// With 256-token tiles, q = 2 or 4 and g >= 32, eight waves of one fragment
+// each (two per SIMD: one wave's dequantisation and barrier wait overlap the
+// other's MFMAs) measured 1-1.4 % faster than four waves of two and fit 128
+// registers; the other forms keep four waves.
 template <int Q, int G, typename TY, bool LR, bool RAWX>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles8 = ((a.d_out + BN - 1) / BN) * ((a.T + 255) / 256);
-  constexpr int FN8 = (!LR && (Q == 2 || Q == 4) && G >= 32) ? 1 : 2;
+  constexpr int FN8 = ((Q == 2 || Q == 4) && G >= 32) ? 1 : 2;
   if (tiles8 >= 1024) return launch_fm<Q, G, TY, LR, 8, RAWX, FN8>(a, s);
   return launch_fm<Q, G, TY, LR, 4, RAWX, 2>(a, s);
 }

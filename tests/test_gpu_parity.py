@@ -495,7 +495,7 @@ def test_wexp_gemm_parity(cfg, T, q, g, r, d_out):
     (2, 4097, None, 8192, 3, 64),      # the planted rank-16 weight of the OPT-350M shape, 8192 rows
 ])
 def test_handle_dense_lowrank(cfg, T, d, d_out, q, g):
-    """r = 16 on a long prompt: the handle's effective weight is
+    """r = 16 on a long prompt, a handle given room for W_hat: its effective weight is
     fp16(W_hat + B A) with W_hat from its own codes, scales, zeros and fp16
     D^(-1/2) and B A the product of its factors, both prefill and
     prepare + linear project with it alone, and Y is within the tolerance of
@@ -511,7 +511,7 @@ def test_handle_dense_lowrank(cfg, T, d, d_out, q, g):
     X = X.astype(np.float16)
     assert T >= ttq.ttq_dense_min_tokens(W.shape[0])
     say(f"dense lowrank cfg={cfg} T={T} d={W.shape[1]} d_out={W.shape[0]} q={q} g={g}")
-    layer = ttq.TTQLinear(dev(W), q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T)
+    layer = ttq.TTQLinear(dev(W), q=q, g=g, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, expand=True)
     assert layer.wexp is not None
     Xd = dev(X)
     Yp = host(layer.prefill(Xd))
@@ -549,7 +549,7 @@ def test_handle_dense_lowrank(cfg, T, d, d_out, q, g):
 
 
 def test_handle_dense_path():
-    """A handle with room for W_hat (the default for long prompts): prepare on
+    """A handle given room for W_hat (opt-in for r = 0): prepare on
     the Qwen3-32B q_proj prompt writes W_hat equal to its definition from the
     handle's own codes, scales, zeros and fp16 D^(-1/2); the projection runs
     the dense GEMM and equals the low-bit kernel on the same codes bit for
@@ -558,7 +558,7 @@ def test_handle_dense_path():
     X, W = cfg_inputs(5)
     T = X.shape[0]
     assert T >= ttq.ttq_dense_min_tokens(W.shape[0])
-    layer = ttq.TTQLinear(dev(W), q=4, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T)
+    layer = ttq.TTQLinear(dev(W), q=4, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=0, T_max=T, expand=True)
     assert layer.wexp is not None
     Xd = dev(X)
     layer.prepare(Xd)
@@ -625,19 +625,23 @@ def test_lowrank_refresh_parity(cfg, d_out):
     assert Rg.view(np.uint16).tobytes() == oracle.residual(W, host(Bd), host(Ad)).view(np.uint16).tobytes()
 
 
-@pytest.mark.parametrize("cfg,q,T", [(2, 3, None), (5, 2, 8192), (5, 4, None)])
-def test_e2e_prepare_refresh(cfg, q, T):
+@pytest.mark.parametrize("cfg,q,T,expand", [(2, 3, None, False), (5, 2, 8192, False), (5, 4, None, False),
+                                             (5, 4, None, True)])
+def test_e2e_prepare_refresh(cfg, q, T, expand):
     """A refreshing handle: prepare (statistic, refresh, residual, quantise)
     then the projection.  D within 1e-5; B A within 1e-5 of the oracle's
     refresh from the SVD basis with the oracle's D; W_res bit-exact given the
     GPU's B, A; codes, scales and zeros bit-exact given the GPU's D and W_res;
     Y within 1e-3 of the oracle's own pipeline (its D, refresh, residual,
-    codes and projection)."""
+    codes and projection).  expand: the handle has room for W_hat, so the
+    long prompt's projection is the dense GEMM on W_hat + B A with the
+    refreshed factors."""
     w = wl.CONFIGS[cfg]
     X, W = cfg_inputs(cfg, T=T)
     T = X.shape[0]
-    say(f"e2e refresh cfg={cfg} q={q} T={T}")
-    layer = ttq.TTQLinear(dev(W), q=q, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, refresh=True)
+    say(f"e2e refresh cfg={cfg} q={q} T={T} expand={expand}")
+    layer = ttq.TTQLinear(dev(W), q=q, g=32, alpha=w.alpha, lam=w.lam, p=w.p, r=16, T_max=T, refresh=True,
+                          expand=expand)
     V0 = host(layer.V).copy()
     Xd = dev(X)
     layer.prepare(Xd)
