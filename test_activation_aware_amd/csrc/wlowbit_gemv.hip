@@ -296,13 +296,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void wlowbit_fewtok_kernel(
       // the input slice: slot j of the wave's part holds token t = j / rowp,
       // piece (i, c ^ (t & 7)) for j % rowp = 8 i + c (i = step of the round,
       // c = 8-channel piece of the step); slots past T rows read clamped
+      // (t = j / rowp through a float reciprocal: j < 16 * 8 * kRound and
+      // rowp <= 8 * kRound, so (j + 1/2) / rowp stays at least 1 / (2 rowp)
+      // from an integer and the rounding error of the product is far below
+      // that; byte offsets in 32 bits: t < 16 and 2 ldx < 2^23)
       const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, ((int64_t)(T - 1) * ldx + d_in) * 2);
       const int nslot = T * rowp;
+      const float inv_rowp = 1.0f / (float)rowp;
+      const int ldx2 = (int)(ldx * 2);
       for (int j0 = 0; j0 < nslot; j0 += 64) {
         const int j = min(j0 + lane, nslot - 1);
-        const int t = j / rowp, rem = j - t * rowp;
+        const int t = (int)(((float)j + 0.5f) * inv_rowp);
+        const int rem = j - t * rowp;
         const int ch = (k0 + (rem >> 3)) * 64 + 8 * ((rem & 7) ^ (t & 7));
-        lds_dma16(rx, (int)(((int64_t)t * ldx + ch) * 2), xw + j0 * 16);
+        lds_dma16(rx, t * ldx2 + 2 * ch, xw + j0 * 16);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
