@@ -130,7 +130,9 @@ typedef struct ttq_sizes {
  * instead (the fp32 sum rounded once; section 2's Y = W_hat X + B (A X) is
  * (W_hat + B A) X), so that GEMM is the whole projection, with no A X; its
  * outputs are then within the tolerance of the low-bit kernel's, not the
- * same bits. */
+ * same bits.  Without it (NULL) every prompt runs the low-bit GEMM on the
+ * codes, which on most MI355X boxes measured was as fast in the whole
+ * prefill step and needs no d_out x d_in fp16 buffer. */
 typedef struct ttq_buffers {
   uint32_t* codes;
   void* scales;

@@ -127,10 +127,12 @@ ttq_status check_x(const void* X, ttq_dtype xdt, int64_t T, int64_t d, int64_t l
 }
 
 // Long prompts with fp16 input run the dense GEMM on the effective fp16
-// weight W_hat when the handle has a buffer for it: once the 256 x 256 tile
-// grid has at least kDenseMinTiles tiles (two workgroups per CU), forming
-// W_hat once costs less than dequantising every weight fragment again for
-// each token tile.
+// weight W_hat when the caller gave the handle a buffer for it (opt-in): from
+// a 256 x 256 tile grid of kDenseMinTiles tiles (two workgroups per CU) on,
+// forming W_hat once per prompt can cost less than dequantising every weight
+// fragment again for each token tile.  Whether it does depends on the
+// machine: the low-bit GEMM measured as fast or faster on most MI355X boxes,
+// so handles without the buffer, the default, keep it.
 constexpr int64_t kDenseMinTiles = 512;
 int64_t dense_min_tokens(int64_t d_out) {
   const int64_t tn = (d_out + 255) / 256;
