@@ -2,7 +2,7 @@
 // 64-channel step of a lane's packed codes from the tiled code layout and
 // unpacking them into fp16 pairs 1024 + c (the code OR-ed into the mantissa
 // of 1024.0, exact for codes below 1024), the raw-input loads of the fused
-// input path, and direct-to-LDS buffer loads.
+// input path, and direct-to-LDS buffer loads (also used by quantize_pack).
 //
 // Lane layout of a step (the A-operand layout of v_mfma_f32_32x32x16_f16):
 // lane l holds row l % 32 of a 32-row tile and, in sub-step s = 0..3 of the
@@ -54,10 +54,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
 }
 
-// 16 bytes per lane from a buffer into LDS; lane l lands at lds_wave_base + 16 l
+// 16 bytes per lane from a buffer into LDS; lane l lands at lds_wave_base + 16 l.
+// AUX: the load's cache-policy bits (2: nontemporal, for data read once).
+template <int AUX = 0>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                           voff, 0, 0, 0);
+                                           voff, 0, 0, AUX);
 }
 
 // Zero, as an opaque value the compiler cannot form before v is in a

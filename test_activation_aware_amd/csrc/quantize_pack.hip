@@ -17,18 +17,23 @@
 // the codes of channels 0 2 4 6 1 3 5 7, packed as a bitstream, words in the
 // tiled order (32-row tiles, one contiguous chunk per 64-channel step).
 //
-// Work split: a workgroup of 128 threads owns one 32-row tile of W over 128
-// input channels (4 blocks of 32), 10240 workgroups at the Qwen3-32B q_proj
-// shape (small workgroups keep many slabs in flight per CU):
-//   * the 32 x 128 fp16 slab (8 KB) comes in with 16-byte loads, one full
-//     row per 16 lanes, and is parked in LDS (rows padded by 16 bytes, so
-//     the block reads below hit 16 distinct bank groups);
-//   * thread (r, b) = (row in tile, 32-channel block) quantises its block
-//     from LDS (as two groups when g = 16); groups of 64 / 128 channels meet
-//     through an LDS min/max exchange;
-//   * codes are placed in LDS in the tiled order and leave as one contiguous
-//     store of 2 steps x 32 rows x 2q words; scales and zeros likewise (all
-//     with nontemporal stores, which measured about 5 % faster here).
+// Two work splits:
+//   * groups of at most 64 channels without the effective weight (the
+//     default prepare): one wave per (32-row tile, 64-channel step), no
+//     workgroup barrier (quantize_pack_step_kernel below; the slab arrives by
+//     direct-to-LDS loads marked nontemporal, W being read once);
+//   * otherwise a workgroup of 128 threads owns one 32-row tile of W over
+//     128 input channels (4 blocks of 32):
+//     - the 32 x 128 fp16 slab (8 KB) comes in with 16-byte loads, one full
+//       row per 16 lanes, and is parked in LDS (rows padded by 16 bytes, so
+//       the block reads below hit 16 distinct bank groups);
+//     - thread (r, b) = (row in tile, 32-channel block) quantises its block
+//       from LDS (as two groups when g = 16); groups of 64 / 128 channels
+//       meet through an LDS min/max exchange;
+//     - codes are placed in LDS in the tiled order and leave as one
+//       contiguous store of 2 steps x 32 rows x 2q words; scales and zeros
+//       likewise (all with nontemporal stores, which measured about 5 %
+//       faster here).
 // v = w * sq is one v_fma_mix_f32 (fp16 operand, fp32 arithmetic) and the
 // codes are packed bytewise with v_cvt_pk_u8_f32.
 //
@@ -59,6 +64,7 @@
 // of a thread's block comes closer, the whole block is redone with the IEEE
 // division and the clamp (rare; the fast codes of the other elements would
 // have been the same).  The zero point takes the same path for -mn/s.
+#include "code_unpack.h"
 #include "ttq_internal.h"
 
 #pragma clang fp contract(off)
@@ -115,6 +121,92 @@ template <int Q>
 __device__ __forceinline__ constexpr int step_pos(int h, int w) {
   if constexpr (Q == 4) return 4 * (w % 2) + 2 * h + w / 2;
   else return Q * h + w;
+}
+
+// Scale s (fp16, and as fp32), zero point zf and 1/s of a group from its
+// range mn <= 0 <= mx.
+template <int Q>
+__device__ __forceinline__ void group_params(float mn, float mx, _Float16& s16, float& s, float& zf, float& rcp) {
+  constexpr float N = (float)((1 << Q) - 1);
+  if (mx == mn) {  // all-zero group
+    s16 = (_Float16)1.0f;
+    s = 1.0f;
+    zf = 0.0f;
+  } else {
+    const float s32 = (mx - mn) / N;
+    s16 = fp16_round_up(s32);
+    s = (float)s16;
+    // z by the same reciprocal fast path as the codes
+    const float x = -mn * __builtin_amdgcn_rcpf(s);
+    float zr = rintf(x);
+    if (fabsf(x - zr) > 0.5f - 0x1p-16f) zr = rintf(-mn / s);
+    zf = fminf(fmaxf(zr, 0.0f), N) + 0.0f;
+  }
+  rcp = __builtin_amdgcn_rcpf(s);
+}
+
+// code(k) gives the integer-valued float stored in slot k of a 32-channel
+// block; packs the block's bitstream (slot k at bit Q*k of its Q words).
+template <int Q, typename F>
+__device__ __forceinline__ void pack_codes(F&& code, uint32_t word[Q]) {
+  if constexpr (Q == 4) {
+    // bytes of lo / hi: codes 8w+2i / 8w+2i+1; lo | hi << 4 interleaves the nibbles
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo = put_byte(code(8 * w + 2 * i), i, lo);
+        hi = put_byte(code(8 * w + 2 * i + 1), i, hi);
+      }
+      word[w] = lo | (hi << 4);
+    }
+  } else if constexpr (Q == 2) {
+    // byte i of part m: code 16w+4i+m; four parts at shifts 0, 2, 4, 6
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t part[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) part[m] = put_byte(code(16 * w + 4 * i + m), i, part[m]);
+      word[w] = part[0] | (part[1] << 2) | (part[2] << 4) | (part[3] << 6);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Q; ++i) word[i] = 0u;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      // code(k) is in [0, N] (the callers' fast path by its error bound, the
+      // exact one by its clamp)
+      const uint32_t ci = (uint32_t)code(k);
+      const int bit = Q * k;
+      word[bit >> 5] |= ci << (bit & 31);
+      if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
+    }
+  }
+}
+
+// The packed codes of a 32-channel block v (CPG channels per group) by the
+// reciprocal fast path, the whole block redone with the IEEE division and
+// the clamp when any element comes within 2^-16 of a rounding boundary.
+template <int Q, int CPG>
+__device__ __forceinline__ void block_codes(const float v[32], const float* s, const float* zf, const float* rcp,
+                                            uint32_t word[Q]) {
+  constexpr float N = (float)((1 << Q) - 1);
+  float far = 0.0f;  // largest distance of u from its rounded value
+  pack_codes<Q>([&](int k) {
+    const int ch = slot_channel(k), sg = ch / CPG;
+    const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
+    const float c = rintf(u);
+    far = fmaxf(far, fabsf(u - c));
+    return c;
+  }, word);
+  if (far > 0.5f - 0x1p-16f)  // rare
+    pack_codes<Q>([&](int k) {
+      const int ch = slot_channel(k), sg = ch / CPG;
+      return fminf(fmaxf(rintf(v[ch] / s[sg]) + zf[sg], 0.0f), N);
+    }, word);
 }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -213,80 +305,13 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     float s[SG], zf[SG], rcp[SG];
     _Float16 s16[SG];
 #pragma unroll
-    for (int sg = 0; sg < SG; ++sg) {
-      if (mx[sg] == mn[sg]) {  // all-zero group
-        s16[sg] = (_Float16)1.0f;
-        s[sg] = 1.0f;
-        zf[sg] = 0.0f;
-      } else {
-        const float s32 = (mx[sg] - mn[sg]) / N;
-        s16[sg] = fp16_round_up(s32);
-        s[sg] = (float)s16[sg];
-        // z by the same reciprocal fast path
-        const float x = -mn[sg] * __builtin_amdgcn_rcpf(s[sg]);
-        float zr = rintf(x);
-        if (fabsf(x - zr) > 0.5f - 0x1p-16f) zr = rintf(-mn[sg] / s[sg]);
-        zf[sg] = fminf(fmaxf(zr, 0.0f), N) + 0.0f;
-      }
-      rcp[sg] = __builtin_amdgcn_rcpf(s[sg]);
-    }
+    for (int sg = 0; sg < SG; ++sg) group_params<Q>(mn[sg], mx[sg], s16[sg], s[sg], zf[sg], rcp[sg]);
 
-    // code(k) gives the integer-valued float stored in slot k; packing into
-    // the bitstream (slot k at bit Q*k of the block's Q words)
     uint32_t word[Q];
-    auto pack = [&](auto&& code) {
-      if constexpr (Q == 4) {
-        // bytes of lo / hi: codes 8w+2i / 8w+2i+1; lo | hi << 4 interleaves the nibbles
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            lo = put_byte(code(8 * w + 2 * i), i, lo);
-            hi = put_byte(code(8 * w + 2 * i + 1), i, hi);
-          }
-          word[w] = lo | (hi << 4);
-        }
-      } else if constexpr (Q == 2) {
-        // byte i of part m: code 16w+4i+m; four parts at shifts 0, 2, 4, 6
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          uint32_t part[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) part[m] = put_byte(code(16 * w + 4 * i + m), i, part[m]);
-          word[w] = part[0] | (part[1] << 2) | (part[2] << 4) | (part[3] << 6);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < Q; ++i) word[i] = 0u;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          // code(k) is in [0, N] on both paths below (the fast one by its
-          // error bound, the exact one by its clamp)
-          const uint32_t ci = (uint32_t)code(k);
-          const int bit = Q * k;
-          word[bit >> 5] |= ci << (bit & 31);
-          if ((bit & 31) + Q > 32) word[(bit >> 5) + 1] |= ci >> (32 - (bit & 31));
-        }
-      }
-    };
-    float far = 0.0f;  // largest distance of u from its rounded value
     if constexpr (!EXPAND) {
-      pack([&](int k) {
-        const int ch = slot_channel(k), sg = ch / CPG;
-        const float u = __builtin_fmaf(v[ch], rcp[sg], zf[sg]);
-        const float c = rintf(u);
-        far = fmaxf(far, fabsf(u - c));
-        return c;
-      });
-      if (far > 0.5f - 0x1p-16f)  // rare: redo the block with the IEEE division
-        pack([&](int k) {
-          const int ch = slot_channel(k), sg = ch / CPG;
-          return fminf(fmaxf(rintf(v[ch] / s[sg]) + zf[sg], 0.0f), N);
-        });
+      block_codes<Q, CPG>(v, s, zf, rcp, word);
     } else {
+      float far = 0.0f;  // largest distance of u from its rounded value
       // the codes replace v in place (the rare exact path rereads the slab)
 #pragma unroll
       for (int ch = 0; ch < 32; ++ch) {
@@ -305,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
           v[ch + 1] = fminf(fmaxf(rintf(mul_hi(raw, sq[bl * 32 + ch + 1]) / s[sg]) + zf[sg], 0.0f), N);
         }
       }
-      pack([&](int k) { return v[slot_channel(k)]; });
+      pack_codes<Q>([&](int k) { return v[slot_channel(k)]; }, word);
     }
     if constexpr (EXPAND) {
       // W_hat of the block, in place of its slab in LDS (this thread's own
@@ -434,6 +459,113 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   }
 }
 
+// The same quantisation without the effective weight, for groups of at most
+// 64 channels, with one wave per (32-row tile, 64-channel step) and no
+// workgroup barrier: each wave copies its 32 x 64 fp16 slab (4 KB) into its
+// own part of LDS by direct-to-LDS loads (8 lanes per 128-byte row piece, the
+// 16-byte pieces XOR-swizzled by row so the block reads below are free of
+// bank conflicts), lane (r, h) = lane h * 32 + r quantises channels
+// 32h .. 32h + 31 of row r (a 64-channel group meets through one lane
+// exchange with lane r + 32), and the step's codes leave as the one
+// contiguous chunk the tiled order gives them (Q x 256 bytes).  Waves never
+// wait for one another; the four waves of a workgroup take four consecutive
+// steps of a tile (32 rows x 512 bytes of W).  The slab copies carry the
+// nontemporal hint: at the Qwen3-32B q_proj shape that measured 3-4 % faster
+// than plain copies, warm and cold.
+constexpr int kStepWaves = 4;
+template <int Q, int G>
+__global__ __launch_bounds__(64 * kStepWaves) void quantize_pack_step_kernel(
+    const _Float16* __restrict__ W, const float* __restrict__ D, int d_in, uint32_t* __restrict__ codes,
+    _Float16* __restrict__ scales, _Float16* __restrict__ zeros) {
+  static_assert(G == 16 || G == 32 || G == 64, "one step holds whole groups");
+  constexpr int SG = G < 32 ? 32 / G : 1;  // groups inside one 32-channel block
+  constexpr int CPG = 32 / SG;
+  constexpr int SW = 2 * Q;  // words per row per step
+  __shared__ __attribute__((aligned(16))) uint4 slab[kStepWaves][256];  // 32 rows x 8 pieces
+  __shared__ __attribute__((aligned(16))) float sqs[kStepWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ksteps = d_in / 64;
+  const int k = blockIdx.x * kStepWaves + wave;  // the wave's step
+  if (k >= ksteps) return;                        // whole waves only: no barrier follows
+  const int nt = blockIdx.y;                      // row tile
+  uint4* sw = &slab[wave][0];
+
+  // sqrt(D) of the step's channels, then the slab: LDS piece 64 i + lane
+  // holds 16-byte piece (lane % 8) ^ (lane / 8) of row 8 i + lane / 8
+  const float dj = D[k * 64 + lane];
+  {
+    const __amdgpu_buffer_rsrc_t rw = unpack::make_rsrc(W + (int64_t)nt * 32 * d_in, (int64_t)32 * d_in * 2);
+    const int pr = lane >> 3, pc = (lane & 7) ^ pr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack::lds_dma16<2>(rw, (8 * i + pr) * d_in * 2 + k * 128 + pc * 16, sw + 64 * i);
+  }
+  sqs[wave][lane] = sqrtf(dj);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies have landed
+
+  const int r = lane & 31, h = lane >> 5;
+  float v[32];
+  float mn[SG], mx[SG];
+#pragma unroll
+  for (int sg = 0; sg < SG; ++sg) mn[sg] = mx[sg] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 raw = sw[8 * r + ((4 * h + i) ^ (r & 7))];
+    const float4 sa = *reinterpret_cast<const float4*>(&sqs[wave][32 * h + 8 * i]);
+    const float4 sb = *reinterpret_cast<const float4*>(&sqs[wave][32 * h + 8 * i + 4]);
+    float* o = &v[8 * i];
+    o[0] = mul_lo(raw.x, sa.x); o[1] = mul_hi(raw.x, sa.y);
+    o[2] = mul_lo(raw.y, sa.z); o[3] = mul_hi(raw.y, sa.w);
+    o[4] = mul_lo(raw.z, sb.x); o[5] = mul_hi(raw.z, sb.y);
+    o[6] = mul_lo(raw.w, sb.z); o[7] = mul_hi(raw.w, sb.w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[(8 * i + e) / CPG] = fminf(mn[(8 * i + e) / CPG], o[e]);
+      mx[(8 * i + e) / CPG] = fmaxf(mx[(8 * i + e) / CPG], o[e]);
+    }
+  }
+  if constexpr (G == 64) {  // the group's other half is lane r + 32 (or r)
+    mn[0] = fminf(mn[0], __shfl_xor(mn[0], 32));
+    mx[0] = fmaxf(mx[0], __shfl_xor(mx[0], 32));
+  }
+  float s[SG], zf[SG], rcp[SG];
+  _Float16 s16[SG];
+#pragma unroll
+  for (int sg = 0; sg < SG; ++sg) group_params<Q>(mn[sg], mx[sg], s16[sg], s[sg], zf[sg], rcp[sg]);
+  uint32_t word[Q];
+  block_codes<Q, CPG>(v, s, zf, rcp, word);
+
+  // the step's code chunk (32 rows x SW words) through the slab's LDS, which
+  // this wave alone has read
+  asm volatile("" ::: "memory");
+  uint32_t* oc = reinterpret_cast<uint32_t*>(sw);
+#pragma unroll
+  for (int w = 0; w < Q; ++w) oc[r * SW + step_pos<Q>(h, w)] = word[w];
+  asm volatile("" ::: "memory");
+  {
+    uint32_t* gdst = codes + ((int64_t)nt * ksteps + k) * 32 * SW;
+#pragma unroll
+    for (int i = lane; i < 8 * SW; i += 64)
+      __builtin_nontemporal_store(reinterpret_cast<const u4v*>(oc)[i], reinterpret_cast<u4v*>(gdst) + i);
+  }
+  // scales and zeros: group gi of tile nt at (nt * d_in / G + gi) * 32 + row
+  const int64_t gbase = (int64_t)nt * (d_in / G) * 32;
+  if constexpr (G == 64) {
+    if (h == 0) {
+      scales[gbase + (int64_t)k * 32 + r] = s16[0];
+      zeros[gbase + (int64_t)k * 32 + r] = (_Float16)zf[0];
+    }
+  } else {
+#pragma unroll
+    for (int sg = 0; sg < SG; ++sg) {
+      const int64_t gi = (int64_t)k * (64 / G) + h * SG + sg;
+      scales[gbase + gi * 32 + r] = s16[sg];
+      zeros[gbase + gi * 32 + r] = (_Float16)zf[sg];
+    }
+  }
+}
+
 template <int Q, bool EX, bool LR>
 hipError_t launch_qe(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
                      _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, const float* B,
@@ -455,6 +587,18 @@ template <int Q>
 hipError_t launch_q(int d_out, int d_in, int g, const _Float16* W, const float* D, uint32_t* codes,
                     _Float16* scales, _Float16* zeros, const _Float16* dinv16, _Float16* wexp, const float* B,
                     const float* A, hipStream_t s) {
+  if (wexp == nullptr && g <= 64) {
+    const dim3 grid((unsigned)((d_in / 64 + kStepWaves - 1) / kStepWaves), (unsigned)(d_out / 32));
+#define TTQ_QS(GV) hipLaunchKernelGGL((quantize_pack_step_kernel<Q, GV>), grid, dim3(64 * kStepWaves), 0, s, W, D, \
+                                      d_in, codes, scales, zeros)
+    switch (g) {
+      case 16: TTQ_QS(16); break;
+      case 32: TTQ_QS(32); break;
+      default: TTQ_QS(64); break;
+    }
+#undef TTQ_QS
+    return hipGetLastError();
+  }
   if (wexp != nullptr && B != nullptr)
     return launch_qe<Q, true, true>(d_out, d_in, g, W, D, codes, scales, zeros, dinv16, wexp, B, A, s);
   if (wexp != nullptr)
