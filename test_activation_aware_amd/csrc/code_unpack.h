@@ -97,20 +97,26 @@ struct CodeStep<5> {
   u4v b;
 };
 
-template <int Q>
+// NT: loads with the nontemporal hint (codes streamed once per call)
+template <typename V, bool NT>
+__device__ __forceinline__ V load_words(const uint32_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
+}
+template <int Q, bool NT = false>
 __device__ __forceinline__ CodeStep<Q> load_codes(const uint32_t* p, int hh) {
   CodeStep<Q> c;
   if constexpr (Q == 4) {
-    c.a = *reinterpret_cast<const u4v*>(p + 4 * hh);
+    c.a = load_words<u4v, NT>(p + 4 * hh);
   } else if constexpr (Q == 2) {
-    c.a = *reinterpret_cast<const u4v*>(p);
+    c.a = load_words<u4v, NT>(p);
   } else if constexpr (Q == 5) {
-    c.a = *reinterpret_cast<const u4a*>(p + hh);
-    c.b = *reinterpret_cast<const u4a*>(p + 5 + hh);
+    c.a = load_words<u4a, NT>(p + hh);
+    c.b = load_words<u4a, NT>(p + 5 + hh);
   } else {
-    const u2v w01 = *reinterpret_cast<const u2v*>(p);
-    const u2v w23 = *reinterpret_cast<const u2v*>(p + 2);
-    c.b = *reinterpret_cast<const u2v*>(p + 4);
+    const u2v w01 = load_words<u2v, NT>(p);
+    const u2v w23 = load_words<u2v, NT>(p + 2);
+    c.b = load_words<u2v, NT>(p + 4);
     c.a = u4v{w01[0], w01[1], w23[0], w23[1]};
   }
   return c;

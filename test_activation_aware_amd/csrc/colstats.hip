@@ -6,8 +6,9 @@
 // HBM-bound column reduction over the T rows of X [T][ldx].
 //   pass 1 (colstats_partial): grid (column slabs, row chunks).  A workgroup
 //     of 4 waves owns one slab of 64*VEC columns; each lane owns VEC adjacent
-//     columns (one 16-byte load per row) and the 4 waves take interleaved
-//     rows of the chunk.  Lane sums stay in fp32 registers, the 4 waves are
+//     columns (one 16-byte load per row, eight rows in flight, nontemporal)
+//     and the 4 waves take interleaved rows of the chunk.  Lane sums stay in
+//     fp32 registers, the 4 waves are
 //     combined through LDS and one partial per (chunk, column) is written.
 //   pass 2 (colstats_finalize): per column, 8 threads sum interleaved slices
 //     of the chunk partials in fp64 and the slices are combined in a fixed
@@ -47,6 +48,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRowsInFlight = 8;  // 16-byte row loads per lane in flight (partial pass)
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 template <int PMODE>
 __device__ __forceinline__ float powabs(float x, float p) {
@@ -79,14 +82,19 @@ __global__ __launch_bounds__(kThreads) void colstats_partial(const TX* __restric
   if (active) {
     const TX* base = X + col0;
     int64_t t = r0 + wave;
-    // four rows in flight per lane
-    for (; t + 3 * kWaves < r1; t += 4 * kWaves) {
-      uint4 raw[4];
+    // eight rows in flight per lane, read with the nontemporal hint (X is
+    // streamed once here): at the Qwen3-32B q_proj prompt (16384 x 5120 fp16)
+    // 26.4 us cold against 31.2-32.0 us for four plain loads in flight, warm
+    // unchanged; rows are still added in row order, so the sums are the same
+    for (; t + (kRowsInFlight - 1) * kWaves < r1; t += kRowsInFlight * kWaves) {
+      uint4 raw[kRowsInFlight];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        raw[u] = *reinterpret_cast<const uint4*>(base + (t + u * kWaves) * ldx);
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const u4v q = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(base + (t + u * kWaves) * ldx));
+        raw[u] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kRowsInFlight; ++u) {
         const TX* e = reinterpret_cast<const TX*>(&raw[u]);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] += powabs<PMODE>((float)e[v], p);
