@@ -234,6 +234,10 @@ def test_quantize_ragged_rows():
     # channel counts that leave a partial 128-channel workgroup (64 channels)
     for d in (192, 320, 384, 448):
         _check_quant(np.ascontiguousarray(W[:64, :d]), D[:d], 4, 64 if d % 128 else 128, f"d{d}")
+    # step counts (d / 64) that leave the last workgroup of four one-step
+    # waves partly empty, for every group size the one-step form takes
+    for d, q, g in ((192, 4, 32), (320, 3, 16), (448, 5, 32), (576, 2, 16), (320, 4, 64)):
+        _check_quant(np.ascontiguousarray(W[:96, :d]), D[:d], q, g, f"d{d}q{q}g{g}")
 
 
 # ---------------------------------------------------------------------------
