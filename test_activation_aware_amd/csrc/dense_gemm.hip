@@ -293,6 +293,52 @@ void dense_gemm_kernel(int64_t T, int d_in, int d_out, const _Float16* __restric
 
   // epilogue: lane holds token l32 of each token fragment, channels
   // 8 (e / 4) + 4 hh + e % 4 of each row fragment
+  if constexpr (sizeof(TY) == 2 && WN == 2 && WM == 4) {
+    // fp16 outputs leave through LDS as whole 512-byte token rows (stored
+    // straight from the accumulators, every store instruction would write 16
+    // bytes into each of 32 rows): the tile (256 tokens x 256 channels, 128
+    // KB) fills the four stages, token group wm (64 tokens) in stage wm, the
+    // 16-byte chunks of row r XOR-swizzled by r % 32.
+    auto stage = [&](int g) -> char* {
+      return reinterpret_cast<char*>(g == 0 ? xs0 : g == 1 ? xs1 : g == 2 ? ws0 : ws1);
+    };
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();  // every wave is done with the stages
+    {
+      char* yb = stage(wm);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int r = j * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int c = (wn * FN + i) * 4 + e4;  // 16-byte chunk (8 channels) of the row
+            const h2 a = {(_Float16)acc[i][j][4 * e4 + 0], (_Float16)acc[i][j][4 * e4 + 1]};
+            const h2 b = {(_Float16)acc[i][j][4 * e4 + 2], (_Float16)acc[i][j][4 * e4 + 3]};
+            *reinterpret_cast<uint2*>(yb + r * 512 + ((c ^ (r & 31)) * 16) + 8 * hh) =
+                make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+          }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    {
+      // wave w stores tile rows 32 w .. 32 w + 31
+      const int g = wave >> 1;
+      const char* yb = stage(g);
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int r = (wave & 1) * 32 + 2 * ii + hh;
+        const int c = l32;
+        const uint4 v = *reinterpret_cast<const uint4*>(yb + r * 512 + ((c ^ (r & 31)) * 16));
+        const int64_t t = m0 + 64 * g + r;
+        const int n = n0 + 8 * c;
+        if (t < T && n < d_out) *reinterpret_cast<uint4*>(Y + t * ldy + n) = v;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
     const int64_t t = m0 + wm * 32 * FM + j * 32 + l32;
