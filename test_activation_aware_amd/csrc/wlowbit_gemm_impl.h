@@ -683,7 +683,13 @@ hipError_t launch_fm(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256-token tiles once there are enough of them to give every CU a few.
+// 256-token tiles (one workgroup per CU at a time) when they fill whole
+// rounds of the 256 CUs or make at least four rounds; otherwise 128-token
+// tiles, whose twice as many workgroups even out a partial last round.
+// Measured with bit-identical outputs at d = 5120, d' = 8192: T = 2048 (256
+// tiles) 153-155 against 159-162 us, T = 4096 (512) 298 against 308 us,
+// T = 6144 (768) 444 against 456 us, but T = 3072 (384 tiles, 1.5 rounds)
+// 259 against 240 us and T = 5120 (640, 2.5 rounds) 406 against 385 us.
 // With 256-token tiles, q = 2 or 4 and g >= 32, eight waves of one fragment
 // each (two per SIMD: one wave's dequantisation and barrier wait overlap the
 // other's MFMAs) measured 1-1.4 % faster than four waves of two and fit 128
@@ -692,7 +698,7 @@ template <int Q, int G, typename TY, bool LR, bool RAWX>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles8 = ((a.d_out + BN - 1) / BN) * ((a.T + 255) / 256);
   constexpr int FN8 = ((Q == 2 || Q == 4) && G >= 32) ? 1 : 2;
-  if (tiles8 >= 1024) return launch_fm<Q, G, TY, LR, 8, RAWX, FN8>(a, s);
+  if (tiles8 >= 1024 || (tiles8 > 0 && tiles8 % 256 == 0)) return launch_fm<Q, G, TY, LR, 8, RAWX, FN8>(a, s);
   return launch_fm<Q, G, TY, LR, 4, RAWX, 2>(a, s);
 }
 

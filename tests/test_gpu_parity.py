@@ -7,8 +7,8 @@ back) and the same W_res; W_res bit-exact; Y within 1e-3 relative Frobenius
 error (fp16 operands, fp32 accumulation), and at the Qwen3 shapes also within
 1e-3 on every token row and on every 256 x 256 output tile, so one wrong
 tile fails.  Sizes span several tiles with ragged tails; the launch forms the
-benchmark times (256-token tiles, chosen once the grid has 1024 of them) are
-compared on every output."""
+benchmark times (256-token tiles, chosen when the grid has at least 1024 of
+them or a multiple of 256) are compared on every output."""
 import functools
 
 import numpy as np
@@ -436,9 +436,10 @@ def test_gemm_parity_full_cfg5(q, r, raw):
     _gemm_case(5, 16384, q, 32, r, raw=raw)
 
 
-# The 256-token instances (chosen when d'/256 * ceil(T/256) >= 1024) on the
-# Qwen3-32B q_proj weight (5120 -> 8192) at the smallest prompts that select
-# them, every output compared: each code width and group size the benchmark
+# The 256-token instances (chosen when n = d'/256 * ceil(T/256) >= 1024 or n
+# is a multiple of 256) on the Qwen3-32B q_proj weight (5120 -> 8192), every
+# output compared, at prompts of 32 to 35 token tiles: each code width and
+# group size the benchmark
 # times, the rank-16 form with the product's host SVD, the pre-scaled input,
 # a token-tile count that is not a multiple of the 4-tile XCD band
 # (T = 8741: 35 token tiles) and a ragged last channel tile (d' = 8160).
